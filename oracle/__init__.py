@@ -1,0 +1,134 @@
+"""fp64 CPU oracle for pool-indexed recurrent-state decode (test infrastructure).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package. It wraps ``oracle.c`` (plain scalar fp64 loops) through
+ctypes; it shares no code with the GPU library and never calls it.
+
+The recurrence it evaluates, and where it comes from, is stated in the header
+of ``oracle.c``. This module only converts inputs to contiguous float64 arrays
+(bf16 and fp32 convert exactly) and hands them over.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+__all__ = ["LIGHTNING", "GDN", "KDA", "L2NORM_QK", "BETA_LOGIT", "build",
+           "decode", "lib_path"]
+
+LIGHTNING, GDN, KDA = 0, 1, 2
+L2NORM_QK, BETA_LOGIT = 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB
+
+
+def build() -> str:
+    """Compile oracle.c with gcc (no fast-math) into liboracle.so."""
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall",
+                    "-Wextra", "-o", tmp, _SRC, "-lm"], check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        # LA_ORACLE_LIB points the pins at a deliberately broken oracle build
+        # (tests/test_oracle_mutations.py); normally it is unset.
+        path = os.environ.get("LA_ORACLE_LIB")
+        if not path:
+            path = _LIB
+            if (not os.path.exists(_LIB)
+                    or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
+                build()
+        lib = ctypes.CDLL(path)
+        dp = ctypes.POINTER(ctypes.c_double)
+        ip = ctypes.POINTER(ctypes.c_int32)
+        lib.oracle_decode.restype = ctypes.c_int
+        lib.oracle_decode.argtypes = (
+            [ctypes.c_int] * 8 + [dp] * 5 + [ctypes.c_int, dp, dp, ip, ip,
+                                             dp, dp])
+        _lib = lib
+    return _lib
+
+
+def _f64(x):
+    """Exact conversion to a contiguous float64 numpy array."""
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor: bf16/fp32 -> fp64 is exact
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _i32(x):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu").numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _ptr(a, ctype):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def decode(variant, q, k, v, g, beta, pool, read_idx, write_idx=None,
+           flags=0, inter=False):
+    """Run the fp64 recurrence.
+
+    q, k: [B,T,H,K]; v: [B,T,HV,V]; g: Lightning [HV] decay factors or None,
+    GDN [B,T,HV], KDA [B,T,HV,K] log-decay; beta: [B,T,HV] or None
+    (Lightning); pool: logical [pool_size,HV,V,K]; read_idx/write_idx: [B].
+
+    Returns a dict with ``out`` [B,T,HV,V], ``pool`` (the pool after the
+    call, float64) and ``inter`` ([B,T,HV,V,K] or None).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    g, beta = _f64(g), _f64(beta)
+    pool_in = _f64(pool)
+    ridx, widx = _i32(read_idx), _i32(write_idx)
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    pool_size = pool_in.shape[0]
+    if k.shape != q.shape or v.shape[:2] != (B, T):
+        raise ValueError("q/k/v shapes disagree")
+    if pool_in.shape[1:] != (HV, V, K):
+        raise ValueError("pool shape %s != [pool_size,%d,%d,%d]"
+                         % (pool_in.shape, HV, V, K))
+    if ridx.shape != (B,) or (widx is not None and widx.shape != (B,)):
+        raise ValueError("index shape")
+    if variant != LIGHTNING and (g is None or beta is None):
+        raise ValueError("GDN/KDA need g and beta")
+    expect_g = {LIGHTNING: (HV,), GDN: (B, T, HV), KDA: (B, T, HV, K)}
+    if g is not None and g.shape != expect_g[variant]:
+        raise ValueError("g shape %s != %s" % (g.shape, expect_g[variant]))
+    if beta is not None and variant != LIGHTNING and beta.shape != (B, T, HV):
+        raise ValueError("beta shape")
+    pool_out = pool_in.copy()
+    # NaN until the oracle writes it: a position it skips cannot pass as 0
+    out = np.full((B, T, HV, V), np.nan, dtype=np.float64)
+    inter_a = np.zeros((B, T, HV, V, K), dtype=np.float64) if inter else None
+    dp = ctypes.c_double
+    rc = _load().oracle_decode(
+        variant, B, T, H, HV, K, V, flags, _ptr(q, dp), _ptr(k, dp),
+        _ptr(v, dp), _ptr(g, dp),
+        _ptr(beta if variant != LIGHTNING else None, dp), pool_size,
+        _ptr(pool_in, dp), _ptr(pool_out, dp), _ptr(ridx, ctypes.c_int32),
+        _ptr(widx, ctypes.c_int32), _ptr(out, dp), _ptr(inter_a, dp))
+    if rc != 0:
+        raise ValueError("oracle_decode rejected its arguments (rc=%d)" % rc)
+    return {"out": out, "pool": pool_out, "inter": inter_a}

@@ -1,0 +1,209 @@
+/*
+ * oracle.c -- plain fp64 CPU reference for pool-indexed recurrent-state decode
+ * of linear attention: Lightning, gated delta rule (GDN) and Kimi delta
+ * attention (KDA).
+ *
+ * TEST INFRASTRUCTURE. This file is the parity oracle. Only the test suite,
+ * the smoke check and the benchmark's CPU-baseline leg may load or call it.
+ * It shares no code, header, table or helper with the GPU library, and the
+ * GPU library never calls it.
+ *
+ * It evaluates the recurrence directly, one request and one value head at a
+ * time, one token after another, in scalar double-precision loops with no
+ * blocking, fusion or reordering. Where it follows the pages:
+ *
+ *  - "[Triton/Gluon] Fused Gluon KDA decode path (950/1250)" (ROCm/aiter
+ *    PR #4584), advisory review, summary paragraph: per token the state is
+ *    decayed by exp(g_t), then corrected by beta_t * k_t (x) (v_t - S^T k_t),
+ *    and the token's output is S^T q_t with the updated state; q/k l2norm and
+ *    the beta sigmoid are fused into that kernel's prologue.
+ *  - "fix: wire h0_indices into Lightning Attention decode for state-pool
+ *    indexing" (cuLA PR #75), Description / What changed: request i reads and
+ *    writes pool row h0_indices[i] * HV + hv, not the batch position.
+ *  - FlashInfer "fp32 sibling of #3268" description (4D pool
+ *    [pool_size, HV, V, K]; "Separate read/write slots"; "API change -- one
+ *    new argument"): the write slot defaults to the read slot and a negative
+ *    write slot skips the writeback; a negative read slot is padding
+ *    ("read-side -1 padding semantics").
+ *
+ * Storage orientation: the pool stores each state tile as S[v][k] with k
+ * contiguous (the [pool_size, HV, V, K] layout). The pages write the update
+ * with the mathematical state as K x V (S^T k); in storage that read-out is
+ * the row-wise dot product u[v] = sum_k S[v][k] * k[k].
+ *
+ * Readings where the pages are silent (each is listed with its reason in the
+ * design notes of the repository):
+ *  - Lightning: the pages name the operation only. The update is the
+ *    decay-masked linear-attention recurrence S <- lambda_h * S + v k^T,
+ *    o = S q, with the standard per-head decay lambda_h = exp(-2^(-8(h+1)/H))
+ *    over the value heads when no decay array is given.
+ *  - g is a log-decay: GDN alpha = exp(g) (scalar per token and value head),
+ *    KDA e = exp(g) (one factor per key channel).
+ *  - l2norm is x / sqrt(sum x^2 + 1e-6).
+ *  - Value head hv uses q/k head h = hv / (HV / H).
+ *  - A padded request (negative read slot) writes zeros to its outputs and
+ *    touches neither the pool nor the intermediate cache.
+ *  - The intermediate cache entry [b, t, hv] is the state after token t,
+ *    written for every active request whatever its write slot.
+ *  - All reads see the pool as it was before the call (pool_in); all writes
+ *    go to pool_out.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_LIGHTNING 0
+#define ORACLE_GDN 1
+#define ORACLE_KDA 2
+
+#define ORACLE_L2NORM_QK 1
+#define ORACLE_BETA_LOGIT 2
+
+#define ORACLE_L2NORM_EPS 1e-6
+
+/* x <- x / sqrt(sum x^2 + eps): the in-kernel l2norm of the KDA page. */
+static void l2_normalise(double *x, int n)
+{
+    double ss = 0.0;
+    for (int i = 0; i < n; ++i)
+        ss += x[i] * x[i];
+    double inv = 1.0 / sqrt(ss + ORACLE_L2NORM_EPS);
+    for (int i = 0; i < n; ++i)
+        x[i] *= inv;
+}
+
+/* The standard Lightning Attention per-head decay. */
+static double lightning_decay(int head, int num_heads)
+{
+    return exp(-pow(2.0, -8.0 * (double)(head + 1) / (double)num_heads));
+}
+
+/*
+ * Returns 0 on success, -1 on a bad argument, -2 if memory ran out.
+ *
+ * Layouts (all contiguous, row-major):
+ *   q, k      [B][T][H][K]
+ *   v         [B][T][HV][V]
+ *   g         Lightning: [HV] decay factors, or NULL for lightning_decay();
+ *             GDN: [B][T][HV] log-decay; KDA: [B][T][HV][K] log-decay
+ *   beta      [B][T][HV] (GDN, KDA); ignored for Lightning
+ *   pool_in   [pool_size][HV][V][K]  the pool before the call (read only)
+ *   pool_out  [pool_size][HV][V][K]  holds a copy of pool_in on entry;
+ *                                    write slots are overwritten
+ *   read_idx, write_idx  [B]; write_idx may be NULL (= read_idx)
+ *   out       [B][T][HV][V]
+ *   inter     [B][T][HV][V][K] or NULL
+ */
+int oracle_decode(int variant, int B, int T, int H, int HV, int K, int V,
+                  int flags, const double *q, const double *k, const double *v,
+                  const double *g, const double *beta, int pool_size,
+                  const double *pool_in, double *pool_out,
+                  const int32_t *read_idx, const int32_t *write_idx,
+                  double *out, double *inter)
+{
+    if (B < 0 || T < 1 || H < 1 || HV < 1 || K < 1 || V < 1 || HV % H != 0)
+        return -1;
+    if (variant != ORACLE_LIGHTNING && variant != ORACLE_GDN &&
+        variant != ORACLE_KDA)
+        return -1;
+
+    const size_t tile = (size_t)V * (size_t)K;
+    double *S = (double *)malloc(tile * sizeof(double));
+    double *qv = (double *)malloc((size_t)K * sizeof(double));
+    double *kv = (double *)malloc((size_t)K * sizeof(double));
+    if (!S || !qv || !kv) {
+        free(S);
+        free(qv);
+        free(kv);
+        return -2;
+    }
+    const int group = HV / H;
+
+    for (int b = 0; b < B; ++b) {
+        const int r = read_idx[b];
+        const int w = write_idx ? write_idx[b] : r;
+        if (r >= pool_size || w >= pool_size) {
+            free(S);
+            free(qv);
+            free(kv);
+            return -1;
+        }
+        for (int hv = 0; hv < HV; ++hv) {
+            if (r < 0) {
+                /* padded request: zero outputs, nothing else */
+                for (int t = 0; t < T; ++t)
+                    for (int i = 0; i < V; ++i)
+                        out[(((size_t)b * T + t) * HV + hv) * V + i] = 0.0;
+                continue;
+            }
+            const int h = hv / group;
+            memcpy(S, pool_in + ((size_t)r * HV + hv) * tile,
+                   tile * sizeof(double));
+
+            for (int t = 0; t < T; ++t) {
+                const size_t qk_off = (((size_t)b * T + t) * H + h) * K;
+                const size_t v_off = (((size_t)b * T + t) * HV + hv) * V;
+                const size_t bt = ((size_t)b * T + t) * HV + hv;
+                memcpy(qv, q + qk_off, (size_t)K * sizeof(double));
+                memcpy(kv, k + qk_off, (size_t)K * sizeof(double));
+                if (flags & ORACLE_L2NORM_QK) {
+                    l2_normalise(qv, K);
+                    l2_normalise(kv, K);
+                }
+                const double *vv = v + v_off;
+
+                if (variant == ORACLE_LIGHTNING) {
+                    const double lam = g ? g[hv] : lightning_decay(hv, HV);
+                    /* S <- lambda * S + v k^T */
+                    for (int i = 0; i < V; ++i)
+                        for (int j = 0; j < K; ++j)
+                            S[(size_t)i * K + j] =
+                                lam * S[(size_t)i * K + j] + vv[i] * kv[j];
+                } else {
+                    double bb = beta[bt];
+                    if (flags & ORACLE_BETA_LOGIT)
+                        bb = 1.0 / (1.0 + exp(-bb));
+                    /* decay: S <- alpha S (GDN) or S <- S diag(exp g) (KDA) */
+                    if (variant == ORACLE_GDN) {
+                        const double alpha = exp(g[bt]);
+                        for (size_t e = 0; e < tile; ++e)
+                            S[e] *= alpha;
+                    } else {
+                        const double *gk = g + bt * (size_t)K;
+                        for (int i = 0; i < V; ++i)
+                            for (int j = 0; j < K; ++j)
+                                S[(size_t)i * K + j] *= exp(gk[j]);
+                    }
+                    /* delta rule: S <- S + beta (v - S k) k^T, one row at a
+                     * time (row i's read-out uses only row i) */
+                    for (int i = 0; i < V; ++i) {
+                        double u = 0.0;
+                        for (int j = 0; j < K; ++j)
+                            u += S[(size_t)i * K + j] * kv[j];
+                        const double c = bb * (vv[i] - u);
+                        for (int j = 0; j < K; ++j)
+                            S[(size_t)i * K + j] += c * kv[j];
+                    }
+                }
+                /* o = S q with the updated state */
+                for (int i = 0; i < V; ++i) {
+                    double o = 0.0;
+                    for (int j = 0; j < K; ++j)
+                        o += S[(size_t)i * K + j] * qv[j];
+                    out[v_off + i] = o;
+                }
+                if (inter)
+                    memcpy(inter + bt * tile, S, tile * sizeof(double));
+            }
+            if (w >= 0)
+                memcpy(pool_out + ((size_t)w * HV + hv) * tile, S,
+                       tile * sizeof(double));
+        }
+    }
+    free(S);
+    free(qv);
+    free(kv);
+    return 0;
+}

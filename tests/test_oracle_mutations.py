@@ -1,0 +1,58 @@
+"""The oracle pins must fail on a broken oracle.
+
+Each case plants one plausible mistake in a copy of oracle.c (CPU only),
+builds it, and runs the pin suite against it; the suite has to fail.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTATIONS = {
+    "no_gdn_decay": ("S[e] *= alpha;", "S[e] *= 1.0;"),
+    "delta_sign": ("const double c = bb * (vv[i] - u);",
+                   "const double c = bb * (u - vv[i]);"),
+    "lightning_outer_transposed": (
+        "lam * S[(size_t)i * K + j] + vv[i] * kv[j];",
+        "lam * S[(size_t)i * K + j] + vv[j % V] * kv[i % K];"),
+    "gva_head_map": ("const int h = hv / group;", "const int h = hv % H;"),
+    "kda_decay_on_rows": ("S[(size_t)i * K + j] *= exp(gk[j]);",
+                          "S[(size_t)i * K + j] *= exp(gk[i % K]);"),
+    "write_to_read_slot": (
+        "memcpy(pool_out + ((size_t)w * HV + hv) * tile, S,",
+        "memcpy(pool_out + ((size_t)r * HV + hv) * tile, S,"),
+    "lightning_decay_index": ("pow(2.0, -8.0 * (double)(head + 1)",
+                              "pow(2.0, -8.0 * (double)(head)"),
+    "padded_output_not_zeroed": (
+        "out[(((size_t)b * T + t) * HV + hv) * V + i] = 0.0;", ";"),
+    "beta_sigmoid_missing": ("bb = 1.0 / (1.0 + exp(-bb));", "bb = bb;"),
+    "output_reads_key": ("o += S[(size_t)i * K + j] * qv[j];",
+                         "o += S[(size_t)i * K + j] * kv[j];"),
+    "readout_before_decay": (
+        "u += S[(size_t)i * K + j] * kv[j];",
+        "u += S[(size_t)i * K + j] / (variant == ORACLE_GDN ? exp(g[bt]) "
+        ": exp(g[bt * (size_t)K + j])) * kv[j];"),
+    "l2norm_skipped_for_k": ("l2_normalise(kv, K);", ";"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTATIONS[name]
+    text = open(SRC).read()
+    assert text.count(old) >= 1, "mutation anchor not found: " + old
+    src = tmp_path / "oracle_mut.c"
+    src.write_text(text.replace(old, new, 1))
+    lib = tmp_path / "liboracle_mut.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o",
+                    str(lib), str(src), "-lm"], check=True)
+    env = dict(os.environ, LA_ORACLE_LIB=str(lib))
+    proc = subprocess.run(
+        [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+         os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+        env=env, cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert proc.returncode != 0, "pins did not catch " + name

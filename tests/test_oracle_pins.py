@@ -1,0 +1,392 @@
+"""Pins of the fp64 oracle to facts fixed outside the oracle itself.
+
+Each test checks the oracle against something other than its own code: hand
+derivations, exact rational brute force in a different formulation, closed
+forms, invariants of the delta rule, special cases that reduce to a library
+routine, and equivariances of the slot indexing. A plausible mistake (a
+dropped decay, a sign, a transposed tile, a wrong head or slot index, an
+update applied after instead of before the read-out) fails at least one.
+"""
+import json
+import math
+import os
+from fractions import Fraction as F
+
+import numpy as np
+import pytest
+import scipy.special
+
+import brute_rational as br
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+VARIANTS = {"lightning": oracle.LIGHTNING, "gdn": oracle.GDN, "kda": oracle.KDA}
+
+
+def _frac(x):
+    return F(x) if not isinstance(x, str) else F(x)
+
+
+def _rel(a, b):
+    a, b = np.asarray(a, float), np.asarray(b, float)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+# ---------------------------------------------------------------- golden
+
+
+def _golden_cases():
+    with open(os.path.join(GOLDEN, "hand_worked_k2.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
+def test_hand_worked_examples(case):
+    var = case["variant"]
+    toks = case["tokens"]
+    T = len(toks)
+    S0 = np.array(case["S0"], dtype=float)
+    V, K = S0.shape
+    q = np.array([[[float(_frac(x)) for x in t["q"]]] for t in toks])[None]
+    k = np.array([[[float(_frac(x)) for x in t["k"]]] for t in toks])[None]
+    v = np.array([[[float(_frac(x)) for x in t["v"]]] for t in toks])[None]
+    if var == "lightning":
+        g = np.array([float(_frac(toks[0]["lam"]))])
+        beta = None
+    elif var == "gdn":
+        g = np.array([[[math.log(float(_frac(t["alpha"])))] for t in toks]])
+        beta = np.array([[[float(_frac(t["beta"]))] for t in toks]])
+    else:
+        g = np.array([[[[math.log(float(_frac(x))) for x in t["e"]]]
+                       for t in toks]])
+        beta = np.array([[[float(_frac(t["beta"]))] for t in toks]])
+    pool = np.random.default_rng(0).normal(size=(case["pool_size"], 1, V, K))
+    r, w = case["read_idx"][0], case["write_idx"][0]
+    pool[r, 0] = S0
+    res = oracle.decode(VARIANTS[var], q, k, v, g, beta, pool,
+                        case["read_idx"], case["write_idx"], inter=True)
+    want_out = np.array([[float(_frac(x)) for x in o] for o in case["outputs"]])
+    want_S = np.array([[float(_frac(x)) for x in row]
+                       for row in case["final_state"]])
+    assert _rel(res["out"][0, :, 0, :], want_out) < 1e-14
+    assert _rel(res["pool"][w, 0], want_S) < 1e-14
+    assert _rel(res["inter"][0, T - 1, 0], want_S) < 1e-14
+    for s in range(case["pool_size"]):
+        if s != w:
+            assert np.array_equal(res["pool"][s], pool[s])
+
+
+# ------------------------------------------------------ rational brute force
+
+
+def _dyadic(rng, shape, scale=16, lo=-16, hi=17):
+    """Random dyadic rationals m/scale: exact in fp64."""
+    return rng.integers(lo, hi, size=shape) / scale
+
+
+def _to_frac(a):
+    return [_to_frac(x) for x in a] if isinstance(a, (list, np.ndarray)) \
+        else F(float(a))
+
+
+@pytest.mark.parametrize("variant", ["lightning", "gdn", "kda"])
+@pytest.mark.parametrize("V,K", [(4, 4), (3, 5), (5, 3)])
+@pytest.mark.parametrize("T", [1, 2, 3])
+def test_rational_brute_force(variant, V, K, T):
+    """fp64 oracle vs exact product-form evaluation, several requests in a
+    larger pool with permuted read slots, separate and skipped writes."""
+    rng = np.random.default_rng(1000 * V + 10 * K + T + len(variant))
+    B, H, HV, pool_size = 3, 1, 2, 6
+    read_idx, write_idx = [4, 0, 2], [1, -1, 5]
+    pool = _dyadic(rng, (pool_size, HV, V, K))
+    q = _dyadic(rng, (B, T, H, K))
+    k = _dyadic(rng, (B, T, H, K), lo=-8, hi=9)
+    v = _dyadic(rng, (B, T, HV, V))
+    if variant == "lightning":
+        lam = rng.integers(1, 17, size=HV) / 16
+        g, beta = lam, None
+    elif variant == "gdn":
+        alpha = rng.integers(1, 17, size=(B, T, HV)) / 16
+        g, beta = np.log(alpha), rng.integers(0, 9, size=(B, T, HV)) / 8
+    else:
+        e = rng.integers(1, 17, size=(B, T, HV, K)) / 16
+        g, beta = np.log(e), rng.integers(0, 9, size=(B, T, HV)) / 8
+    res = oracle.decode(VARIANTS[variant], q, k, v, g, beta, pool, read_idx,
+                        write_idx, inter=True)
+    for b in range(B):
+        for hv in range(HV):
+            toks = []
+            for t in range(T):
+                tok = dict(q=_to_frac(q[b, t, 0]), k=_to_frac(k[b, t, 0]),
+                           v=_to_frac(v[b, t, hv]))
+                if variant == "lightning":
+                    tok["lam"] = F(float(lam[hv]))
+                elif variant == "gdn":
+                    tok["alpha"] = F(float(alpha[b, t, hv]))
+                    tok["beta"] = F(float(beta[b, t, hv]))
+                else:
+                    tok["e"] = _to_frac(e[b, t, hv])
+                    tok["beta"] = F(float(beta[b, t, hv]))
+                toks.append(tok)
+            outs, states = br.run(variant, _to_frac(pool[read_idx[b], hv]),
+                                  toks)
+            scale = max(1.0, max(abs(float(x)) for st in states
+                                 for row in st for x in row))
+            for t in range(T):
+                o = np.array([float(x) for x in outs[t]])
+                st = np.array([[float(x) for x in row] for row in states[t]])
+                assert np.max(np.abs(res["out"][b, t, hv] - o)) <= 1e-14 * scale * K
+                assert np.max(np.abs(res["inter"][b, t, hv] - st)) <= 1e-14 * scale
+            if write_idx[b] >= 0:
+                assert np.max(np.abs(res["pool"][write_idx[b], hv] - st)) \
+                    <= 1e-14 * scale
+    # slots 0, 3 and the read-only slots stay as they were
+    for s in (0, 3, 4, 2):
+        if s not in write_idx:
+            assert np.array_equal(res["pool"][s], pool[s])
+
+
+# ------------------------------------------------------------- invariants
+
+
+def _random_case(rng, variant, B=2, T=3, H=2, HV=2, K=8, V=6, pool_size=5):
+    pool = rng.normal(size=(pool_size, HV, V, K)) * 0.3
+    q = rng.normal(size=(B, T, H, K))
+    k = rng.normal(size=(B, T, H, K))
+    v = rng.normal(size=(B, T, HV, V))
+    if variant == oracle.LIGHTNING:
+        g, beta = rng.uniform(0.5, 1.0, size=HV), None
+    elif variant == oracle.GDN:
+        g, beta = rng.uniform(-1, 0, size=(B, T, HV)), rng.normal(size=(B, T, HV))
+    else:
+        g = rng.uniform(-1, 0, size=(B, T, HV, K))
+        beta = rng.normal(size=(B, T, HV))
+    return dict(q=q, k=k, v=v, g=g, beta=beta, pool=pool)
+
+
+@pytest.mark.parametrize("variant", [oracle.GDN, oracle.KDA])
+def test_delta_rule_writes_value_at_unit_key(variant):
+    """beta = 1 and |k| = 1: after the update S k = v, whatever the decay."""
+    rng = np.random.default_rng(7)
+    B, T, H, HV, K, V = 2, 1, 1, 3, 16, 12
+    c = _random_case(rng, variant, B=B, T=T, H=H, HV=HV, K=K, V=V)
+    k = c["k"] / np.linalg.norm(c["k"], axis=-1, keepdims=True)
+    beta = np.ones((B, T, HV))
+    res = oracle.decode(variant, c["q"], k, c["v"], c["g"], beta, c["pool"],
+                        [1, 3], inter=True)
+    for b in range(B):
+        for hv in range(HV):
+            S = res["inter"][b, 0, hv]
+            assert _rel(S @ k[b, 0, 0], c["v"][b, 0, hv]) < 1e-12
+    # exact with a coordinate key: column j of the new state equals v
+    kj = np.zeros_like(k)
+    kj[..., 5] = 1.0
+    res = oracle.decode(variant, c["q"], kj, c["v"], c["g"], beta, c["pool"],
+                        [1, 3], inter=True)
+    for b in range(B):
+        for hv in range(HV):
+            assert _rel(res["inter"][b, 0, hv][:, 5], c["v"][b, 0, hv]) < 1e-15
+
+
+@pytest.mark.parametrize("variant", [oracle.GDN, oracle.KDA])
+def test_zero_beta_zero_gate_is_identity(variant):
+    rng = np.random.default_rng(8)
+    c = _random_case(rng, variant)
+    g = np.zeros_like(c["g"])
+    beta = np.zeros_like(c["beta"])
+    res = oracle.decode(variant, c["q"], c["k"], c["v"], g, beta, c["pool"],
+                        [3, 0], inter=True)
+    for b, r in enumerate([3, 0]):
+        for hv in range(2):
+            S0 = c["pool"][r, hv]
+            np.testing.assert_array_equal(res["pool"][r, hv], S0)
+            h = hv // 1
+            for t in range(3):
+                np.testing.assert_allclose(res["out"][b, t, hv],
+                                           S0 @ c["q"][b, t, h], rtol=1e-14)
+
+
+def test_lightning_closed_form():
+    """Unrolled Lightning recurrence = decay-masked linear attention:
+    o_t = lam^(t+1) S0 q_t + sum_{s<=t} lam^(t-s) (k_s . q_t) v_s and
+    S_T = lam^T S0 + sum_t lam^(T-1-t) v_t k_t^T."""
+    rng = np.random.default_rng(9)
+    B, T, H, K, V = 1, 8, 3, 16, 12
+    c = _random_case(rng, oracle.LIGHTNING, B=B, T=T, H=H, HV=H, K=K, V=V,
+                     pool_size=2)
+    lam = c["g"]
+    res = oracle.decode(oracle.LIGHTNING, c["q"], c["k"], c["v"], lam, None,
+                        c["pool"], [1])
+    for h in range(H):
+        Q, Kt, Vt = c["q"][0, :, h], c["k"][0, :, h], c["v"][0, :, h]
+        S0 = c["pool"][1, h]
+        ts = np.arange(T)
+        mask = np.tril(lam[h] ** (ts[:, None] - ts[None, :]).astype(float))
+        A = (Q @ Kt.T) * mask                        # [T, T]
+        want = A @ Vt + (lam[h] ** (ts + 1))[:, None] * (Q @ S0.T)
+        assert _rel(res["out"][0, :, h], want) < 1e-13
+        ST = lam[h] ** T * S0 + (Vt.T * lam[h] ** (T - 1 - ts)) @ Kt
+        assert _rel(res["pool"][1, h], ST) < 1e-13
+
+
+def test_lightning_builtin_decay_schedule():
+    """No decay array: head h of H decays by exp(-2^(-8(h+1)/H))."""
+    H, K, V = 8, 4, 4
+    pool = np.ones((1, H, V, K))
+    z = np.zeros((1, 1, H, K))
+    res = oracle.decode(oracle.LIGHTNING, z, z, np.zeros((1, 1, H, V)), None,
+                        None, pool, [0])
+    # exp(-1/2) and exp(-1/256), written out
+    assert abs(res["pool"][0, 0, 0, 0] - 0.6065306597126334) < 1e-15
+    assert abs(res["pool"][0, 7, 0, 0] - 0.9961013694701175) < 1e-15
+    vals = res["pool"][0, :, 0, 0]
+    assert np.all(np.diff(vals) > 0)
+
+
+def test_kda_constant_gate_equals_gdn():
+    rng = np.random.default_rng(10)
+    c = _random_case(rng, oracle.GDN)
+    gk = np.repeat(c["g"][..., None], c["q"].shape[-1], axis=-1)
+    a = oracle.decode(oracle.GDN, c["q"], c["k"], c["v"], c["g"], c["beta"],
+                      c["pool"], [2, 4], flags=oracle.BETA_LOGIT)
+    b = oracle.decode(oracle.KDA, c["q"], c["k"], c["v"], gk, c["beta"],
+                      c["pool"], [2, 4], flags=oracle.BETA_LOGIT)
+    assert _rel(b["out"], a["out"]) < 1e-14
+    assert _rel(b["pool"], a["pool"]) < 1e-14
+
+
+def test_gdn_zero_beta_is_pure_decay():
+    rng = np.random.default_rng(11)
+    c = _random_case(rng, oracle.GDN, B=1, T=4, H=1, HV=1)
+    beta = np.zeros((1, 4, 1))
+    res = oracle.decode(oracle.GDN, c["q"], c["k"], c["v"], c["g"], beta,
+                        c["pool"], [2], inter=True)
+    S0 = c["pool"][2, 0]
+    cum = np.cumsum(c["g"][0, :, 0])
+    for t in range(4):
+        assert _rel(res["inter"][0, t, 0], math.exp(cum[t]) * S0) < 1e-14
+        assert _rel(res["out"][0, t, 0], math.exp(cum[t]) * (S0 @ c["q"][0, t, 0])) < 1e-13
+
+
+def test_ungated_delta_rule_orthonormal_keys():
+    """g = 0, beta = 1 and orthonormal keys: every token's value is stored
+    exactly at its key and directions orthogonal to all keys keep S0."""
+    rng = np.random.default_rng(12)
+    K, V, T = 8, 5, 4
+    Qm, _ = np.linalg.qr(rng.normal(size=(K, K)))
+    keys = Qm[:, :T].T                                # [T, K]
+    v = rng.normal(size=(1, T, 1, V))
+    pool = rng.normal(size=(1, 1, V, K))
+    res = oracle.decode(oracle.GDN, rng.normal(size=(1, T, 1, K)),
+                        keys[None, :, None, :], v, np.zeros((1, T, 1)),
+                        np.ones((1, T, 1)), pool, [0])
+    S = res["pool"][0, 0]
+    for t in range(T):
+        assert _rel(S @ keys[t], v[0, t, 0]) < 1e-12
+    for j in range(T, K):
+        assert _rel(S @ Qm[:, j], pool[0, 0] @ Qm[:, j]) < 1e-12
+
+
+@pytest.mark.parametrize("variant", [oracle.LIGHTNING, oracle.GDN, oracle.KDA])
+def test_token_split_equals_multi_token(variant):
+    """T single-token calls chained through the pool = one T-token call."""
+    rng = np.random.default_rng(13)
+    c = _random_case(rng, variant, T=4)
+    flags = 0 if variant == oracle.LIGHTNING else oracle.BETA_LOGIT
+    whole = oracle.decode(variant, c["q"], c["k"], c["v"], c["g"], c["beta"],
+                          c["pool"], [1, 4], flags=flags, inter=True)
+    pool = c["pool"]
+    for t in range(4):
+        sl = slice(t, t + 1)
+        g = c["g"] if variant == oracle.LIGHTNING else c["g"][:, sl]
+        beta = None if c["beta"] is None else c["beta"][:, sl]
+        step = oracle.decode(variant, c["q"][:, sl], c["k"][:, sl],
+                             c["v"][:, sl], g, beta, pool, [1, 4], flags=flags)
+        assert _rel(step["out"][:, 0], whole["out"][:, t]) < 1e-14
+        pool = step["pool"]
+    assert _rel(pool, whole["pool"]) < 1e-14
+
+
+def test_grouped_value_heads_equal_repeated_qk():
+    """HV = 2H with value head hv reading q/k head hv // 2 is the H = HV run
+    with q and k repeated along heads."""
+    rng = np.random.default_rng(14)
+    c = _random_case(rng, oracle.GDN, H=2, HV=4)
+    a = oracle.decode(oracle.GDN, c["q"], c["k"], c["v"], c["g"], c["beta"],
+                      c["pool"], [0, 3], flags=oracle.L2NORM_QK)
+    q2 = np.repeat(c["q"], 2, axis=2)
+    k2 = np.repeat(c["k"], 2, axis=2)
+    b = oracle.decode(oracle.GDN, q2, k2, c["v"], c["g"], c["beta"],
+                      c["pool"], [0, 3], flags=oracle.L2NORM_QK)
+    np.testing.assert_array_equal(a["out"], b["out"])
+    np.testing.assert_array_equal(a["pool"], b["pool"])
+
+
+@pytest.mark.parametrize("pattern", [
+    ("identity", 4, [0, 1, 2, 3]),
+    ("non_identity", 6, [2, 0, 5, 1]),
+    ("reversed", 4, [3, 2, 1, 0]),
+])
+def test_slot_indexing_equals_direct_evaluation(pattern):
+    """Index patterns of the cuLA pool tests: request b's result equals a
+    one-request call on its own slot, and only written slots change."""
+    _, pool_size, ridx = pattern
+    rng = np.random.default_rng(15)
+    c = _random_case(rng, oracle.GDN, B=4, pool_size=pool_size)
+    whole = oracle.decode(oracle.GDN, c["q"], c["k"], c["v"], c["g"],
+                          c["beta"], c["pool"], ridx, inter=True)
+    for b in range(4):
+        sl = slice(b, b + 1)
+        one = oracle.decode(oracle.GDN, c["q"][sl], c["k"][sl], c["v"][sl],
+                            c["g"][sl], c["beta"][sl],
+                            c["pool"][ridx[b]:ridx[b] + 1], [0], inter=True)
+        np.testing.assert_array_equal(whole["out"][b], one["out"][0])
+        np.testing.assert_array_equal(whole["pool"][ridx[b]], one["pool"][0])
+    for s in range(pool_size):
+        if s not in ridx:
+            np.testing.assert_array_equal(whole["pool"][s], c["pool"][s])
+
+
+def test_padding_and_skipped_writes():
+    rng = np.random.default_rng(16)
+    c = _random_case(rng, oracle.KDA, B=3, pool_size=6)
+    res = oracle.decode(oracle.KDA, c["q"], c["k"], c["v"], c["g"], c["beta"],
+                        c["pool"], [2, -1, 5], [1, 3, -1], inter=True)
+    # padded request: zero outputs, no cache rows, no pool write
+    assert not res["out"][1].any()
+    assert not res["inter"][1].any()
+    # skipped write: outputs and cache are still computed
+    assert np.abs(res["out"][2]).max() > 0 and np.abs(res["inter"][2]).max() > 0
+    changed = [s for s in range(6)
+               if not np.array_equal(res["pool"][s], c["pool"][s])]
+    assert changed == [1]
+    np.testing.assert_array_equal(res["pool"][1], res["inter"][0, -1])
+
+
+def test_l2norm_and_beta_logit_flags():
+    rng = np.random.default_rng(17)
+    c = _random_case(rng, oracle.GDN)
+    qn = c["q"] / np.linalg.norm(c["q"], axis=-1, keepdims=True)
+    kn = c["k"] / np.linalg.norm(c["k"], axis=-1, keepdims=True)
+    ref = oracle.decode(oracle.GDN, qn, kn, c["v"], c["g"],
+                        scipy.special.expit(c["beta"]), c["pool"], [0, 1])
+    # large scales make the 1e-6 guard under the square root negligible
+    got = oracle.decode(oracle.GDN, 1000.0 * c["q"], 300.0 * c["k"], c["v"],
+                        c["g"], c["beta"], c["pool"], [0, 1],
+                        flags=oracle.L2NORM_QK | oracle.BETA_LOGIT)
+    assert _rel(got["out"], ref["out"]) < 1e-10
+    assert _rel(got["pool"], ref["pool"]) < 1e-10
+
+
+def test_l2norm_of_zero_vectors_stays_finite():
+    """A zero key leaves the decayed state without a delta write and a zero
+    query gives a zero output: the guard under the square root keeps both
+    finite."""
+    rng = np.random.default_rng(18)
+    c = _random_case(rng, oracle.GDN, B=1, T=1, H=1, HV=1)
+    z = np.zeros_like(c["q"])
+    res = oracle.decode(oracle.GDN, z, z, c["v"], c["g"], c["beta"],
+                        c["pool"], [2], flags=oracle.L2NORM_QK)
+    assert not res["out"].any()
+    alpha = math.exp(c["g"][0, 0, 0])
+    assert _rel(res["pool"][2, 0], alpha * c["pool"][2, 0]) < 1e-15

@@ -1,0 +1,223 @@
+"""Seeded synthetic inputs for pool-indexed recurrent-state decode.
+
+This module draws random inputs and builds index tables. It holds none of the
+decode method's arithmetic; the GPU library and the CPU oracle each consume
+what it returns. Every tensor is drawn on the CPU from a
+``torch.Generator().manual_seed(seed)`` in a fixed order: pool, q, k, v, g,
+beta logit, indices.
+
+Shapes and distributions follow the workloads the source pages describe
+(cuLA "fix: wire h0_indices into Lightning Attention decode for state-pool
+indexing", Tests; FlashInfer "fp32 sibling of #3268", Tests; aiter "Fused
+Gluon KDA decode path (950/1250)", review): pools larger than the batch with
+random distinct slots, multi-token verify with separate write slots and
+negative entries, strided pools cut from an oversized buffer, per-key-channel
+gates.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import torch
+
+LIGHTNING, GDN, KDA = "lightning", "gdn", "kda"
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    variant: str
+    B: int
+    T: int
+    H: int
+    HV: int
+    K: int
+    V: int
+    pool_size: int
+    l2norm: bool
+    beta_logit: bool
+    q: torch.Tensor            # [B,T,H,K]
+    k: torch.Tensor            # [B,T,H,K]
+    v: torch.Tensor            # [B,T,HV,V]
+    g: Optional[torch.Tensor]  # lightning [HV] decay factors or None;
+    #                            gdn [B,T,HV]; kda [B,T,HV,K] (log-decay)
+    beta: Optional[torch.Tensor]  # [B,T,HV] (logits when beta_logit)
+    backing: torch.Tensor      # fp32 [stride_mult*pool_size, HV, V, K]
+    stride_mult: int
+    read_idx: torch.Tensor     # int32 [B]
+    write_idx: Optional[torch.Tensor]  # int32 [B] or None (= read_idx)
+    inter: bool                # cache the state after every token
+    out_dtype: torch.dtype = torch.float32
+
+    def pool(self, backing: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """The logical pool [pool_size, HV, V, K]: every stride_mult-th slot
+        of the backing buffer (a strided view when stride_mult > 1)."""
+        b = self.backing if backing is None else backing
+        return b[:: self.stride_mult]
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.T
+
+    def to(self, device) -> "Workload":
+        """A copy with every tensor moved to ``device``."""
+        moved = {}
+        for f in dataclasses.fields(self):
+            val = getattr(self, f.name)
+            moved[f.name] = val.to(device) if isinstance(val, torch.Tensor) else val
+        return Workload(**moved)
+
+    def state_bytes(self) -> int:
+        """Algorithmic state bytes one call must move: one read and one
+        write per active (request, value head) tile, plus one cache write
+        per token when intermediate states are kept."""
+        tile = self.V * self.K * 4
+        ridx = self.read_idx.tolist()
+        widx = self.write_idx.tolist() if self.write_idx is not None else ridx
+        reads = sum(1 for r in ridx if r >= 0)
+        writes = sum(1 for r, w in zip(ridx, widx) if r >= 0 and w >= 0)
+        total = (reads + writes) * self.HV * tile
+        if self.inter:
+            total += reads * self.T * self.HV * tile
+        return total
+
+    def io_bytes(self) -> int:
+        """Algorithmic bytes of everything except the state: q, k, v, gates,
+        beta, indices and outputs."""
+        act = self.q.element_size()
+        B, T, H, HV, K, V = self.B, self.T, self.H, self.HV, self.K, self.V
+        n = 2 * B * T * H * K * act + B * T * HV * V * act
+        if self.variant == GDN:
+            n += B * T * HV * 4
+        elif self.variant == KDA:
+            n += B * T * HV * K * 4
+        elif self.g is not None:
+            n += HV * 4
+        if self.beta is not None:
+            n += B * T * HV * 4
+        n += B * 4 * (2 if self.write_idx is not None else 1)
+        out_size = torch.empty((), dtype=self.out_dtype).element_size()
+        n += B * T * HV * V * out_size
+        return n
+
+
+def _randperm(n, gen):
+    return torch.randperm(n, generator=gen)
+
+
+def make(name, variant, B, T, H, HV, K, V, pool_size, *, seed,
+         act_dtype=torch.bfloat16, pool_std=0.05, g_low=-1.0, g_high=0.0,
+         l2norm=True, beta_logit=True, stride_mult=1, read_idx=None,
+         write_idx=None, separate_write=False, write_skip=0.0,
+         inter=False, lightning_decay=None, out_dtype=torch.float32):
+    """Draw one workload.
+
+    read_idx: explicit list, or None for ``randperm(pool_size)[:B]``.
+    write_idx: explicit list, or None: equal to read_idx unless
+    ``separate_write`` (then B slots drawn from the slots no request reads,
+    and a ``write_skip`` fraction of them set to -1).
+    """
+    gen = torch.Generator().manual_seed(seed)
+    backing = torch.randn((stride_mult * pool_size, HV, V, K),
+                          generator=gen, dtype=torch.float32) * pool_std
+    q = torch.randn((B, T, H, K), generator=gen).to(act_dtype)
+    k = torch.randn((B, T, H, K), generator=gen).to(act_dtype)
+    v = torch.randn((B, T, HV, V), generator=gen).to(act_dtype)
+    if variant == LIGHTNING:
+        g = lightning_decay
+        beta = None
+    else:
+        gshape = (B, T, HV) if variant == GDN else (B, T, HV, K)
+        g = g_low + (g_high - g_low) * torch.rand(gshape, generator=gen)
+        beta = torch.randn((B, T, HV), generator=gen)
+    perm = _randperm(pool_size, gen)
+    if read_idx is None:
+        if B > pool_size:
+            raise ValueError("need pool_size >= B for distinct slots")
+        ridx = perm[:B].to(torch.int32)
+    else:
+        ridx = torch.tensor(read_idx, dtype=torch.int32)
+    if write_idx is not None:
+        widx = torch.tensor(write_idx, dtype=torch.int32)
+    elif separate_write:
+        used = set(ridx.tolist())
+        free = [s for s in perm.tolist() if s not in used]
+        if len(free) < B:
+            raise ValueError("not enough free slots for separate writes")
+        widx = torch.tensor(free[:B], dtype=torch.int32)
+        n_skip = int(round(write_skip * B))
+        if n_skip:
+            drop = _randperm(B, gen)[:n_skip]
+            widx[drop] = -1
+    else:
+        widx = None
+    return Workload(name=name, variant=variant, B=B, T=T, H=H, HV=HV, K=K,
+                    V=V, pool_size=pool_size, l2norm=l2norm,
+                    beta_logit=beta_logit if variant != LIGHTNING else False,
+                    q=q, k=k, v=v, g=g, beta=beta, backing=backing,
+                    stride_mult=stride_mult, read_idx=ridx, write_idx=widx,
+                    inter=inter, out_dtype=out_dtype)
+
+
+# The named workloads. Each is the shape, distribution and index structure of
+# one decode setting; the seed is fixed per workload.
+
+def gdn_small_k64(seed=1):
+    """GDN single-token decode, fp32 throughout: B=4 requests in a pool of 6
+    at slots [2,0,5,1] (the cuLA pool test's non-identity offsets), H=HV=2,
+    K=V=64, pool ~N(0,0.1), g ~U(-1,0), beta logit ~N(0,1), q/k
+    l2-normalised in the kernel."""
+    return make("gdn_small_k64", GDN, B=4, T=1, H=2, HV=2, K=64, V=64,
+                pool_size=6, seed=seed, act_dtype=torch.float32,
+                pool_std=0.1, g_low=-1.0, g_high=0.0, read_idx=[2, 0, 5, 1])
+
+
+def lightning_b33_h64(seed=2):
+    """Lightning decode: B=33 requests at random distinct slots of a pool of
+    40 (the cuLA big-batch pool test), H=64, K=V=128, T=1, bf16 q/k/v
+    ~N(0,1) unnormalised, pool ~N(0,0.05), built-in per-head decay."""
+    return make("lightning_b33_h64", LIGHTNING, B=33, T=1, H=64, HV=64,
+                K=128, V=128, pool_size=40, seed=seed, l2norm=False)
+
+
+def gdn_gva_b64(seed=3):
+    """GDN grouped-value decode: B=64, 16 q/k heads, 32 value heads,
+    K=V=128, T=1, pool of 128 with random distinct slots, bf16 q/k/v,
+    in-kernel l2norm, beta logit ~N(0,1), g ~U(-0.5,0), pool ~N(0,0.05)."""
+    return make("gdn_gva_b64", GDN, B=64, T=1, H=16, HV=32, K=128, V=128,
+                pool_size=128, seed=seed, g_low=-0.5, g_high=0.0)
+
+
+def gdn_mtp_b32_t4(seed=4):
+    """GDN multi-token verify: B=32, T=4, H=16, HV=32, K=V=128; the pool of
+    96 slots is every second slot of a [192,32,128,128] buffer; write slots
+    are disjoint from read slots, 25% of them -1; every token's state is
+    cached to a [B,T,HV,V,K] buffer."""
+    return make("gdn_mtp_b32_t4", GDN, B=32, T=4, H=16, HV=32, K=128, V=128,
+                pool_size=96, seed=seed, g_low=-0.5, g_high=0.0,
+                stride_mult=2, separate_write=True, write_skip=0.25,
+                inter=True)
+
+
+def kda_b256(T, seed=5):
+    """KDA decode with a per-key-channel gate: B=256, H=HV=24, K=V=128,
+    g in R^K per (token, head) ~U(-1,0), in-kernel l2norm and beta sigmoid,
+    pool of 512 with random distinct slots, bf16 q/k/v."""
+    return make("kda_b256_t%d" % T, KDA, B=256, T=T, H=24, HV=24, K=128,
+                V=128, pool_size=512, seed=seed, g_low=-1.0, g_high=0.0)
+
+
+NAMED = {
+    "gdn_small_k64": gdn_small_k64,
+    "lightning_b33_h64": lightning_b33_h64,
+    "gdn_gva_b64": gdn_gva_b64,
+    "gdn_mtp_b32_t4": gdn_mtp_b32_t4,
+    "kda_b256_t1": lambda seed=5: kda_b256(1, seed),
+    "kda_b256_t8": lambda seed=5: kda_b256(8, seed),
+}
+
+
+def named(name: str, seed: Optional[int] = None) -> Workload:
+    fn = NAMED[name]
+    return fn() if seed is None else fn(seed=seed)
