@@ -1,0 +1,177 @@
+/*
+ * la_decode.h -- C ABI of the MI355X (gfx950) pool-indexed recurrent-state
+ * decode library for linear attention: Lightning, gated delta rule (GDN) and
+ * Kimi delta attention (KDA).
+ *
+ * What a call computes. For every request b and value head hv:
+ *   1. r = read_idx[b], w = write_idx ? write_idx[b] : r.
+ *      r < 0 marks a padded request: its outputs are set to 0 and neither
+ *      the pool nor the intermediate cache is read or written.
+ *   2. S = pool[r, hv] (a V x K fp32 tile, k contiguous).
+ *   3. For t = 0..T-1 (tokens in order), with q/k head h = hv / (HV / H):
+ *        Lightning:  S <- lambda[hv] * S + v_t k_t^T
+ *        GDN:        S <- exp(g[b,t,hv]) * S
+ *                    S <- S + beta_t (v_t - S k_t) k_t^T
+ *        KDA:        S <- S diag(exp(g[b,t,hv,:]))
+ *                    S <- S + beta_t (v_t - S k_t) k_t^T
+ *        out[b,t,hv,:] = S q_t   (with the updated S)
+ *        inter[b,t,hv] = S       (when an intermediate cache is given)
+ *   4. If w >= 0: pool[w, hv] = S, in place.
+ *
+ * Sources (page titles and sections):
+ *  - "fix: wire h0_indices into Lightning Attention decode for state-pool
+ *    indexing" (cuLA PR #75), Description: the state is read and written
+ *    through the per-request slot index (row h0_indices[i] * HV + hv of the
+ *    pool), and the grid covers the active requests, not the pool rows.
+ *  - FlashInfer "fp32 sibling of #3268" (gated_delta_rule_mtp), Description
+ *    items 1-2, "Before vs after", "API change -- one new argument": 4D pool
+ *    [pool_size, HV, V, K] read and written in place through its strides
+ *    (never a silent copy); an optional separate write-slot array that
+ *    defaults to the read slots, negative entries skipping the writeback;
+ *    multi-token (MTP) verify with optional per-token state caching.
+ *  - FlashInfer packed-QKV fix, Description: q/k/v may be head-dim slices of
+ *    one fused buffer (non-compact strides), with results identical to
+ *    contiguous inputs.
+ *  - "[Triton/Gluon] Fused Gluon KDA decode path (950/1250)" (ROCm/aiter PR
+ *    #4584), advisory review: the per-token update and output above, with
+ *    q/k l2norm, the beta sigmoid and the gate fused into the kernel; and the
+ *    reviewer's lesson that ambiguous or inconsistent arguments must be
+ *    rejected, not silently reinterpreted.
+ *
+ * Conventions for every entry point:
+ *  - All data pointers are DEVICE pointers; the caller owns every buffer.
+ *    The library never allocates, copies, reshapes or synchronises, and
+ *    keeps no state between calls.
+ *  - Strides are in elements (not bytes), must be >= 0, and the innermost
+ *    dimension of every tensor has stride 1.
+ *  - The call is asynchronous on `stream` (a hipStream_t, NULL = the null
+ *    stream). Argument checks run on the host before anything is launched:
+ *    on any error status nothing is launched and no byte is touched.
+ *  - B == 0 is a no-op returning LA_OK.
+ *  - Device preconditions, not checked on the hot path (la_check_indices
+ *    checks them): read and write slots are < pool_size; the non-negative
+ *    write slots are distinct; no request's write slot equals another
+ *    request's read slot (all reads are meant to see the pool as it was
+ *    before the call). Breaking them is undefined behaviour.
+ *  - Calls on different streams may run concurrently when their write slots
+ *    are disjoint from each other's read and write slots.
+ */
+#ifndef LA_DECODE_H
+#define LA_DECODE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum la_status {
+    LA_OK = 0,
+    LA_ERR_NULL = 1,        /* a required pointer is NULL                    */
+    LA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent        */
+    LA_ERR_STRIDE = 3,      /* negative stride, innermost stride != 1, or
+                               overlapping pool tiles                        */
+    LA_ERR_ALIGN = 4,       /* pool / cache row not 16-byte aligned, or an
+                               activation not aligned to its element size    */
+    LA_ERR_DTYPE = 5,       /* unknown dtype code                            */
+    LA_ERR_ARG = 6,         /* argument inconsistent with the entry point
+                               (e.g. beta or flags given to la_decode, an
+                               unknown flag bit)                             */
+    LA_ERR_UNSUPPORTED = 7, /* K or V not in {64, 128}                        */
+    LA_ERR_LAUNCH = 8       /* the HIP runtime refused the launch            */
+} la_status;
+
+typedef enum la_dtype {
+    LA_F32 = 0,
+    LA_BF16 = 1
+} la_dtype;
+
+/* flags (GDN and KDA only; la_decode requires flags == 0) */
+#define LA_F_L2NORM_QK 0x1u  /* q, k <- x / sqrt(sum x^2 + 1e-6) per head */
+#define LA_F_BETA_LOGIT 0x2u /* beta holds logits; beta <- 1/(1+exp(-x))  */
+
+/* Element strides of an activation tensor [B, T, heads, (inner)]. */
+typedef struct la_act_strides {
+    int64_t b, t, h;
+} la_act_strides;
+
+/* Element strides of the state pool [pool_size, HV, V, K]; K stride is 1. */
+typedef struct la_pool_strides {
+    int64_t slot, head, row;
+} la_pool_strides;
+
+typedef struct la_decode_args {
+    int32_t B;         /* requests in the batch, >= 0                       */
+    int32_t T;         /* tokens per request, >= 1                          */
+    int32_t H;         /* q/k heads, >= 1                                   */
+    int32_t HV;        /* value heads = state tiles per slot; HV % H == 0   */
+    int32_t K;         /* key width: 64 or 128                              */
+    int32_t V;         /* value width: 64 or 128                            */
+    int32_t pool_size; /* slots in the pool, >= 1                           */
+    uint32_t flags;    /* LA_F_* bits                                       */
+    la_dtype qkv_dtype; /* dtype of q, k, v                                 */
+    la_dtype out_dtype; /* dtype of out                                     */
+
+    const void *q;     /* [B, T, H, K]   */
+    la_act_strides sq;
+    const void *k;     /* [B, T, H, K]   */
+    la_act_strides sk;
+    const void *v;     /* [B, T, HV, V]  */
+    la_act_strides sv;
+    /* Decay input, fp32:
+     *   la_decode:      lambda[HV] decay factors (contiguous), or NULL for
+     *                   lambda[hv] = exp(-2^(-8 (hv+1) / HV)); sg unused
+     *   gdn_decode_mtp: g[B, T, HV] log-decay (sg.b, sg.t, sg.h)
+     *   kda_decode_mtp: g[B, T, HV, K] log-decay, K stride 1               */
+    const float *g;
+    la_act_strides sg;
+    /* beta[B, T, HV] fp32 (GDN, KDA; logits when LA_F_BETA_LOGIT);
+     * must be NULL for la_decode */
+    const float *beta;
+    la_act_strides sbeta;
+
+    float *pool;       /* [pool_size, HV, V, K] fp32, updated in place;
+                          base and every row start 16-byte aligned         */
+    la_pool_strides sp;
+    const int32_t *read_idx;  /* [B] contiguous                             */
+    const int32_t *write_idx; /* [B] contiguous, or NULL (= read_idx)       */
+    float *inter;      /* [B, T, HV, V, K] contiguous fp32, or NULL         */
+    void *out;         /* [B, T, HV, V] in out_dtype                        */
+    la_act_strides so;
+} la_decode_args;
+
+/* Lightning decode (cuLA page): S <- lambda_h S + v k^T, o = S q.
+ * Requires beta == NULL and flags == 0. */
+la_status la_decode(const la_decode_args *args, void *stream);
+
+/* Gated delta rule decode, single- or multi-token (FlashInfer
+ * gated_delta_rule_mtp page): scalar decay exp(g) then the delta update. */
+la_status gdn_decode_mtp(const la_decode_args *args, void *stream);
+
+/* KDA decode (aiter KDA page): per-key-channel decay exp(g[:]) then the
+ * delta update. */
+la_status kda_decode_mtp(const la_decode_args *args, void *stream);
+
+/* Debug validator of the device preconditions above (the aiter review's
+ * failure modes: slots out of range, snapshots written into other
+ * sequences' slots). Writes a bit set to *dev_result (device int32):
+ *   1 = a read slot >= pool_size,  2 = a write slot >= pool_size,
+ *   4 = two requests write the same slot,
+ *   8 = a request writes a slot another request reads.
+ * 0 means the index set is valid. write_idx may be NULL (= read_idx).
+ * Asynchronous on `stream`; B == 0 writes 0. */
+la_status la_check_indices(int32_t B, int32_t pool_size,
+                           const int32_t *read_idx, const int32_t *write_idx,
+                           int32_t *dev_result, void *stream);
+
+/* Static description of a status code; never NULL. */
+const char *la_status_string(la_status status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int32_t la_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LA_DECODE_H */

@@ -1,0 +1,11 @@
+"""Pool-indexed recurrent-state decode for linear attention on MI355X.
+
+Hand-written gfx950 HIP kernels behind a C ABI (include/la_decode.h), with a
+thin ctypes binding. Entry points: la_decode (Lightning), gdn_decode_mtp
+(gated delta rule), kda_decode_mtp (Kimi delta attention), check_indices.
+"""
+from ._binding import (DecodeArgs, LaDecodeError, check_indices,
+                       gdn_decode_mtp, kda_decode_mtp, la_decode, lib)
+
+__all__ = ["DecodeArgs", "LaDecodeError", "check_indices", "gdn_decode_mtp",
+           "kda_decode_mtp", "la_decode", "lib"]

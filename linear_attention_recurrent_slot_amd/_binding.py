@@ -1,0 +1,278 @@
+"""ctypes binding of libla_decode.so (argument marshalling only).
+
+Every function here reads pointers, strides and dtypes off torch tensors,
+fills the C argument struct of include/la_decode.h and calls the library on
+the current HIP stream. No step of the decode runs in Python, and there is
+no fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libla_decode.so")
+
+# la_status
+LA_OK = 0
+STATUS_NAMES = {0: "LA_OK", 1: "LA_ERR_NULL", 2: "LA_ERR_SHAPE",
+                3: "LA_ERR_STRIDE", 4: "LA_ERR_ALIGN", 5: "LA_ERR_DTYPE",
+                6: "LA_ERR_ARG", 7: "LA_ERR_UNSUPPORTED", 8: "LA_ERR_LAUNCH"}
+# la_dtype
+LA_F32, LA_BF16 = 0, 1
+# flags
+LA_F_L2NORM_QK, LA_F_BETA_LOGIT = 0x1, 0x2
+
+ENTRY_POINTS = ("la_decode", "gdn_decode_mtp", "kda_decode_mtp")
+
+
+class ActStrides(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int64), ("t", ctypes.c_int64),
+                ("h", ctypes.c_int64)]
+
+
+class PoolStrides(ctypes.Structure):
+    _fields_ = [("slot", ctypes.c_int64), ("head", ctypes.c_int64),
+                ("row", ctypes.c_int64)]
+
+
+class DecodeArgs(ctypes.Structure):
+    """Mirror of la_decode_args."""
+    _fields_ = [
+        ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+        ("HV", ctypes.c_int32), ("K", ctypes.c_int32), ("V", ctypes.c_int32),
+        ("pool_size", ctypes.c_int32), ("flags", ctypes.c_uint32),
+        ("qkv_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+        ("q", ctypes.c_void_p), ("sq", ActStrides),
+        ("k", ctypes.c_void_p), ("sk", ActStrides),
+        ("v", ctypes.c_void_p), ("sv", ActStrides),
+        ("g", ctypes.c_void_p), ("sg", ActStrides),
+        ("beta", ctypes.c_void_p), ("sbeta", ActStrides),
+        ("pool", ctypes.c_void_p), ("sp", PoolStrides),
+        ("read_idx", ctypes.c_void_p), ("write_idx", ctypes.c_void_p),
+        ("inter", ctypes.c_void_p),
+        ("out", ctypes.c_void_p), ("so", ActStrides),
+    ]
+
+
+class LaDecodeError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__("%s: %s (%s)" % (what, STATUS_NAMES.get(status, status),
+                                          status_string(status)))
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libla_decode.so is not built (expected at %s); run "
+                "__graft_entry__.build() or python -m "
+                "linear_attention_recurrent_slot_amd.build" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        for name in ENTRY_POINTS:
+            fn = getattr(L, name)
+            fn.restype = ctypes.c_int
+            fn.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]
+        L.la_check_indices.restype = ctypes.c_int
+        L.la_check_indices.argtypes = [ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p]
+        L.la_status_string.restype = ctypes.c_char_p
+        L.la_status_string.argtypes = [ctypes.c_int]
+        L.la_version.restype = ctypes.c_int32
+        L.la_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().la_status_string(status).decode()
+
+
+def call(entry: str, args: DecodeArgs, stream=None) -> int:
+    """Raw C-ABI call; returns the la_status code."""
+    return getattr(lib(), entry)(ctypes.byref(args), _stream_handle(stream))
+
+
+def _stream_handle(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(stream)
+
+
+def _dtype_code(t: torch.Tensor, what: str) -> int:
+    if t.dtype == torch.float32:
+        return LA_F32
+    if t.dtype == torch.bfloat16:
+        return LA_BF16
+    raise TypeError("%s must be float32 or bfloat16, got %s" % (what, t.dtype))
+
+
+def _act(t: torch.Tensor, ndim: int, what: str):
+    if t.dim() != ndim:
+        raise ValueError("%s must have %d dims, got %s" % (what, ndim,
+                                                           tuple(t.shape)))
+    if ndim == 4 and t.stride(3) != 1:
+        raise ValueError("%s: innermost stride must be 1" % what)
+    s = t.stride()
+    return ctypes.c_void_p(t.data_ptr()), ActStrides(s[0], s[1], s[2])
+
+
+def _idx(t):
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or t.dim() != 1 or t.stride(0) != 1:
+        raise ValueError("slot indices must be contiguous 1-D int32")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def build_args(variant: str, q, k, v, g, beta, pool, read_idx, write_idx,
+               out, inter, flags: int) -> DecodeArgs:
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q must be [B,T,H,K] and v [B,T,HV,V]")
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    if pool.dim() != 4 or pool.dtype != torch.float32 or pool.stride(3) != 1:
+        raise ValueError("pool must be a float32 [pool_size, HV, V, K] tensor "
+                         "with unit innermost stride")
+    # The library sees raw pointers: every extent it will index is checked
+    # here against the tensors that back it.
+    want = {"k": (k, (B, T, H, K)), "v": (v, (B, T, HV, V)),
+            "out": (out, (B, T, HV, V)), "read_idx": (read_idx, (B,))}
+    if tuple(pool.shape[1:]) != (HV, V, K):
+        raise ValueError("pool shape %s does not match [*, %d, %d, %d]"
+                         % (tuple(pool.shape), HV, V, K))
+    if write_idx is not None:
+        want["write_idx"] = (write_idx, (B,))
+    if beta is not None:
+        want["beta"] = (beta, (B, T, HV))
+    if g is not None:
+        want["g"] = (g, {"lightning": (HV,), "gdn": (B, T, HV),
+                         "kda": (B, T, HV, K)}[variant])
+    if inter is not None:
+        want["inter"] = (inter, (B, T, HV, V, K))
+    dev = pool.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a HIP device")
+    for name, (t, shape) in want.items():
+        if tuple(t.shape) != shape:
+            raise ValueError("%s shape %s != %s" % (name, tuple(t.shape), shape))
+        if t.device != dev:
+            raise ValueError("%s is on %s, pool on %s" % (name, t.device, dev))
+    if q.device != dev:
+        raise ValueError("q is on %s, pool on %s" % (q.device, dev))
+    a = DecodeArgs()
+    a.B, a.T, a.H, a.HV, a.K, a.V = B, T, H, HV, K, V
+    a.pool_size = pool.shape[0]
+    a.flags = flags
+    a.qkv_dtype = _dtype_code(q, "q")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    a.out_dtype = _dtype_code(out, "out")
+    a.q, a.sq = _act(q, 4, "q")
+    a.k, a.sk = _act(k, 4, "k")
+    a.v, a.sv = _act(v, 4, "v")
+    if g is not None:
+        if g.dtype != torch.float32:
+            raise TypeError("g must be float32")
+        if variant == "lightning":
+            if g.dim() != 1 or g.stride(0) != 1:
+                raise ValueError("lambda must be a contiguous [HV] tensor")
+            a.g = ctypes.c_void_p(g.data_ptr())
+        elif variant == "gdn":
+            if g.dim() != 3:
+                raise ValueError("gdn g must be [B, T, HV]")
+            a.g = ctypes.c_void_p(g.data_ptr())
+            a.sg = ActStrides(*g.stride())
+        else:
+            a.g, a.sg = _act(g, 4, "g")
+    if beta is not None:
+        if beta.dtype != torch.float32 or beta.dim() != 3:
+            raise ValueError("beta must be float32 [B, T, HV]")
+        a.beta = ctypes.c_void_p(beta.data_ptr())
+        a.sbeta = ActStrides(*beta.stride())
+    a.pool = ctypes.c_void_p(pool.data_ptr())
+    a.sp = PoolStrides(*pool.stride()[:3])
+    a.read_idx = _idx(read_idx)
+    a.write_idx = _idx(write_idx)
+    if inter is not None:
+        if (inter.dtype != torch.float32 or not inter.is_contiguous()
+                or tuple(inter.shape) != (B, T, HV, V, K)):
+            raise ValueError("inter must be contiguous float32 [B,T,HV,V,K]")
+        a.inter = ctypes.c_void_p(inter.data_ptr())
+    a.out, a.so = _act(out, 4, "out")
+    return a
+
+
+def _run(variant, entry, q, k, v, g, beta, pool, read_idx, write_idx, out,
+         inter, flags, out_dtype, stream):
+    B, T = q.shape[0], q.shape[1]
+    HV, V, K = v.shape[2], v.shape[3], q.shape[3]
+    if out is None:
+        out = torch.empty((B, T, HV, V), dtype=out_dtype, device=q.device)
+    if inter is True:
+        inter = torch.empty((B, T, HV, V, K), dtype=torch.float32,
+                            device=q.device)
+    elif inter is False:
+        inter = None
+    args = build_args(variant, q, k, v, g, beta, pool, read_idx, write_idx,
+                      out, inter, flags)
+    st = call(entry, args, stream)
+    if st != LA_OK:
+        raise LaDecodeError(st, entry)
+    return out, inter
+
+
+def la_decode(q, k, v, pool, read_idx, write_idx=None, *, lam=None, out=None,
+              inter=None, out_dtype=torch.float32, stream=None):
+    """Lightning decode. lam: optional float32 [HV] decay factors (default:
+    exp(-2^(-8(h+1)/HV)) per value head). Returns (out, inter)."""
+    return _run("lightning", "la_decode", q, k, v, lam, None, pool, read_idx,
+                write_idx, out, inter, 0, out_dtype, stream)
+
+
+def gdn_decode_mtp(q, k, v, g, beta, pool, read_idx, write_idx=None, *,
+                   out=None, inter=None, l2norm_qk=False, beta_logit=False,
+                   out_dtype=torch.float32, stream=None):
+    """Gated delta rule decode over T tokens. g: [B,T,HV] log-decay;
+    beta: [B,T,HV] (logits if beta_logit). Returns (out, inter)."""
+    flags = (LA_F_L2NORM_QK if l2norm_qk else 0) | \
+        (LA_F_BETA_LOGIT if beta_logit else 0)
+    return _run("gdn", "gdn_decode_mtp", q, k, v, g, beta, pool, read_idx,
+                write_idx, out, inter, flags, out_dtype, stream)
+
+
+def kda_decode_mtp(q, k, v, g, beta, pool, read_idx, write_idx=None, *,
+                   out=None, inter=None, l2norm_qk=False, beta_logit=False,
+                   out_dtype=torch.float32, stream=None):
+    """KDA decode over T tokens. g: [B,T,HV,K] per-key-channel log-decay.
+    Returns (out, inter)."""
+    flags = (LA_F_L2NORM_QK if l2norm_qk else 0) | \
+        (LA_F_BETA_LOGIT if beta_logit else 0)
+    return _run("kda", "kda_decode_mtp", q, k, v, g, beta, pool, read_idx,
+                write_idx, out, inter, flags, out_dtype, stream)
+
+
+def check_indices(read_idx, write_idx, pool_size, result=None, stream=None):
+    """Launch the index validator; returns the device int32 result tensor
+    (bits: 1 read out of range, 2 write out of range, 4 duplicate write,
+    8 write into another request's read slot)."""
+    if result is None:
+        result = torch.empty((1,), dtype=torch.int32, device=read_idx.device)
+    st = lib().la_check_indices(read_idx.shape[0], pool_size, _idx(read_idx),
+                                _idx(write_idx),
+                                ctypes.c_void_p(result.data_ptr()),
+                                _stream_handle(stream))
+    if st != LA_OK:
+        raise LaDecodeError(st, "la_check_indices")
+    return result

@@ -1,0 +1,728 @@
+// la_decode.hip -- gfx950 kernels and C-ABI entry points for pool-indexed
+// recurrent-state decode of linear attention (Lightning, GDN, KDA).
+//
+// The operation, argument layouts and error behaviour are specified in
+// include/la_decode.h. The sources it follows:
+//  - cuLA "fix: wire h0_indices into Lightning Attention decode for
+//    state-pool indexing", Description: state read/written through the
+//    request's slot index; grid over the active (request, head) units.
+//  - FlashInfer "fp32 sibling of #3268", Description and "API change": 4D
+//    pool [pool_size, HV, V, K] addressed in place through its strides,
+//    separate write slots (negative = skip), multi-token verify with
+//    optional per-token state caching.
+//  - aiter "Fused Gluon KDA decode path (950/1250)", advisory review: the
+//    per-token update (decay by exp(g), delta correction, output S^T q with
+//    the updated state) with l2norm, sigmoid and gate fused into the kernel.
+//
+// Kernel design (gfx950, wave64):
+//  - One workgroup per (request, value head) pair; V/32 waves, each owning
+//    32 rows of the V x K fp32 state tile for the whole call. The tile is
+//    held in VGPRs across all T tokens, so the pool sees one read and at most
+//    one write per pair per call.
+//  - Within a wave, 8 lanes share one row: lane (c, r) with c = lane & 7 and
+//    r = lane >> 3 holds rows {32 w + 8 i + r} and the 16-byte column chunks
+//    {c + 8 m}. Each global_load_dwordx4 of the wave reads 8 whole 128-byte
+//    row segments; every byte of the tile is read once and written once.
+//  - Row dot products (S k and S q) reduce over the 8 lanes of a row with
+//    three DPP butterfly adds; the butterfly leaves a bit-identical sum in
+//    all 8 lanes, so the rank-1 update needs no broadcast.
+//  - The per-token prologue (l2norm of q and k, beta sigmoid, exp of the
+//    gate, the k.q product, v) is computed once per workgroup for up to 8
+//    tokens at a time, one token per wave, and staged in LDS.
+//  - No MFMA: per token the work is two matrix-vector products and a rank-1
+//    update against one vector operand, bound by HBM traffic of the state.
+//  - Per token and element: one multiply (decay), two FMAs (read-outs) and
+//    one FMA (update); Lightning needs no key read-out.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "la_decode.h"
+
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+enum Variant { VAR_LA = 0, VAR_GDN = 1, VAR_KDA = 2 };
+
+constexpr int kRowsPerWave = 32;
+constexpr int kTokChunk = 8;
+constexpr float kL2Eps = 1e-6f;
+
+struct Params {
+    int32_t B, T, HV, group;  // group = HV / H
+    uint32_t flags;
+    int32_t pad_;
+    const void *q;
+    int64_t sq_b, sq_t, sq_h;
+    const void *k;
+    int64_t sk_b, sk_t, sk_h;
+    const void *v;
+    int64_t sv_b, sv_t, sv_h;
+    const float *g;
+    int64_t sg_b, sg_t, sg_h;
+    const float *beta;
+    int64_t sb_b, sb_t, sb_h;
+    float *pool;
+    int64_t sp_slot, sp_head, sp_row;
+    const int32_t *ridx;
+    const int32_t *widx;
+    float *inter;
+    void *out;
+    int64_t so_b, so_t, so_h;
+};
+
+// ---------------------------------------------------------------- helpers
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h)
+{
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float x)
+{
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load_act(const void *base, int64_t i)
+{
+    if constexpr (BF16)
+        return bf16_to_f32(static_cast<const uint16_t *>(base)[i]);
+    else
+        return static_cast<const float *>(base)[i];
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_out(void *base, int64_t i, float x)
+{
+    if constexpr (BF16)
+        static_cast<uint16_t *>(base)[i] = f32_to_bf16(x);
+    else
+        static_cast<float *>(base)[i] = x;
+}
+
+// DPP lane moves inside groups of 8 lanes (bound_ctrl on, all rows/banks).
+__device__ __forceinline__ float dpp_xor1(float x)
+{
+    return __int_as_float(
+        __builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp_xor2(float x)
+{
+    return __int_as_float(
+        __builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp_half_mirror(float x)
+{
+    return __int_as_float(
+        __builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));
+}
+
+// Sum over the 8 lanes (lane & ~7) .. (lane | 7). Each step adds a lane
+// pair's values in both lanes, so all 8 lanes end with the same bits.
+__device__ __forceinline__ float sum8(float x)
+{
+    x += dpp_xor1(x);
+    x += dpp_xor2(x);
+    x += dpp_half_mirror(x);
+    return x;
+}
+
+// Sum over the whole wave (prologue only).
+__device__ __forceinline__ float wave_sum(float x)
+{
+    x = sum8(x);
+    x += __shfl_xor(x, 8);
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+__device__ __forceinline__ f4 load_nt(const float *p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const f4 *>(p));
+}
+
+__device__ __forceinline__ void store_nt(float *p, f4 x)
+{
+    __builtin_nontemporal_store(x, reinterpret_cast<f4 *>(p));
+}
+
+// LDS-only barrier: orders LDS traffic across the workgroup without
+// waiting for outstanding global loads (the state tile may still be in
+// flight while the prologue runs).
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// LDS record of one token: k^[K], q^[K], (KDA: e[K]), v[V] (rows permuted so
+// each lane's rows are adjacent), and 4 scalars (beta, decay, k^.q^, pad).
+template <int VAR, int K, int V>
+struct TokLayout {
+    static constexpr int kOff = 0;
+    static constexpr int qOff = K;
+    static constexpr int eOff = 2 * K;
+    static constexpr int vOff = (VAR == VAR_KDA ? 3 : 2) * K;
+    static constexpr int sOff = vOff + V;
+    static constexpr int size = sOff + 4;  // floats; a multiple of 4
+};
+
+// Position of state row `row` inside the LDS v record: the rows a lane owns
+// (32 w + 8 i + r, i = 0..3) sit at 32 w + 4 r + i.
+__device__ __forceinline__ int v_slot(int row)
+{
+    const int w = row >> 5, i = (row >> 3) & 3, r = row & 7;
+    return (w << 5) + (r << 2) + i;
+}
+
+// Prologue of token t for one wave: fills the LDS record `rec`.
+template <int VAR, int K, int V, bool BF16IN>
+__device__ __forceinline__ void token_prologue(const Params &p, int b, int hv,
+                                               int t, float *rec, int lane)
+{
+    using L = TokLayout<VAR, K, V>;
+    constexpr int EPL = K / 64;  // key elements per lane
+    constexpr int VPL = V / 64;  // value elements per lane
+    const int h = hv / p.group;
+    const int64_t qo = b * p.sq_b + t * p.sq_t + h * p.sq_h;
+    const int64_t ko = b * p.sk_b + t * p.sk_t + h * p.sk_h;
+    float qx[EPL], kx[EPL];
+    float ssq = 0.f, ssk = 0.f, qk = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int j = lane * EPL + i;
+        qx[i] = load_act<BF16IN>(p.q, qo + j);
+        kx[i] = load_act<BF16IN>(p.k, ko + j);
+        ssq = fmaf(qx[i], qx[i], ssq);
+        ssk = fmaf(kx[i], kx[i], ssk);
+        qk = fmaf(qx[i], kx[i], qk);
+    }
+    float rq = 1.f, rk = 1.f;
+    qk = wave_sum(qk);
+    if (p.flags & LA_F_L2NORM_QK) {
+        ssq = wave_sum(ssq);
+        ssk = wave_sum(ssk);
+        rq = __frsqrt_rn(ssq + kL2Eps);
+        rk = __frsqrt_rn(ssk + kL2Eps);
+    }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int j = lane * EPL + i;
+        rec[L::kOff + j] = kx[i] * rk;
+        rec[L::qOff + j] = qx[i] * rq;
+    }
+    const int64_t vo = b * p.sv_b + t * p.sv_t + hv * p.sv_h;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int j = lane * VPL + i;
+        rec[L::vOff + v_slot(j)] = load_act<BF16IN>(p.v, vo + j);
+    }
+    const int64_t go = b * p.sg_b + t * p.sg_t + hv * p.sg_h;
+    if constexpr (VAR == VAR_KDA) {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int j = lane * EPL + i;
+            rec[L::eOff + j] = __expf(p.g[go + j]);
+        }
+    }
+    if (lane == 0) {
+        float beta = 1.f, decay;
+        if constexpr (VAR == VAR_LA) {
+            decay = p.g ? p.g[hv]
+                        : __expf(-exp2f(-8.f * static_cast<float>(hv + 1) /
+                                        static_cast<float>(p.HV)));
+        } else {
+            const float x = p.beta[b * p.sb_b + t * p.sb_t + hv * p.sb_h];
+            beta = (p.flags & LA_F_BETA_LOGIT) ? 1.f / (1.f + __expf(-x)) : x;
+            decay = (VAR == VAR_GDN) ? __expf(p.g[go]) : 1.f;
+        }
+        rec[L::sOff + 0] = beta;
+        rec[L::sOff + 1] = decay;
+        rec[L::sOff + 2] = qk * rq * rk;
+        rec[L::sOff + 3] = 0.f;
+    }
+}
+
+template <int VAR, int K, int V, bool BF16IN, bool BF16OUT>
+__global__ void __launch_bounds__((V / kRowsPerWave) * 64)
+decode_kernel(const Params p)
+{
+    extern __shared__ f4 lds_raw[];
+    float *lds = reinterpret_cast<float *>(lds_raw);
+    using L = TokLayout<VAR, K, V>;
+    constexpr int NW = V / kRowsPerWave;  // waves per workgroup
+    constexpr int RPL = kRowsPerWave / 8;  // rows per lane
+    constexpr int CPL = K / 32;            // 16-byte chunks per lane and row
+
+    const int pair = blockIdx.x;
+    const int b = pair / p.HV;
+    const int hv = pair - b * p.HV;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int c8 = lane & 7;
+    const int rs = lane >> 3;
+    const int T = p.T;
+
+    const int r = p.ridx[b];
+    const int w = p.widx ? p.widx[b] : r;
+
+    // Output row written by this lane (lanes with c8 < RPL cover the wave's
+    // 32 rows exactly once): row 32 wave + 8 c8 + rs.
+    const int orow = wave * kRowsPerWave + (c8 & (RPL - 1)) * 8 + rs;
+    const bool olane = c8 < RPL;
+    const int64_t obase = b * p.so_b + hv * p.so_h + orow;
+
+    if (r < 0) {  // padded request: zero outputs, touch nothing else
+        if (olane)
+            for (int t = 0; t < T; ++t)
+                store_out<BF16OUT>(p.out, obase + t * p.so_t, 0.f);
+        return;
+    }
+
+    // Gather the tile rows this lane owns (128-bit, streamed).
+    const float *src = p.pool + r * p.sp_slot + hv * p.sp_head;
+    f4 S[RPL][CPL];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+        const int row = wave * kRowsPerWave + i * 8 + rs;
+#pragma unroll
+        for (int m = 0; m < CPL; ++m)
+            S[i][m] = load_nt(src + row * p.sp_row + 4 * (c8 + 8 * m));
+    }
+
+    for (int t0 = 0; t0 < T; t0 += kTokChunk) {
+        const int nt = min(kTokChunk, T - t0);
+        if (t0 > 0)
+            lds_barrier();  // every wave is done with the previous chunk
+        for (int tt = wave; tt < nt; tt += NW)
+            token_prologue<VAR, K, V, BF16IN>(p, b, hv, t0 + tt,
+                                              lds + tt * L::size, lane);
+        lds_barrier();
+
+        for (int tt = 0; tt < nt; ++tt) {
+            const int t = t0 + tt;
+            const float *rec = lds + tt * L::size;
+            const float beta = rec[L::sOff + 0];
+            const float decay = rec[L::sOff + 1];
+            const float kq = rec[L::sOff + 2];
+            float vr[RPL];
+#pragma unroll
+            for (int i = 0; i < RPL; ++i)
+                vr[i] = rec[L::vOff + wave * kRowsPerWave + rs * RPL + i];
+
+            // decay
+            if constexpr (VAR == VAR_KDA) {
+#pragma unroll
+                for (int m = 0; m < CPL; ++m) {
+                    const f4 e = *reinterpret_cast<const f4 *>(
+                        rec + L::eOff + 4 * (c8 + 8 * m));
+#pragma unroll
+                    for (int i = 0; i < RPL; ++i)
+                        S[i][m] *= e;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < RPL; ++i)
+#pragma unroll
+                    for (int m = 0; m < CPL; ++m)
+                        S[i][m] *= decay;
+            }
+
+            // read-outs u = S k (delta rules) and w = S q
+            f4 kk[CPL];
+            float u[RPL], wq[RPL];
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) {
+                u[i] = 0.f;
+                wq[i] = 0.f;
+            }
+#pragma unroll
+            for (int m = 0; m < CPL; ++m) {
+                kk[m] = *reinterpret_cast<const f4 *>(
+                    rec + L::kOff + 4 * (c8 + 8 * m));
+                const f4 qq = *reinterpret_cast<const f4 *>(
+                    rec + L::qOff + 4 * (c8 + 8 * m));
+#pragma unroll
+                for (int i = 0; i < RPL; ++i) {
+                    if constexpr (VAR != VAR_LA) {
+                        u[i] = fmaf(S[i][m].x, kk[m].x, u[i]);
+                        u[i] = fmaf(S[i][m].y, kk[m].y, u[i]);
+                        u[i] = fmaf(S[i][m].z, kk[m].z, u[i]);
+                        u[i] = fmaf(S[i][m].w, kk[m].w, u[i]);
+                    }
+                    wq[i] = fmaf(S[i][m].x, qq.x, wq[i]);
+                    wq[i] = fmaf(S[i][m].y, qq.y, wq[i]);
+                    wq[i] = fmaf(S[i][m].z, qq.z, wq[i]);
+                    wq[i] = fmaf(S[i][m].w, qq.w, wq[i]);
+                }
+            }
+            float c[RPL], o[RPL];
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) {
+                wq[i] = sum8(wq[i]);
+                if constexpr (VAR == VAR_LA) {
+                    c[i] = vr[i];
+                } else {
+                    u[i] = sum8(u[i]);
+                    c[i] = beta * (vr[i] - u[i]);
+                }
+                o[i] = fmaf(c[i], kq, wq[i]);
+            }
+
+            // rank-1 update S += c k^T
+#pragma unroll
+            for (int i = 0; i < RPL; ++i)
+#pragma unroll
+                for (int m = 0; m < CPL; ++m) {
+                    S[i][m].x = fmaf(c[i], kk[m].x, S[i][m].x);
+                    S[i][m].y = fmaf(c[i], kk[m].y, S[i][m].y);
+                    S[i][m].z = fmaf(c[i], kk[m].z, S[i][m].z);
+                    S[i][m].w = fmaf(c[i], kk[m].w, S[i][m].w);
+                }
+
+            // output: lane (c8, rs) with c8 < RPL writes row 32 w + 8 c8 + rs
+            float mine = o[0];
+#pragma unroll
+            for (int i = 1; i < RPL; ++i)
+                mine = (c8 == i) ? o[i] : mine;
+            if (olane)
+                store_out<BF16OUT>(p.out, obase + t * p.so_t, mine);
+
+            if (p.inter) {
+                float *dst = p.inter +
+                             ((static_cast<int64_t>(b) * T + t) * p.HV + hv) *
+                                 static_cast<int64_t>(V * K);
+#pragma unroll
+                for (int i = 0; i < RPL; ++i) {
+                    const int row = wave * kRowsPerWave + i * 8 + rs;
+#pragma unroll
+                    for (int m = 0; m < CPL; ++m)
+                        store_nt(dst + row * K + 4 * (c8 + 8 * m), S[i][m]);
+                }
+            }
+        }
+    }
+
+    if (w >= 0) {  // in-place writeback to the write slot
+        float *dst = p.pool + w * p.sp_slot + hv * p.sp_head;
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            const int row = wave * kRowsPerWave + i * 8 + rs;
+#pragma unroll
+            for (int m = 0; m < CPL; ++m)
+                store_nt(dst + row * p.sp_row + 4 * (c8 + 8 * m), S[i][m]);
+        }
+    }
+}
+
+// Validator of the device preconditions (one workgroup).
+__global__ void __launch_bounds__(1024)
+check_indices_kernel(int32_t B, int32_t pool_size, const int32_t *ridx,
+                     const int32_t *widx, int32_t *result)
+{
+    __shared__ int32_t flags;
+    if (threadIdx.x == 0)
+        flags = 0;
+    __syncthreads();
+    int32_t f = 0;
+    for (int i = threadIdx.x; i < B; i += blockDim.x) {
+        const int32_t r = ridx[i];
+        const int32_t w = widx ? widx[i] : r;
+        if (r >= pool_size)
+            f |= 1;
+        if (r >= 0 && w >= pool_size)
+            f |= 2;
+        if (r < 0 || w < 0)
+            continue;
+        for (int j = 0; j < B; ++j) {
+            if (j == i)
+                continue;
+            const int32_t rj = ridx[j];
+            if (rj < 0)
+                continue;
+            const int32_t wj = widx ? widx[j] : rj;
+            if (wj == w)
+                f |= 4;
+            if (rj == w)
+                f |= 8;
+        }
+    }
+    if (f)
+        atomicOr(&flags, f);
+    __syncthreads();
+    if (threadIdx.x == 0)
+        *result = flags;
+}
+
+// ------------------------------------------------------------- host side
+
+typedef void (*KernelFn)(const Params);
+
+template <int VAR, int K, int V>
+KernelFn pick_dtype(bool bf16_in, bool bf16_out)
+{
+    if (bf16_in)
+        return bf16_out ? decode_kernel<VAR, K, V, true, true>
+                        : decode_kernel<VAR, K, V, true, false>;
+    return bf16_out ? decode_kernel<VAR, K, V, false, true>
+                    : decode_kernel<VAR, K, V, false, false>;
+}
+
+template <int VAR>
+KernelFn pick(int K, int V, bool bf16_in, bool bf16_out)
+{
+    if (K == 128)
+        return V == 128 ? pick_dtype<VAR, 128, 128>(bf16_in, bf16_out)
+                        : pick_dtype<VAR, 128, 64>(bf16_in, bf16_out);
+    return V == 128 ? pick_dtype<VAR, 64, 128>(bf16_in, bf16_out)
+                    : pick_dtype<VAR, 64, 64>(bf16_in, bf16_out);
+}
+
+int lds_floats_per_token(int var, int K, int V)
+{
+    return (var == VAR_KDA ? 3 : 2) * K + V + 4;
+}
+
+bool aligned(const void *p, uintptr_t a)
+{
+    return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+bool strides_nonneg(const la_act_strides &s)
+{
+    return s.b >= 0 && s.t >= 0 && s.h >= 0;
+}
+
+// True when the n blocks (extent[i] copies at stride[i]) of `inner`
+// contiguous elements never overlap: sorted by stride, each stride must
+// clear everything nested inside it.
+bool no_overlap(int n, const int64_t *stride, const int64_t *extent,
+                int64_t inner)
+{
+    int order[4];
+    for (int i = 0; i < n; ++i)
+        order[i] = i;
+    for (int i = 1; i < n; ++i)
+        for (int j = i; j > 0 && stride[order[j]] < stride[order[j - 1]]; --j) {
+            const int tmp = order[j];
+            order[j] = order[j - 1];
+            order[j - 1] = tmp;
+        }
+    int64_t span = inner;  // elements covered by the dims processed so far
+    for (int i = 0; i < n; ++i) {
+        const int d = order[i];
+        if (extent[d] <= 1)
+            continue;
+        if (stride[d] < span)
+            return false;
+        span = stride[d] * (extent[d] - 1) + span;
+    }
+    return true;
+}
+
+la_status validate(const la_decode_args *a, int var)
+{
+    if (!a)
+        return LA_ERR_NULL;
+    if (a->B < 0 || a->T < 1 || a->H < 1 || a->HV < 1 || a->pool_size < 1)
+        return LA_ERR_SHAPE;
+    if (a->HV % a->H != 0)
+        return LA_ERR_SHAPE;
+    if ((a->K != 64 && a->K != 128) || (a->V != 64 && a->V != 128))
+        return LA_ERR_UNSUPPORTED;
+    if ((a->qkv_dtype != LA_F32 && a->qkv_dtype != LA_BF16) ||
+        (a->out_dtype != LA_F32 && a->out_dtype != LA_BF16))
+        return LA_ERR_DTYPE;
+    if (var == VAR_LA) {
+        if (a->flags != 0 || a->beta != nullptr)
+            return LA_ERR_ARG;
+    } else {
+        if (a->flags & ~(LA_F_L2NORM_QK | LA_F_BETA_LOGIT))
+            return LA_ERR_ARG;
+    }
+    if (static_cast<int64_t>(a->B) * a->HV > INT32_MAX)
+        return LA_ERR_SHAPE;
+    if (a->B == 0)
+        return LA_OK;
+
+    if (!a->q || !a->k || !a->v || !a->pool || !a->read_idx || !a->out)
+        return LA_ERR_NULL;
+    if (var != VAR_LA && (!a->g || !a->beta))
+        return LA_ERR_NULL;
+
+    if (!strides_nonneg(a->sq) || !strides_nonneg(a->sk) ||
+        !strides_nonneg(a->sv) || !strides_nonneg(a->so))
+        return LA_ERR_STRIDE;
+    if (var != VAR_LA && (!strides_nonneg(a->sg) || !strides_nonneg(a->sbeta)))
+        return LA_ERR_STRIDE;
+    if (a->sp.slot < 0 || a->sp.head < 0 || a->sp.row < 0)
+        return LA_ERR_STRIDE;
+
+    // pool tiles: rows K wide inside a tile, tiles disjoint
+    {
+        const int64_t st[3] = {a->sp.row, a->sp.head, a->sp.slot};
+        const int64_t ex[3] = {a->V, a->HV, a->pool_size};
+        if (!no_overlap(3, st, ex, a->K))
+            return LA_ERR_STRIDE;
+    }
+    // outputs must not overlap each other
+    {
+        const int64_t st[3] = {a->so.h, a->so.t, a->so.b};
+        const int64_t ex[3] = {a->HV, a->T, a->B};
+        if (!no_overlap(3, st, ex, a->V))
+            return LA_ERR_STRIDE;
+    }
+
+    const uintptr_t act = a->qkv_dtype == LA_BF16 ? 2 : 4;
+    const uintptr_t outsz = a->out_dtype == LA_BF16 ? 2 : 4;
+    if (!aligned(a->q, act) || !aligned(a->k, act) || !aligned(a->v, act) ||
+        !aligned(a->out, outsz) || !aligned(a->read_idx, 4) ||
+        !aligned(a->write_idx, 4))
+        return LA_ERR_ALIGN;
+    if (a->g && !aligned(a->g, 4))
+        return LA_ERR_ALIGN;
+    if (a->beta && !aligned(a->beta, 4))
+        return LA_ERR_ALIGN;
+    if (!aligned(a->pool, 16) || (a->sp.slot % 4) || (a->sp.head % 4) ||
+        (a->sp.row % 4))
+        return LA_ERR_ALIGN;
+    if (a->inter && !aligned(a->inter, 16))
+        return LA_ERR_ALIGN;
+    return LA_OK;
+}
+
+la_status launch(const la_decode_args *a, void *stream, int var)
+{
+    const la_status st = validate(a, var);
+    if (st != LA_OK || a->B == 0)
+        return st;
+
+    Params p;
+    p.B = a->B;
+    p.T = a->T;
+    p.HV = a->HV;
+    p.group = a->HV / a->H;
+    p.flags = a->flags;
+    p.pad_ = 0;
+    p.q = a->q;
+    p.sq_b = a->sq.b;
+    p.sq_t = a->sq.t;
+    p.sq_h = a->sq.h;
+    p.k = a->k;
+    p.sk_b = a->sk.b;
+    p.sk_t = a->sk.t;
+    p.sk_h = a->sk.h;
+    p.v = a->v;
+    p.sv_b = a->sv.b;
+    p.sv_t = a->sv.t;
+    p.sv_h = a->sv.h;
+    p.g = a->g;
+    p.sg_b = a->sg.b;
+    p.sg_t = a->sg.t;
+    p.sg_h = a->sg.h;
+    p.beta = a->beta;
+    p.sb_b = a->sbeta.b;
+    p.sb_t = a->sbeta.t;
+    p.sb_h = a->sbeta.h;
+    p.pool = a->pool;
+    p.sp_slot = a->sp.slot;
+    p.sp_head = a->sp.head;
+    p.sp_row = a->sp.row;
+    p.ridx = a->read_idx;
+    p.widx = a->write_idx;
+    p.inter = a->inter;
+    p.out = a->out;
+    p.so_b = a->so.b;
+    p.so_t = a->so.t;
+    p.so_h = a->so.h;
+
+    const bool bi = a->qkv_dtype == LA_BF16, bo = a->out_dtype == LA_BF16;
+    KernelFn fn = var == VAR_LA    ? pick<VAR_LA>(a->K, a->V, bi, bo)
+                  : var == VAR_GDN ? pick<VAR_GDN>(a->K, a->V, bi, bo)
+                                   : pick<VAR_KDA>(a->K, a->V, bi, bo);
+    const int chunk = a->T < kTokChunk ? a->T : kTokChunk;
+    const size_t lds = static_cast<size_t>(chunk) *
+                       lds_floats_per_token(var, a->K, a->V) * sizeof(float);
+    const dim3 grid(static_cast<unsigned>(a->B) * a->HV);
+    const dim3 block((a->V / kRowsPerWave) * 64);
+    void *kargs[] = {&p};
+    const hipError_t e =
+        hipLaunchKernel(reinterpret_cast<const void *>(fn), grid, block,
+                        kargs, lds, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+la_status la_decode(const la_decode_args *args, void *stream)
+{
+    return launch(args, stream, VAR_LA);
+}
+
+la_status gdn_decode_mtp(const la_decode_args *args, void *stream)
+{
+    return launch(args, stream, VAR_GDN);
+}
+
+la_status kda_decode_mtp(const la_decode_args *args, void *stream)
+{
+    return launch(args, stream, VAR_KDA);
+}
+
+la_status la_check_indices(int32_t B, int32_t pool_size,
+                           const int32_t *read_idx, const int32_t *write_idx,
+                           int32_t *dev_result, void *stream)
+{
+    if (B < 0 || pool_size < 1)
+        return LA_ERR_SHAPE;
+    if (!dev_result || (B > 0 && !read_idx))
+        return LA_ERR_NULL;
+    if (!aligned(dev_result, 4) || !aligned(read_idx, 4) ||
+        !aligned(write_idx, 4))
+        return LA_ERR_ALIGN;
+    void *kargs[] = {&B, &pool_size, &read_idx, &write_idx, &dev_result};
+    const hipError_t e = hipLaunchKernel(
+        reinterpret_cast<const void *>(check_indices_kernel), dim3(1),
+        dim3(1024), kargs, 0, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
+}
+
+const char *la_status_string(la_status s)
+{
+    switch (s) {
+    case LA_OK:
+        return "ok";
+    case LA_ERR_NULL:
+        return "a required pointer is NULL";
+    case LA_ERR_SHAPE:
+        return "a size is out of range or inconsistent";
+    case LA_ERR_STRIDE:
+        return "bad stride: negative, innermost != 1, or overlapping tiles";
+    case LA_ERR_ALIGN:
+        return "misaligned pointer or stride";
+    case LA_ERR_DTYPE:
+        return "unknown dtype";
+    case LA_ERR_ARG:
+        return "argument inconsistent with the entry point";
+    case LA_ERR_UNSUPPORTED:
+        return "unsupported size (K and V must be 64 or 128)";
+    case LA_ERR_LAUNCH:
+        return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+int32_t la_version(void) { return 100; }
+
+}  // extern "C"

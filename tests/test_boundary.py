@@ -1,0 +1,218 @@
+"""C-ABI boundary checks that need no GPU.
+
+The library must load, export every function include/la_decode.h declares,
+agree with the ctypes mirror on the argument struct layout, and reject bad
+arguments on the host before anything is launched (the pointers used here
+are fake and never dereferenced).
+"""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "la_decode.h")
+
+from linear_attention_recurrent_slot_amd import _binding as bnd  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bnd.LIB_PATH):
+        from linear_attention_recurrent_slot_amd import build
+        build.build()
+    return bnd.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ("la_decode", "gdn_decode_mtp", "kda_decode_mtp",
+              "la_check_indices", "la_status_string", "la_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", bnd.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for name in _declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_struct_layout_matches_ctypes(tmp_path):
+    """Compile a C program against the header and compare sizeof/offsetof
+    of every la_decode_args field with the ctypes mirror."""
+    fields = [f for f, _ in bnd.DecodeArgs._fields_]
+    body = "\n".join(
+        '  printf("%s %%zu\\n", offsetof(la_decode_args, %s));' % (f, f)
+        for f in fields)
+    src = tmp_path / "layout.c"
+    src.write_text(
+        "#include <stdio.h>\n#include <stddef.h>\n#include \"la_decode.h\"\n"
+        "int main(void){\n  printf(\"size %%zu\\n\", sizeof(la_decode_args));\n"
+        "%s\n  return 0;\n}\n" % body)
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(exe)], check=True)
+    got = dict(ln.split() for ln in
+               subprocess.run([str(exe)], capture_output=True, text=True,
+                              check=True).stdout.splitlines())
+    assert int(got["size"]) == ctypes.sizeof(bnd.DecodeArgs)
+    for f in fields:
+        assert int(got[f]) == getattr(bnd.DecodeArgs, f).offset, f
+
+
+def test_status_strings_and_version(lib):
+    for code in range(0, 9):
+        s = bnd.status_string(code)
+        assert s and s != "unknown status"
+    assert bnd.status_string(99) == "unknown status"
+    assert lib.la_version() >= 100
+
+
+FAKE = 0x7f0000000000  # 16-byte aligned, never dereferenced
+
+
+def _valid_args(variant="gdn", B=4, T=2, H=2, HV=4, K=128, V=128,
+                pool_size=8, bf16=True):
+    a = bnd.DecodeArgs()
+    a.B, a.T, a.H, a.HV, a.K, a.V, a.pool_size = B, T, H, HV, K, V, pool_size
+    a.flags = 0 if variant == "lightning" else 3
+    a.qkv_dtype = bnd.LA_BF16 if bf16 else bnd.LA_F32
+    a.out_dtype = bnd.LA_F32
+    a.q = FAKE
+    a.sq = bnd.ActStrides(T * H * K, H * K, K)
+    a.k = FAKE + 0x100000
+    a.sk = bnd.ActStrides(T * H * K, H * K, K)
+    a.v = FAKE + 0x200000
+    a.sv = bnd.ActStrides(T * HV * V, HV * V, V)
+    if variant == "gdn":
+        a.g = FAKE + 0x300000
+        a.sg = bnd.ActStrides(T * HV, HV, 1)
+    elif variant == "kda":
+        a.g = FAKE + 0x300000
+        a.sg = bnd.ActStrides(T * HV * K, HV * K, K)
+    if variant != "lightning":
+        a.beta = FAKE + 0x400000
+        a.sbeta = bnd.ActStrides(T * HV, HV, 1)
+    a.pool = FAKE + 0x1000000
+    a.sp = bnd.PoolStrides(HV * V * K, V * K, K)
+    a.read_idx = FAKE + 0x500000
+    a.write_idx = FAKE + 0x500100
+    a.out = FAKE + 0x600000
+    a.so = bnd.ActStrides(T * HV * V, HV * V, V)
+    return a
+
+
+ENTRY = {"lightning": "la_decode", "gdn": "gdn_decode_mtp",
+         "kda": "kda_decode_mtp"}
+
+
+def _status(variant, a):
+    return getattr(bnd.lib(), ENTRY[variant])(ctypes.byref(a), None)
+
+
+def _mut(**kw):
+    def f(a):
+        for key, val in kw.items():
+            setattr(a, key, val)
+    return f
+
+
+REJECT = [
+    ("null_args", None, "gdn", 1),
+    ("null_q", _mut(q=None), "gdn", 1),
+    ("null_pool", _mut(pool=None), "kda", 1),
+    ("null_read_idx", _mut(read_idx=None), "lightning", 1),
+    ("null_out", _mut(out=None), "gdn", 1),
+    ("null_beta_gdn", _mut(beta=None), "gdn", 1),
+    ("null_g_kda", _mut(g=None), "kda", 1),
+    ("T_zero", _mut(T=0), "gdn", 2),
+    ("B_negative", _mut(B=-1), "gdn", 2),
+    ("H_not_dividing_HV", _mut(H=3), "gdn", 2),
+    ("pool_size_zero", _mut(pool_size=0), "gdn", 2),
+    ("grid_too_large", _mut(B=2 ** 30, HV=4), "gdn", 2),
+    ("K_96", _mut(K=96), "gdn", 7),
+    ("V_256", _mut(V=256), "kda", 7),
+    ("dtype_code", _mut(qkv_dtype=7), "gdn", 5),
+    ("out_dtype_code", _mut(out_dtype=3), "lightning", 5),
+    ("beta_for_lightning", _mut(beta=FAKE), "lightning", 6),
+    ("flags_for_lightning", _mut(flags=1), "lightning", 6),
+    ("unknown_flag_bit", _mut(flags=4), "gdn", 6),
+    ("negative_q_stride", _mut(sq=bnd.ActStrides(-1, 0, 0)), "gdn", 3),
+    ("negative_pool_stride", _mut(sp=bnd.PoolStrides(-4, 0, 128)), "gdn", 3),
+    ("pool_rows_overlap", _mut(sp=bnd.PoolStrides(4 * 128 * 128 * 4,
+                                                  128 * 128, 64)), "gdn", 3),
+    ("pool_heads_overlap", _mut(sp=bnd.PoolStrides(4 * 128 * 128, 64 * 128,
+                                                   128)), "gdn", 3),
+    ("pool_slots_overlap", _mut(sp=bnd.PoolStrides(128 * 128, 128 * 128 * 2,
+                                                   128)), "gdn", 3),
+    ("out_rows_overlap", _mut(so=bnd.ActStrides(2 * 4 * 128, 4 * 128, 64)),
+     "gdn", 3),
+    ("pool_misaligned", _mut(pool=FAKE + 0x1000004), "gdn", 4),
+    ("pool_row_stride_misaligned",
+     _mut(sp=bnd.PoolStrides(4 * 130 * 128, 130 * 128, 130)), "gdn", 4),
+    ("inter_misaligned", _mut(inter=FAKE + 0x2000008), "kda", 4),
+    ("bf16_q_odd_address", _mut(q=FAKE + 1), "gdn", 4),
+    ("read_idx_misaligned", _mut(read_idx=FAKE + 0x500002), "gdn", 4),
+]
+
+
+@pytest.mark.parametrize("name,mutate,variant,code", REJECT,
+                         ids=[r[0] for r in REJECT])
+def test_host_validation_rejects(lib, name, mutate, variant, code):
+    if mutate is None:
+        st = getattr(lib, ENTRY[variant])(None, None)
+    else:
+        a = _valid_args(variant)
+        mutate(a)
+        st = _status(variant, a)
+    assert st == code, (name, bnd.STATUS_NAMES.get(st))
+
+
+@pytest.mark.parametrize("variant", ["lightning", "gdn", "kda"])
+def test_empty_batch_is_a_noop(lib, variant):
+    a = _valid_args(variant)
+    a.B = 0
+    a.q = a.k = a.v = a.pool = a.out = a.read_idx = None
+    assert _status(variant, a) == 0
+
+
+def test_check_indices_host_rejections(lib):
+    L = lib
+    assert L.la_check_indices(-1, 4, FAKE, None, FAKE, None) == 2
+    assert L.la_check_indices(4, 0, FAKE, None, FAKE, None) == 2
+    assert L.la_check_indices(4, 4, FAKE, None, None, None) == 1
+    assert L.la_check_indices(4, 4, None, None, FAKE, None) == 1
+    assert L.la_check_indices(4, 4, FAKE, None, FAKE + 2, None) == 4
+
+
+def test_valid_call_without_gpu_reports_launch_failure():
+    """With no GPU the validated call reaches hipLaunchKernel, which fails;
+    the library reports LA_ERR_LAUNCH instead of crashing. Run in a child
+    process so the HIP runtime never initialises inside the test runner."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; the launch would run")
+    code = (
+        "import sys, ctypes; sys.path.insert(0, %r); sys.path.insert(0, %r)\n"
+        "from linear_attention_recurrent_slot_amd import _binding as b\n"
+        "import test_boundary as tb\n"
+        "a = tb._valid_args('gdn')\n"
+        "print(b.lib().gdn_decode_mtp(ctypes.byref(a), None))\n"
+        % (ROOT, os.path.join(ROOT, "tests")))
+    proc = subprocess.run([sys.executable, "-c", code], capture_output=True,
+                          text=True, timeout=120)
+    assert proc.returncode == 0, proc.stderr
+    assert proc.stdout.strip().splitlines()[-1] == "8"

@@ -1,0 +1,522 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Element by element on the same seeded inputs (workloads.py), for every
+variant, dtype and tile shape, index patterns from the pages' tests, strided
+pools, packed views, token splitting, padding and skipped writes, plus
+bytewise checks that every slot the call must not write is untouched.
+
+Tolerances (max over a tensor of |gpu - oracle|):
+  fp32 q/k/v: relative to max |oracle|, <= 1e-4 for outputs and states;
+  bf16 q/k/v with the fp32 state: absolute <= 2e-3 (outputs), <= 1e-3
+  (states and cached intermediates).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+VARIANT_CODE = {W.LIGHTNING: oracle.LIGHTNING, W.GDN: oracle.GDN,
+                W.KDA: oracle.KDA}
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print("\n[gpu-test] %s" % request.node.nodeid, flush=True)
+    yield
+
+
+def _lad():
+    import linear_attention_recurrent_slot_amd as lad
+    lad.lib()  # raises if the HIP library is missing
+    return lad
+
+
+# ------------------------------------------------------------------ runners
+
+
+def gpu_run(wl, *, q=None, k=None, v=None, backing=None, stream=None,
+            inter_fill=float("nan")):
+    """Run the workload on the GPU. Returns CPU copies of out, backing and
+    inter (inter pre-filled with NaN so untouched rows stay NaN)."""
+    lad = _lad()
+    d = wl.to(DEV)
+    if backing is None:
+        backing = d.backing
+    pool = backing[:: wl.stride_mult]
+    q = d.q if q is None else q
+    k = d.k if k is None else k
+    v = d.v if v is None else v
+    # every index set must satisfy the device preconditions before a launch
+    bad = lad.check_indices(d.read_idx, d.write_idx, wl.pool_size)
+    assert int(bad.item()) == 0, "invalid index set in a test case"
+    inter = None
+    if wl.inter:
+        inter = torch.full((wl.B, wl.T, wl.HV, wl.V, wl.K), inter_fill,
+                           dtype=torch.float32, device=DEV)
+    if wl.variant == W.LIGHTNING:
+        out, _ = lad.la_decode(q, k, v, pool, d.read_idx, d.write_idx,
+                               lam=d.g, inter=inter, out_dtype=wl.out_dtype,
+                               stream=stream)
+    else:
+        fn = lad.gdn_decode_mtp if wl.variant == W.GDN else lad.kda_decode_mtp
+        out, _ = fn(q, k, v, d.g, d.beta, pool, d.read_idx, d.write_idx,
+                    inter=inter, l2norm_qk=wl.l2norm,
+                    beta_logit=wl.beta_logit, out_dtype=wl.out_dtype,
+                    stream=stream)
+    torch.cuda.synchronize()
+    return {"out": out.cpu(), "backing": backing.cpu(),
+            "inter": None if inter is None else inter.cpu()}
+
+
+def _flags(wl):
+    return ((oracle.L2NORM_QK if wl.l2norm else 0)
+            | (oracle.BETA_LOGIT if wl.beta_logit else 0))
+
+
+def oracle_run(wl, reqs=None):
+    """Oracle on the requests `reqs` (all by default), on a mini pool made of
+    their read slots (reads at 0..n-1, writes at n..2n-1)."""
+    B = wl.B
+    reqs = list(range(B)) if reqs is None else list(reqs)
+    n = len(reqs)
+    pool = wl.pool()
+    ridx = wl.read_idx.tolist()
+    widx = wl.write_idx.tolist() if wl.write_idx is not None else ridx
+    mini = torch.zeros((2 * n,) + tuple(pool.shape[1:]), dtype=torch.float64)
+    mr, mw = [], []
+    for i, b in enumerate(reqs):
+        if ridx[b] >= 0:
+            mini[i] = pool[ridx[b]].double()
+            mr.append(i)
+            mw.append(n + i if widx[b] >= 0 else -1)
+        else:
+            mr.append(-1)
+            mw.append(-1)
+    sel = torch.tensor(reqs)
+    g = wl.g
+    if wl.variant != W.LIGHTNING:
+        g = g[sel]
+    beta = None if wl.beta is None else wl.beta[sel]
+    res = oracle.decode(VARIANT_CODE[wl.variant], wl.q[sel], wl.k[sel],
+                        wl.v[sel], g, beta, mini, mr, mw, flags=_flags(wl),
+                        inter=wl.inter)
+    res["reqs"] = reqs
+    res["mini_write"] = mw
+    return res
+
+
+def _tol(wl):
+    if wl.q.dtype == torch.float32:
+        return ("rel", 1e-4, 1e-4)
+    return ("abs", 2e-3, 1e-3)
+
+
+def _err(kind, got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert np.isfinite(got).all(), "non-finite GPU values"
+    e = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    if kind == "rel":
+        e /= max(float(np.max(np.abs(ref))), 1e-30)
+    return e
+
+
+def check_parity(wl, got, before_backing, reqs=None):
+    """Compare the sampled requests with the oracle; check every untouched
+    byte of the backing buffer over the whole pool."""
+    ref = oracle_run(wl, reqs)
+    kind, tol_out, tol_state = _tol(wl)
+    reqs = ref["reqs"]
+    ridx = wl.read_idx.tolist()
+    widx = wl.write_idx.tolist() if wl.write_idx is not None else ridx
+    m = wl.stride_mult
+    errs = {"out": 0.0, "state": 0.0, "inter": 0.0}
+    out = got["out"].float().numpy()
+    for i, b in enumerate(reqs):
+        if wl.out_dtype == torch.bfloat16:
+            # the kernel rounds its fp32 result to nearest even: allow one
+            # bf16 step on top of the fp32 tolerance
+            ref_b = torch.tensor(ref["out"][i]).to(torch.bfloat16).float()
+            step = torch.abs(ref_b) * 2.0 ** -7 + 1e-30
+            diff = torch.abs(torch.tensor(out[b]) - ref_b)
+            assert bool((diff <= step + (tol_out if kind == "abs" else 0)
+                         ).all()), "bf16 output off by more than one step"
+        else:
+            errs["out"] = max(errs["out"], _err(kind, out[b], ref["out"][i]))
+        if ridx[b] < 0:
+            assert not np.any(out[b]), "padded request must output zeros"
+            if wl.inter:
+                assert torch.isnan(got["inter"][b]).all(), \
+                    "padded request must not touch the cache"
+            continue
+        if wl.inter:
+            errs["inter"] = max(errs["inter"], _err(
+                kind, got["inter"][b].numpy(), ref["inter"][i]))
+        if widx[b] >= 0:
+            errs["state"] = max(errs["state"], _err(
+                kind, got["backing"][m * widx[b]].numpy(),
+                ref["pool"][ref["mini_write"][i]]))
+    assert errs["out"] <= tol_out, errs
+    assert errs["state"] <= tol_state, errs
+    assert errs["inter"] <= tol_state, errs
+    # bytewise: only the backing slots of non-negative write slots of active
+    # requests may change
+    written = {m * w for r, w in zip(ridx, widx) if r >= 0 and w >= 0}
+    a = got["backing"].view(torch.int32)
+    b0 = before_backing.view(torch.int32)
+    keep = torch.ones(a.shape[0], dtype=torch.bool)
+    if written:
+        keep[torch.tensor(sorted(written))] = False
+    assert torch.equal(a[keep], b0[keep]), "a slot that must not change did"
+    return errs
+
+
+def run_and_check(wl, reqs=None):
+    before = wl.backing.clone()
+    got = gpu_run(wl)
+    errs = check_parity(wl, got, before, reqs)
+    print("  %s errors %s" % (wl.name, {k: "%.2e" % v for k, v in errs.items()}),
+          flush=True)
+    return got
+
+
+# ------------------------------------------------------- named workloads
+
+# Sampled requests for the large workloads: the oracle checks these one by
+# one; the untouched-byte check still covers the whole pool.
+SAMPLE = {"gdn_small_k64": None, "lightning_b33_h64": None,
+          "gdn_gva_b64": range(0, 64, 3), "gdn_mtp_b32_t4": range(32),
+          "kda_b256_t1": range(0, 256, 9), "kda_b256_t8": range(0, 256, 17)}
+
+
+@pytest.mark.parametrize("name", list(W.NAMED))
+def test_named_workload_parity(name):
+    wl = W.named(name)
+    run_and_check(wl, SAMPLE[name])
+
+
+def test_small_workload_host_normalised_inputs():
+    """q and k normalised before the call (flag off) give the same result
+    as raw inputs normalised in the kernel."""
+    wl = W.gdn_small_k64()
+    qn = wl.q / wl.q.norm(dim=-1, keepdim=True)
+    kn = wl.k / wl.k.norm(dim=-1, keepdim=True)
+    wl2 = W.gdn_small_k64()
+    wl2.q, wl2.k, wl2.l2norm = qn, kn, False
+    run_and_check(wl2)
+
+
+# ------------------------------------------------- shapes, dtypes, tokens
+
+
+SHAPES = [(64, 64), (128, 128), (64, 128), (128, 64)]
+
+
+@pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN, W.KDA])
+@pytest.mark.parametrize("K,V", SHAPES)
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16],
+                         ids=["f32", "bf16"])
+@pytest.mark.parametrize("T", [1, 3, 9])
+def test_shapes_dtypes_tokens(variant, K, V, dtype, T):
+    seed = (1000 + 100 * [W.LIGHTNING, W.GDN, W.KDA].index(variant)
+            + 10 * SHAPES.index((K, V)) + T
+            + (500 if dtype == torch.bfloat16 else 0))
+    wl = W.make("shape", variant, B=3, T=T, H=2, HV=4, K=K, V=V,
+                pool_size=7, seed=seed, act_dtype=dtype, pool_std=0.1,
+                l2norm=variant != W.LIGHTNING, separate_write=True,
+                write_skip=0.34, inter=True)
+    run_and_check(wl)
+
+
+def test_long_multi_token_run_crosses_chunks():
+    """T = 17: three prologue chunks of up to 8 tokens."""
+    wl = W.make("long", W.KDA, B=5, T=17, H=1, HV=2, K=128, V=128,
+                pool_size=9, seed=21, inter=True)
+    run_and_check(wl)
+
+
+# ------------------------------------------- index patterns of the pages
+
+
+def _gdn_pool_case(B, pool_size, read_idx, T=1, seed=30, **kw):
+    return W.make("pool", W.GDN, B=B, T=T, H=2, HV=4, K=128, V=128,
+                  pool_size=pool_size, seed=seed, read_idx=read_idx,
+                  act_dtype=torch.float32, **kw)
+
+
+@pytest.mark.parametrize("B,pool_size,read_idx", [
+    (4, 4, [0, 1, 2, 3]),           # identity offsets
+    (4, 6, [2, 0, 5, 1]),           # non-identity, pool larger than batch
+    (4, 4, [3, 2, 1, 0]),           # reversed, pool = batch
+    (33, 40, None),                 # big batch in a pool of 40
+], ids=["identity", "non_identity", "reversed", "b33_pool40"])
+def test_page_index_patterns(B, pool_size, read_idx):
+    wl = _gdn_pool_case(B, pool_size, read_idx)
+    run_and_check(wl)
+
+
+@pytest.mark.parametrize("B,pool_size,read_idx", [
+    (4, 6, [2, 0, 5, 1]), (4, 4, [3, 2, 1, 0]), (33, 40, None)])
+def test_index_equivariance_bit_identical(B, pool_size, read_idx):
+    """Batched results equal one-request calls on the same slots, bit for
+    bit: the arithmetic does not depend on B or the slot."""
+    wl = _gdn_pool_case(B, pool_size, read_idx, T=2)
+    whole = gpu_run(wl)
+    for b in range(B):
+        one = W.make("one", W.GDN, B=1, T=2, H=2, HV=4, K=128, V=128,
+                     pool_size=pool_size, seed=0, act_dtype=torch.float32,
+                     read_idx=[int(wl.read_idx[b])])
+        one.q, one.k, one.v = wl.q[b:b + 1], wl.k[b:b + 1], wl.v[b:b + 1]
+        one.g, one.beta = wl.g[b:b + 1], wl.beta[b:b + 1]
+        one.backing = wl.backing.clone()
+        got = gpu_run(one)
+        assert torch.equal(got["out"][0], whole["out"][b])
+        r = int(wl.read_idx[b])
+        assert torch.equal(got["backing"][r], whole["backing"][r])
+
+
+@pytest.mark.parametrize("B", [1, 4, 16])
+@pytest.mark.parametrize("T", [2, 4])
+@pytest.mark.parametrize("separate", [False, True])
+@pytest.mark.parametrize("cache", [False, True])
+def test_mtp_fp32_state_pool(B, T, separate, cache):
+    """The FlashInfer fp32 MTP pool matrix: batch x seq_len x separate
+    output indices x intermediate caching."""
+    wl = W.make("mtp", W.GDN, B=B, T=T, H=16, HV=32, K=128, V=128,
+                pool_size=2 * B + 3, seed=100 + B * 10 + T, act_dtype=torch.float32,
+                separate_write=separate, write_skip=0.25 if separate else 0.0,
+                inter=cache)
+    run_and_check(wl)
+
+
+@pytest.mark.parametrize("B", [1, 4])
+@pytest.mark.parametrize("T", [2, 4])
+@pytest.mark.parametrize("mult", [2, 3])
+def test_mtp_fp32_state_pool_non_contiguous(B, T, mult):
+    """Strided pools cut from an oversized buffer are updated in place and
+    the gap slots stay untouched."""
+    wl = W.make("strided", W.GDN, B=B, T=T, H=16, HV=32, K=128, V=128,
+                pool_size=2 * B + 2, seed=200 + B * 10 + T + mult,
+                act_dtype=torch.float32, stride_mult=mult,
+                separate_write=True, inter=True)
+    run_and_check(wl)
+
+
+@pytest.mark.parametrize("mult", [2, 3])
+def test_strided_pool_bit_identical_to_contiguous(mult):
+    wl = W.make("s", W.KDA, B=4, T=3, H=2, HV=4, K=128, V=128, pool_size=9,
+                seed=40 + mult, stride_mult=mult, separate_write=True)
+    got_s = gpu_run(wl)
+    wl_c = W.make("c", W.KDA, B=4, T=3, H=2, HV=4, K=128, V=128, pool_size=9,
+                  seed=40 + mult, stride_mult=mult, separate_write=True)
+    wl_c.backing = wl.pool().contiguous()
+    wl_c.stride_mult = 1
+    got_c = gpu_run(wl_c)
+    assert torch.equal(got_s["out"], got_c["out"])
+    assert torch.equal(got_s["backing"][::mult], got_c["backing"])
+
+
+# ------------------------------------------------------ packed q/k/v views
+
+
+@pytest.mark.parametrize("variant", [W.GDN, W.KDA, W.LIGHTNING])
+def test_packed_qkv_views_bit_identical(variant):
+    """q/k/v as head-dim slices of one fused [B, T, 2HK + HV V] buffer give
+    exactly the contiguous result."""
+    wl = W.make("pk", variant, B=5, T=2, H=2, HV=4, K=128, V=64, pool_size=8,
+                seed=50, l2norm=variant != W.LIGHTNING)
+    B, T, H, HV, K, V = wl.B, wl.T, wl.H, wl.HV, wl.K, wl.V
+    fused = torch.cat([wl.q.reshape(B, T, H * K), wl.k.reshape(B, T, H * K),
+                       wl.v.reshape(B, T, HV * V)], dim=-1).to(DEV)
+    qv = fused[..., : H * K].unflatten(-1, (H, K))
+    kv = fused[..., H * K: 2 * H * K].unflatten(-1, (H, K))
+    vv = fused[..., 2 * H * K:].unflatten(-1, (HV, V))
+    assert not qv.is_contiguous()
+    packed = gpu_run(wl, q=qv, k=kv, v=vv)
+    plain = gpu_run(W.make("pk", variant, B=5, T=2, H=2, HV=4, K=128, V=64,
+                           pool_size=8, seed=50,
+                           l2norm=variant != W.LIGHTNING))
+    assert torch.equal(packed["out"], plain["out"])
+    assert torch.equal(packed["backing"], plain["backing"])
+
+
+# --------------------------------------------------------- token splitting
+
+
+@pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN, W.KDA])
+def test_token_split_bit_identical(variant):
+    """T single-token calls chained through the pool = one T-token call,
+    bit for bit (outputs and final state)."""
+    T = 5
+    wl = W.make("split", variant, B=3, T=T, H=2, HV=4, K=128, V=128,
+                pool_size=5, seed=60, l2norm=variant != W.LIGHTNING)
+    whole = gpu_run(wl)
+    backing = wl.backing.clone().to(DEV)
+    for t in range(T):
+        step = W.make("split", variant, B=3, T=T, H=2, HV=4, K=128, V=128,
+                      pool_size=5, seed=60, l2norm=variant != W.LIGHTNING)
+        step.T = 1
+        step.q, step.k, step.v = (x[:, t:t + 1] for x in (wl.q, wl.k, wl.v))
+        if variant != W.LIGHTNING:
+            step.g = wl.g[:, t:t + 1]
+            step.beta = wl.beta[:, t:t + 1]
+        got = gpu_run(step, backing=backing)
+        assert torch.equal(got["out"][:, 0], whole["out"][:, t])
+    assert torch.equal(backing.cpu(), whole["backing"])
+
+
+# ------------------------------------------------- padding and degenerate
+
+
+@pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN, W.KDA])
+def test_padding_and_skipped_writes(variant):
+    wl = W.make("pad", variant, B=6, T=2, H=2, HV=2, K=64, V=128, pool_size=9,
+                seed=70, read_idx=[3, -1, 0, 8, -1, 5],
+                write_idx=[1, 2, -1, 7, 4, -1], inter=True)
+    got = run_and_check(wl)
+    assert not got["out"][1].any() and not got["out"][4].any()
+
+
+def test_zero_beta_zero_gate_leaves_state():
+    wl = W.make("z", W.GDN, B=3, T=2, H=1, HV=2, K=128, V=128, pool_size=4,
+                seed=80, act_dtype=torch.float32, beta_logit=False)
+    wl.g = torch.zeros_like(wl.g)
+    wl.beta = torch.zeros_like(wl.beta)
+    before = wl.backing.clone()
+    got = gpu_run(wl)
+    assert torch.equal(got["backing"], before)
+    check_parity(wl, got, before)
+
+
+def test_zero_query_and_key_stay_finite():
+    wl = W.make("zq", W.KDA, B=2, T=2, H=1, HV=2, K=128, V=128, pool_size=3,
+                seed=81)
+    wl.q = torch.zeros_like(wl.q)
+    wl.k = torch.zeros_like(wl.k)
+    got = run_and_check(wl)
+    assert not got["out"].any()
+
+
+def test_unit_key_beta_one_writes_value():
+    """beta = 1, |k| = 1 (l2norm on): the new state maps k to v."""
+    wl = W.make("uk", W.GDN, B=2, T=1, H=1, HV=2, K=128, V=128, pool_size=2,
+                seed=82, act_dtype=torch.float32, beta_logit=False,
+                inter=True)
+    wl.beta = torch.ones_like(wl.beta)
+    got = gpu_run(wl)
+    kn = wl.k / torch.sqrt((wl.k.double() ** 2).sum(-1, keepdim=True) + 1e-6)
+    for b in range(2):
+        for hv in range(2):
+            S = got["inter"][b, 0, hv].double()
+            err = (S @ kn[b, 0, 0].double() - wl.v[b, 0, hv].double()).abs().max()
+            assert float(err) < 1e-4
+
+
+def test_empty_batch_noop():
+    lad = _lad()
+    wl = W.make("e", W.GDN, B=1, T=1, H=1, HV=1, K=64, V=64, pool_size=2,
+                seed=83)
+    d = wl.to(DEV)
+    out, _ = lad.gdn_decode_mtp(d.q[:0], d.k[:0], d.v[:0], d.g[:0],
+                                d.beta[:0], d.pool(), d.read_idx[:0])
+    torch.cuda.synchronize()
+    assert out.shape[0] == 0
+    assert torch.equal(d.backing.cpu(), wl.backing)
+
+
+def test_bf16_output():
+    wl = W.make("bo", W.GDN, B=4, T=2, H=2, HV=4, K=128, V=128, pool_size=6,
+                seed=84, out_dtype=torch.bfloat16)
+    run_and_check(wl)
+
+
+def test_int64_pool_addressing():
+    """A slot beyond 2^31 elements from the pool base (8.6 GB buffer)."""
+    K = V = 128
+    tile = V * K
+    slot_stride = 2 ** 31 + tile
+    n = slot_stride + tile
+    buf = torch.empty(n, dtype=torch.float32, device=DEV)
+    gen = torch.Generator().manual_seed(90)
+    tiles = torch.randn((2, 1, V, K), generator=gen) * 0.05
+    pool = torch.as_strided(buf, (2, 1, V, K), (slot_stride, tile, K, 1))
+    pool.copy_(tiles.to(DEV))
+    wl = W.make("big", W.GDN, B=2, T=2, H=1, HV=1, K=K, V=V, pool_size=2,
+                seed=91, read_idx=[1, 0])
+    wl.backing = tiles
+    lad = _lad()
+    d = wl.to(DEV)
+    out, _ = lad.gdn_decode_mtp(d.q, d.k, d.v, d.g, d.beta, pool, d.read_idx,
+                                d.write_idx, l2norm_qk=True, beta_logit=True)
+    torch.cuda.synchronize()
+    ref = oracle_run(wl)
+    kind, tol_out, tol_state = _tol(wl)
+    assert _err(kind, out.cpu().numpy(), ref["out"]) <= tol_out
+    after = pool.cpu()
+    # request 0 read and wrote slot 1 (mini-pool write slot 2), request 1
+    # slot 0 (mini-pool write slot 3)
+    assert _err(kind, after[1].numpy(), ref["pool"][2]) <= tol_state
+    assert _err(kind, after[0].numpy(), ref["pool"][3]) <= tol_state
+    del buf, pool
+
+
+# ------------------------------------------------------- index validator
+
+
+@pytest.mark.parametrize("ridx,widx,expect", [
+    ([0, 1, 2], None, 0),
+    ([0, 1, 2], [3, 4, -1], 0),
+    ([0, -1, 2], [3, 0, 5], 0),     # a padded request writes nothing
+    ([0, 1, 9], None, 3),           # the default write slot is out of range too
+    ([0, 1, 9], [2, 3, 4], 1),
+    ([0, 1, 2], [3, 9, 4], 2),
+    ([0, 1, 2], [3, 3, 4], 4),
+    ([0, 1, 2], [1, 4, 5], 8),
+    ([0, 0, 2], None, 12),          # two requests write back one slot
+    ([0, 0, 2], [3, 4, 5], 0),      # shared read slot, distinct writes
+])
+def test_check_indices(ridx, widx, expect):
+    lad = _lad()
+    r = torch.tensor(ridx, dtype=torch.int32, device=DEV)
+    w = None if widx is None else torch.tensor(widx, dtype=torch.int32,
+                                               device=DEV)
+    res = lad.check_indices(r, w, pool_size=6)
+    assert int(res.item()) == expect
+
+
+def test_check_indices_empty_and_large():
+    lad = _lad()
+    r = torch.empty(0, dtype=torch.int32, device=DEV)
+    assert int(lad.check_indices(r, None, pool_size=4).item()) == 0
+    perm = torch.randperm(4096, generator=torch.Generator().manual_seed(3))
+    r = perm[:2000].to(torch.int32).to(DEV)
+    w = perm[2000:4000].to(torch.int32).to(DEV)
+    assert int(lad.check_indices(r, w, pool_size=4096).item()) == 0
+    w2 = w.clone()
+    w2[1999] = w2[0]
+    assert int(lad.check_indices(r, w2, pool_size=4096).item()) == 4
+
+
+def test_workload_index_sets_are_valid():
+    lad = _lad()
+    for name in W.NAMED:
+        wl = W.named(name)
+        r = wl.read_idx.to(DEV)
+        w = None if wl.write_idx is None else wl.write_idx.to(DEV)
+        assert int(lad.check_indices(r, w, wl.pool_size).item()) == 0, name
+
+
+def test_side_stream():
+    """Calls honour the caller's stream."""
+    wl = W.make("st", W.GDN, B=3, T=2, H=1, HV=2, K=128, V=128, pool_size=4,
+                seed=95)
+    s = torch.cuda.Stream()
+    before = wl.backing.clone()
+    with torch.cuda.stream(s):
+        got = gpu_run(wl, stream=s)
+    check_parity(wl, got, before)

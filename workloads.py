@@ -153,7 +153,8 @@ def make(name, variant, B, T, H, HV, K, V, pool_size, *, seed,
     else:
         widx = None
     return Workload(name=name, variant=variant, B=B, T=T, H=H, HV=HV, K=K,
-                    V=V, pool_size=pool_size, l2norm=l2norm,
+                    V=V, pool_size=pool_size,
+                    l2norm=l2norm if variant != LIGHTNING else False,
                     beta_logit=beta_logit if variant != LIGHTNING else False,
                     q=q, k=k, v=v, g=g, beta=beta, backing=backing,
                     stride_mult=stride_mult, read_idx=ridx, write_idx=widx,
