@@ -69,8 +69,9 @@ typedef enum la_status {
     LA_OK = 0,
     LA_ERR_NULL = 1,        /* a required pointer is NULL                    */
     LA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent        */
-    LA_ERR_STRIDE = 3,      /* negative stride, innermost stride != 1, or
-                               overlapping pool tiles                        */
+    LA_ERR_STRIDE = 3,      /* negative stride, innermost stride != 1,
+                               overlapping pool tiles or outputs, or a tile
+                               whose rows span 2 GiB or more                 */
     LA_ERR_ALIGN = 4,       /* pool / cache row not 16-byte aligned, or an
                                activation not aligned to its element size    */
     LA_ERR_DTYPE = 5,       /* unknown dtype code                            */

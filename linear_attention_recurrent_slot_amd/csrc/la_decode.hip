@@ -15,12 +15,12 @@
 //    the updated state) with l2norm, sigmoid and gate fused into the kernel.
 //
 // Kernel design (gfx950, wave64):
-//  - One workgroup per (request, value head) pair; V/32 waves, each owning
-//    32 rows of the V x K fp32 state tile for the whole call. The tile is
+//  - One workgroup per (request, value head) pair; V/R waves, each owning
+//    R (32 by default) rows of the V x K fp32 state tile for the whole call. The tile is
 //    held in VGPRs across all T tokens, so the pool sees one read and at most
 //    one write per pair per call.
 //  - Within a wave, 8 lanes share one row: lane (c, r) with c = lane & 7 and
-//    r = lane >> 3 holds rows {32 w + 8 i + r} and the 16-byte column chunks
+//    r = lane >> 3 holds rows {R w + 8 i + r} and the 16-byte column chunks
 //    {c + 8 m}. Each global_load_dwordx4 of the wave reads 8 whole 128-byte
 //    row segments; every byte of the tile is read once and written once.
 //  - Row dot products (S k and S q) reduce over the 8 lanes of a row with
@@ -45,7 +45,24 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 enum Variant { VAR_LA = 0, VAR_GDN = 1, VAR_KDA = 2 };
 
-constexpr int kRowsPerWave = 32;
+// Tunables (compile-time; the defaults are the measured best on MI355X).
+#ifndef LA_ROWS_PER_WAVE
+#define LA_ROWS_PER_WAVE 32  // state rows a wave keeps in VGPRs: 16 or 32
+#endif
+// Cache-policy bits of the state tile's buffer loads and stores (gfx950:
+// 1 = sc0, 2 = nt, 16 = sc1); 2 streams the tile through the caches.
+#ifndef LA_LOAD_POLICY
+#define LA_LOAD_POLICY 2
+#endif
+#ifndef LA_STORE_POLICY
+#define LA_STORE_POLICY 2
+#endif
+#ifndef LA_WAVES_PER_EU
+#define LA_WAVES_PER_EU 0  // >0: ask the register allocator for this occupancy
+#endif
+
+constexpr int kRowsPerWave = LA_ROWS_PER_WAVE;
+static_assert(kRowsPerWave == 16 || kRowsPerWave == 32, "16 or 32 rows");
 constexpr int kTokChunk = 8;
 constexpr float kL2Eps = 1e-6f;
 
@@ -144,14 +161,35 @@ __device__ __forceinline__ float wave_sum(float x)
     return x;
 }
 
-__device__ __forceinline__ f4 load_nt(const float *p)
+// Buffer resources: the tile base lives in SGPRs (uniform per workgroup),
+// each lane adds one 32-bit byte offset, row groups add a uniform offset.
+// Accesses past `bytes` read zero / are dropped by the hardware.
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+typedef unsigned u4 __attribute__((ext_vector_type(4)));
+constexpr int kBufDword3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format
+constexpr int kLoadPolicy = LA_LOAD_POLICY;
+constexpr int kStorePolicy = LA_STORE_POLICY;
+
+__device__ __forceinline__ BufRsrc make_rsrc(const float *base, uint32_t bytes)
 {
-    return __builtin_nontemporal_load(reinterpret_cast<const f4 *>(p));
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base),
+                                             static_cast<short>(0),
+                                             static_cast<int>(bytes),
+                                             kBufDword3);
 }
 
-__device__ __forceinline__ void store_nt(float *p, f4 x)
+__device__ __forceinline__ f4 buf_load(BufRsrc r, uint32_t voff,
+                                       uint32_t soff)
 {
-    __builtin_nontemporal_store(x, reinterpret_cast<f4 *>(p));
+    return __builtin_bit_cast(
+        f4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kLoadPolicy));
+}
+
+__device__ __forceinline__ void buf_store(BufRsrc r, uint32_t voff,
+                                          uint32_t soff, f4 x)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, x), r, voff,
+                                           soff, kStorePolicy);
 }
 
 // LDS-only barrier: orders LDS traffic across the workgroup without
@@ -177,34 +215,70 @@ struct TokLayout {
 };
 
 // Position of state row `row` inside the LDS v record: the rows a lane owns
-// (32 w + 8 i + r, i = 0..3) sit at 32 w + 4 r + i.
+// (R w + 8 i + r, i = 0..R/8-1, R rows per wave) sit at R w + (R/8) r + i.
 __device__ __forceinline__ int v_slot(int row)
 {
-    const int w = row >> 5, i = (row >> 3) & 3, r = row & 7;
-    return (w << 5) + (r << 2) + i;
+    constexpr int R = kRowsPerWave, RPL = kRowsPerWave / 8;
+    const int w = row / R, i = (row % R) / 8, r = row % 8;
+    return w * R + r * RPL + i;
 }
 
-// Prologue of token t for one wave: fills the LDS record `rec`.
+// Raw per-token inputs one lane loads for the prologue.
+template <int K, int V>
+struct TokRaw {
+    float q[K / 64], k[K / 64], e[K / 64], v[V / 64];
+    float g, beta;
+};
+
+// First half of the prologue of token t: global loads only, so they can be
+// issued ahead of the state tile and arrive first.
 template <int VAR, int K, int V, bool BF16IN>
-__device__ __forceinline__ void token_prologue(const Params &p, int b, int hv,
-                                               int t, float *rec, int lane)
+__device__ __forceinline__ void prologue_load(const Params &p, int b, int hv,
+                                              int t, int lane,
+                                              TokRaw<K, V> &raw)
 {
-    using L = TokLayout<VAR, K, V>;
     constexpr int EPL = K / 64;  // key elements per lane
     constexpr int VPL = V / 64;  // value elements per lane
     const int h = hv / p.group;
     const int64_t qo = b * p.sq_b + t * p.sq_t + h * p.sq_h;
     const int64_t ko = b * p.sk_b + t * p.sk_t + h * p.sk_h;
-    float qx[EPL], kx[EPL];
+    const int64_t vo = b * p.sv_b + t * p.sv_t + hv * p.sv_h;
+    const int64_t go = b * p.sg_b + t * p.sg_t + hv * p.sg_h;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        raw.q[i] = load_act<BF16IN>(p.q, qo + lane * EPL + i);
+        raw.k[i] = load_act<BF16IN>(p.k, ko + lane * EPL + i);
+        if constexpr (VAR == VAR_KDA)
+            raw.e[i] = p.g[go + lane * EPL + i];
+    }
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+        raw.v[i] = load_act<BF16IN>(p.v, vo + lane * VPL + i);
+    if constexpr (VAR == VAR_LA) {
+        raw.g = p.g ? p.g[hv] : 0.f;
+        raw.beta = 1.f;
+    } else {
+        raw.g = (VAR == VAR_GDN) ? p.g[go] : 0.f;
+        raw.beta = p.beta[b * p.sb_b + t * p.sb_t + hv * p.sb_h];
+    }
+}
+
+// Second half: l2norm, k.q, sigmoid, exp; writes the LDS record `rec`.
+template <int VAR, int K, int V>
+__device__ __forceinline__ void prologue_finish(const Params &p, int hv,
+                                                int lane,
+                                                const TokRaw<K, V> &raw,
+                                                float *rec)
+{
+    using L = TokLayout<VAR, K, V>;
+    constexpr int EPL = K / 64;
+    constexpr int VPL = V / 64;
     float ssq = 0.f, ssk = 0.f, qk = 0.f;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-        const int j = lane * EPL + i;
-        qx[i] = load_act<BF16IN>(p.q, qo + j);
-        kx[i] = load_act<BF16IN>(p.k, ko + j);
-        ssq = fmaf(qx[i], qx[i], ssq);
-        ssk = fmaf(kx[i], kx[i], ssk);
-        qk = fmaf(qx[i], kx[i], qk);
+        ssq = fmaf(raw.q[i], raw.q[i], ssq);
+        ssk = fmaf(raw.k[i], raw.k[i], ssk);
+        qk = fmaf(raw.q[i], raw.k[i], qk);
     }
     float rq = 1.f, rk = 1.f;
     qk = wave_sum(qk);
@@ -217,33 +291,25 @@ __device__ __forceinline__ void token_prologue(const Params &p, int b, int hv,
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int j = lane * EPL + i;
-        rec[L::kOff + j] = kx[i] * rk;
-        rec[L::qOff + j] = qx[i] * rq;
+        rec[L::kOff + j] = raw.k[i] * rk;
+        rec[L::qOff + j] = raw.q[i] * rq;
+        if constexpr (VAR == VAR_KDA)
+            rec[L::eOff + j] = __expf(raw.e[i]);
     }
-    const int64_t vo = b * p.sv_b + t * p.sv_t + hv * p.sv_h;
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        const int j = lane * VPL + i;
-        rec[L::vOff + v_slot(j)] = load_act<BF16IN>(p.v, vo + j);
-    }
-    const int64_t go = b * p.sg_b + t * p.sg_t + hv * p.sg_h;
-    if constexpr (VAR == VAR_KDA) {
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            const int j = lane * EPL + i;
-            rec[L::eOff + j] = __expf(p.g[go + j]);
-        }
-    }
+    for (int i = 0; i < VPL; ++i)
+        rec[L::vOff + v_slot(lane * VPL + i)] = raw.v[i];
     if (lane == 0) {
         float beta = 1.f, decay;
         if constexpr (VAR == VAR_LA) {
-            decay = p.g ? p.g[hv]
+            decay = p.g ? raw.g
                         : __expf(-exp2f(-8.f * static_cast<float>(hv + 1) /
                                         static_cast<float>(p.HV)));
         } else {
-            const float x = p.beta[b * p.sb_b + t * p.sb_t + hv * p.sb_h];
-            beta = (p.flags & LA_F_BETA_LOGIT) ? 1.f / (1.f + __expf(-x)) : x;
-            decay = (VAR == VAR_GDN) ? __expf(p.g[go]) : 1.f;
+            beta = (p.flags & LA_F_BETA_LOGIT)
+                       ? 1.f / (1.f + __expf(-raw.beta))
+                       : raw.beta;
+            decay = (VAR == VAR_GDN) ? __expf(raw.g) : 1.f;
         }
         rec[L::sOff + 0] = beta;
         rec[L::sOff + 1] = decay;
@@ -252,8 +318,14 @@ __device__ __forceinline__ void token_prologue(const Params &p, int b, int hv,
     }
 }
 
+#if LA_WAVES_PER_EU > 0
+#define LA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(LA_WAVES_PER_EU)))
+#else
+#define LA_OCCUPANCY
+#endif
+
 template <int VAR, int K, int V, bool BF16IN, bool BF16OUT>
-__global__ void __launch_bounds__((V / kRowsPerWave) * 64)
+__global__ void __launch_bounds__((V / kRowsPerWave) * 64) LA_OCCUPANCY
 decode_kernel(const Params p)
 {
     extern __shared__ f4 lds_raw[];
@@ -262,21 +334,24 @@ decode_kernel(const Params p)
     constexpr int NW = V / kRowsPerWave;  // waves per workgroup
     constexpr int RPL = kRowsPerWave / 8;  // rows per lane
     constexpr int CPL = K / 32;            // 16-byte chunks per lane and row
+    constexpr int TPW = (kTokChunk + NW - 1) / NW;  // prologue tokens per wave
 
     const int pair = blockIdx.x;
     const int b = pair / p.HV;
     const int hv = pair - b * p.HV;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // wave index and slots are uniform across the wave; saying so keeps the
+    // buffer descriptors and row offsets in SGPRs
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c8 = lane & 7;
     const int rs = lane >> 3;
     const int T = p.T;
 
-    const int r = p.ridx[b];
-    const int w = p.widx ? p.widx[b] : r;
+    const int r = __builtin_amdgcn_readfirstlane(p.ridx[b]);
+    const int w = __builtin_amdgcn_readfirstlane(p.widx ? p.widx[b] : r);
 
     // Output row written by this lane (lanes with c8 < RPL cover the wave's
-    // 32 rows exactly once): row 32 wave + 8 c8 + rs.
+    // rows exactly once): row R wave + 8 c8 + rs.
     const int orow = wave * kRowsPerWave + (c8 & (RPL - 1)) * 8 + rs;
     const bool olane = c8 < RPL;
     const int64_t obase = b * p.so_b + hv * p.so_h + orow;
@@ -288,24 +363,32 @@ decode_kernel(const Params p)
         return;
     }
 
-    // Gather the tile rows this lane owns (128-bit, streamed).
-    const float *src = p.pool + r * p.sp_slot + hv * p.sp_head;
+    // Gather the tile rows this lane owns: 128-bit buffer loads from the
+    // read tile; the lane's part of the address is one 32-bit offset.
+    const uint32_t row_bytes = static_cast<uint32_t>(p.sp_row) * 4u;
+    const uint32_t tile_bytes = static_cast<uint32_t>(
+        (static_cast<int64_t>(V - 1) * p.sp_row + K) * 4);
+    const uint32_t lane_off = rs * row_bytes + c8 * 16u;
+    const BufRsrc src = make_rsrc(p.pool + r * p.sp_slot + hv * p.sp_head,
+                                  tile_bytes);
     f4 S[RPL][CPL];
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
-        const int row = wave * kRowsPerWave + i * 8 + rs;
+        const uint32_t row0 = (wave * kRowsPerWave + i * 8) * row_bytes;
 #pragma unroll
         for (int m = 0; m < CPL; ++m)
-            S[i][m] = load_nt(src + row * p.sp_row + 4 * (c8 + 8 * m));
+            S[i][m] = buf_load(src, lane_off + m * 128u, row0);
     }
 
     for (int t0 = 0; t0 < T; t0 += kTokChunk) {
         const int nt = min(kTokChunk, T - t0);
         if (t0 > 0)
             lds_barrier();  // every wave is done with the previous chunk
-        for (int tt = wave; tt < nt; tt += NW)
-            token_prologue<VAR, K, V, BF16IN>(p, b, hv, t0 + tt,
-                                              lds + tt * L::size, lane);
+        for (int tt = wave; tt < nt; tt += NW) {
+            TokRaw<K, V> rw;
+            prologue_load<VAR, K, V, BF16IN>(p, b, hv, t0 + tt, lane, rw);
+            prologue_finish<VAR, K, V>(p, hv, lane, rw, lds + tt * L::size);
+        }
         lds_barrier();
 
         for (int tt = 0; tt < nt; ++tt) {
@@ -389,7 +472,7 @@ decode_kernel(const Params p)
                     S[i][m].w = fmaf(c[i], kk[m].w, S[i][m].w);
                 }
 
-            // output: lane (c8, rs) with c8 < RPL writes row 32 w + 8 c8 + rs
+            // output: lane (c8, rs) with c8 < RPL writes row R w + 8 c8 + rs
             float mine = o[0];
 #pragma unroll
             for (int i = 1; i < RPL; ++i)
@@ -398,28 +481,32 @@ decode_kernel(const Params p)
                 store_out<BF16OUT>(p.out, obase + t * p.so_t, mine);
 
             if (p.inter) {
-                float *dst = p.inter +
-                             ((static_cast<int64_t>(b) * T + t) * p.HV + hv) *
-                                 static_cast<int64_t>(V * K);
+                // contiguous [B, T, HV, V, K] cache: rows are K floats apart
+                const BufRsrc dst = make_rsrc(
+                    p.inter + ((static_cast<int64_t>(b) * T + t) * p.HV + hv) *
+                                  static_cast<int64_t>(V * K),
+                    V * K * 4);
+                const uint32_t ioff = rs * (K * 4u) + c8 * 16u;
 #pragma unroll
                 for (int i = 0; i < RPL; ++i) {
-                    const int row = wave * kRowsPerWave + i * 8 + rs;
+                    const uint32_t row0 = (wave * kRowsPerWave + i * 8) * K * 4u;
 #pragma unroll
                     for (int m = 0; m < CPL; ++m)
-                        store_nt(dst + row * K + 4 * (c8 + 8 * m), S[i][m]);
+                        buf_store(dst, ioff + m * 128u, row0, S[i][m]);
                 }
             }
         }
     }
 
     if (w >= 0) {  // in-place writeback to the write slot
-        float *dst = p.pool + w * p.sp_slot + hv * p.sp_head;
+        const BufRsrc dst = make_rsrc(p.pool + w * p.sp_slot + hv * p.sp_head,
+                                      tile_bytes);
 #pragma unroll
         for (int i = 0; i < RPL; ++i) {
-            const int row = wave * kRowsPerWave + i * 8 + rs;
+            const uint32_t row0 = (wave * kRowsPerWave + i * 8) * row_bytes;
 #pragma unroll
             for (int m = 0; m < CPL; ++m)
-                store_nt(dst + row * p.sp_row + 4 * (c8 + 8 * m), S[i][m]);
+                buf_store(dst, lane_off + m * 128u, row0, S[i][m]);
         }
     }
 }
@@ -574,6 +661,9 @@ la_status validate(const la_decode_args *a, int var)
         if (!no_overlap(3, st, ex, a->K))
             return LA_ERR_STRIDE;
     }
+    // a tile is addressed with 32-bit byte offsets from its first row
+    if ((static_cast<int64_t>(a->V - 1) * a->sp.row + a->K) * 4 > INT32_MAX)
+        return LA_ERR_STRIDE;
     // outputs must not overlap each other
     {
         const int64_t st[3] = {a->so.h, a->so.t, a->so.b};

@@ -160,6 +160,8 @@ REJECT = [
                                                    128)), "gdn", 3),
     ("out_rows_overlap", _mut(so=bnd.ActStrides(2 * 4 * 128, 4 * 128, 64)),
      "gdn", 3),
+    ("tile_rows_span_2GiB", _mut(sp=bnd.PoolStrides(2 ** 30, 2 ** 26, 2 ** 22)),
+     "gdn", 3),
     ("pool_misaligned", _mut(pool=FAKE + 0x1000004), "gdn", 4),
     ("pool_row_stride_misaligned",
      _mut(sp=bnd.PoolStrides(4 * 130 * 128, 130 * 128, 130)), "gdn", 4),
