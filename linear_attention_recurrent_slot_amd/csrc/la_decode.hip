@@ -49,14 +49,6 @@ enum Variant { VAR_LA = 0, VAR_GDN = 1, VAR_KDA = 2 };
 #ifndef LA_ROWS_PER_WAVE
 #define LA_ROWS_PER_WAVE 32  // state rows a wave keeps in VGPRs: 16 or 32
 #endif
-// Cache-policy bits of the state tile's buffer loads and stores (gfx950:
-// 1 = sc0, 2 = nt, 16 = sc1); 2 streams the tile through the caches.
-#ifndef LA_LOAD_POLICY
-#define LA_LOAD_POLICY 2
-#endif
-#ifndef LA_STORE_POLICY
-#define LA_STORE_POLICY 2
-#endif
 #ifndef LA_WAVES_PER_EU
 #define LA_WAVES_PER_EU 0  // >0: ask the register allocator for this occupancy
 #endif
@@ -69,7 +61,7 @@ constexpr float kL2Eps = 1e-6f;
 struct Params {
     int32_t B, T, HV, group;  // group = HV / H
     uint32_t flags;
-    int32_t pad_;
+    int32_t stream_loads;  // 1: nontemporal state loads, 0: cached loads
     const void *q;
     int64_t sq_b, sq_t, sq_h;
     const void *k;
@@ -167,8 +159,9 @@ __device__ __forceinline__ float wave_sum(float x)
 typedef __amdgpu_buffer_rsrc_t BufRsrc;
 typedef unsigned u4 __attribute__((ext_vector_type(4)));
 constexpr int kBufDword3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format
-constexpr int kLoadPolicy = LA_LOAD_POLICY;
-constexpr int kStorePolicy = LA_STORE_POLICY;
+// Cache-policy bits of the state tile's buffer accesses (gfx950: 2 = nt).
+constexpr int kStreamPolicy = 2;  // nontemporal: the tile is used once
+constexpr int kCachedPolicy = 0;
 
 __device__ __forceinline__ BufRsrc make_rsrc(const float *base, uint32_t bytes)
 {
@@ -178,18 +171,19 @@ __device__ __forceinline__ BufRsrc make_rsrc(const float *base, uint32_t bytes)
                                              kBufDword3);
 }
 
+template <int POLICY>
 __device__ __forceinline__ f4 buf_load(BufRsrc r, uint32_t voff,
                                        uint32_t soff)
 {
     return __builtin_bit_cast(
-        f4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kLoadPolicy));
+        f4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, POLICY));
 }
 
 __device__ __forceinline__ void buf_store(BufRsrc r, uint32_t voff,
                                           uint32_t soff, f4 x)
 {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, x), r, voff,
-                                           soff, kStorePolicy);
+                                           soff, kStreamPolicy);
 }
 
 // LDS-only barrier: orders LDS traffic across the workgroup without
@@ -372,12 +366,24 @@ decode_kernel(const Params p)
     const BufRsrc src = make_rsrc(p.pool + r * p.sp_slot + hv * p.sp_head,
                                   tile_bytes);
     f4 S[RPL][CPL];
+    if (p.stream_loads) {
 #pragma unroll
-    for (int i = 0; i < RPL; ++i) {
-        const uint32_t row0 = (wave * kRowsPerWave + i * 8) * row_bytes;
+        for (int i = 0; i < RPL; ++i) {
+            const uint32_t row0 = (wave * kRowsPerWave + i * 8) * row_bytes;
 #pragma unroll
-        for (int m = 0; m < CPL; ++m)
-            S[i][m] = buf_load(src, lane_off + m * 128u, row0);
+            for (int m = 0; m < CPL; ++m)
+                S[i][m] = buf_load<kStreamPolicy>(src, lane_off + m * 128u,
+                                                  row0);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            const uint32_t row0 = (wave * kRowsPerWave + i * 8) * row_bytes;
+#pragma unroll
+            for (int m = 0; m < CPL; ++m)
+                S[i][m] = buf_load<kCachedPolicy>(src, lane_off + m * 128u,
+                                                  row0);
+        }
     }
 
     for (int t0 = 0; t0 < T; t0 += kTokChunk) {
@@ -702,7 +708,10 @@ la_status launch(const la_decode_args *a, void *stream, int var)
     p.HV = a->HV;
     p.group = a->HV / a->H;
     p.flags = a->flags;
-    p.pad_ = 0;
+    // Streaming (nontemporal) state loads, except where cached loads
+    // measured faster on MI355X: calls that also write the per-token cache,
+    // and delta-rule calls of one or two tokens.
+    p.stream_loads = !(a->inter || (var != VAR_LA && a->T <= 2));
     p.q = a->q;
     p.sq_b = a->sq.b;
     p.sq_t = a->sq.t;
