@@ -106,8 +106,14 @@ def make_call(wl, d, inter, out, stream):
     if wl.variant != "lightning":
         flags = ((bnd.LA_F_L2NORM_QK if wl.l2norm else 0)
                  | (bnd.LA_F_BETA_LOGIT if wl.beta_logit else 0))
-    args = bnd.build_args(wl.variant, d.q, d.k, d.v, d.g, d.beta, d.pool(),
-                          d.read_idx, d.write_idx, out, inter, flags)
+    if d.token_slots is not None:
+        args = bnd.build_args(wl.variant, d.q, d.k, d.v, d.g, d.beta,
+                              d.pool(), None, None, out, inter, flags,
+                              d.token_slots, d.num_accepted)
+    else:
+        args = bnd.build_args(wl.variant, d.q, d.k, d.v, d.g, d.beta,
+                              d.pool(), d.read_idx, d.write_idx, out, inter,
+                              flags)
     entry = getattr(bnd.lib(), {"lightning": "la_decode",
                                 "gdn": "gdn_decode_mtp",
                                 "kda": "kda_decode_mtp"}[wl.variant])
@@ -163,9 +169,13 @@ def cpu_baseline(wl, seconds):
         beta = None if wl.beta is None else wl.beta[sel]
         widx = None if wl.write_idx is None else wl.write_idx[sel]
         t0 = time.perf_counter()
+        paged = {}
+        if wl.token_slots is not None:
+            paged = dict(token_slots=wl.token_slots[sel],
+                         num_accepted=wl.num_accepted[sel])
         oracle.decode(variant, wl.q[sel], wl.k[sel], wl.v[sel], g, beta,
                       wl.pool(), wl.read_idx[sel], widx, flags=flags,
-                      inter=wl.inter)
+                      inter=wl.inter, **paged)
         return time.perf_counter() - t0
 
     nb = wl.B
@@ -210,7 +220,12 @@ def main():
     copies = make_copies(wl, R, dev)
     calls = [make_call(wl, d, inter, out, stream) for d, inter, out in copies]
     for c in copies:
-        bad = lad.check_indices(c[0].read_idx, c[0].write_idx, wl.pool_size)
+        if wl.token_slots is not None:
+            bad = lad.check_token_slots(c[0].token_slots, c[0].num_accepted,
+                                        wl.pool_size, wl.T)
+        else:
+            bad = lad.check_indices(c[0].read_idx, c[0].write_idx,
+                                    wl.pool_size)
         if int(bad.item()) != 0:
             raise RuntimeError("workload index set violates the preconditions")
 
@@ -257,7 +272,8 @@ def main():
                    "pool_size": wl.pool_size, "qkv_dtype":
                    str(wl.q.dtype).replace("torch.", ""),
                    "state_dtype": "float32", "stride_mult": wl.stride_mult,
-                   "inter_cache": wl.inter, "rotation": R},
+                   "inter_cache": wl.inter,
+                   "paged_slots": wl.token_slots is not None, "rotation": R},
         "roofline": {"bound": "hbm", "achieved": achieved,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic},

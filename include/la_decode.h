@@ -17,6 +17,9 @@
  *        out[b,t,hv,:] = S q_t   (with the updated S)
  *        inter[b,t,hv] = S       (when an intermediate cache is given)
  *   4. If w >= 0: pool[w, hv] = S, in place.
+ *   With a per-token slot table (see la_decode_args), the seed slot is the
+ *   last accepted token's entry and step 4 becomes a write after every
+ *   token to that token's entry.
  *
  * Sources (page titles and sections):
  *  - "fix: wire h0_indices into Lightning Attention decode for state-pool
@@ -139,6 +142,21 @@ typedef struct la_decode_args {
     float *inter;      /* [B, T, HV, V, K] contiguous fp32, or NULL         */
     void *out;         /* [B, T, HV, V] in out_dtype                        */
     la_act_strides so;
+
+    /* Paged per-token state slots for speculative decoding (aiter KDA page,
+     * advisory review), or NULL. token_slots is a [B, T] int32 table with
+     * row stride token_slots_stride (>= T, in elements; a flat table is
+     * rejected rather than guessed at). Request b reads its seed state from
+     * slot token_slots[b][num_accepted[b] - 1], the slot of its last
+     * accepted token, and after each token t writes the state to slot
+     * token_slots[b][t] (a negative entry skips that write). When the table
+     * is given, read_idx and write_idx must be NULL and num_accepted ([B],
+     * contiguous) is required. A request whose num_accepted is outside
+     * [1, T] or whose seed entry is negative is padding: zero outputs, no
+     * pool or cache access. */
+    const int32_t *token_slots;
+    int64_t token_slots_stride;
+    const int32_t *num_accepted;
 } la_decode_args;
 
 /* Lightning decode (cuLA page): S <- lambda_h S + v k^T, o = S q.
@@ -164,6 +182,19 @@ la_status kda_decode_mtp(const la_decode_args *args, void *stream);
 la_status la_check_indices(int32_t B, int32_t pool_size,
                            const int32_t *read_idx, const int32_t *write_idx,
                            int32_t *dev_result, void *stream);
+
+/* Debug validator for the paged per-token slot table (same conventions as
+ * la_check_indices). Bits written to *dev_result:
+ *   1 = a seed slot >= pool_size,  2 = a table entry >= pool_size,
+ *   4 = two requests write the same slot,
+ *   8 = a request writes another request's seed slot,
+ *   16 = a num_accepted entry outside [1, T] (that request is padding).
+ * table_stride must be >= T. */
+la_status la_check_token_slots(int32_t B, int32_t T, int32_t pool_size,
+                               const int32_t *token_slots,
+                               int64_t table_stride,
+                               const int32_t *num_accepted,
+                               int32_t *dev_result, void *stream);
 
 /* Static description of a status code; never NULL. */
 const char *la_status_string(la_status status);

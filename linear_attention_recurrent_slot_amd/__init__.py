@@ -2,10 +2,13 @@
 
 Hand-written gfx950 HIP kernels behind a C ABI (include/la_decode.h), with a
 thin ctypes binding. Entry points: la_decode (Lightning), gdn_decode_mtp
-(gated delta rule), kda_decode_mtp (Kimi delta attention), check_indices.
+(gated delta rule), kda_decode_mtp (Kimi delta attention), and the index
+validators check_indices and check_token_slots.
 """
 from ._binding import (DecodeArgs, LaDecodeError, check_indices,
-                       gdn_decode_mtp, kda_decode_mtp, la_decode, lib)
+                       check_token_slots, gdn_decode_mtp, kda_decode_mtp,
+                       la_decode, lib)
 
-__all__ = ["DecodeArgs", "LaDecodeError", "check_indices", "gdn_decode_mtp",
-           "kda_decode_mtp", "la_decode", "lib"]
+__all__ = ["DecodeArgs", "LaDecodeError", "check_indices",
+           "check_token_slots", "gdn_decode_mtp", "kda_decode_mtp",
+           "la_decode", "lib"]

@@ -54,6 +54,9 @@ class DecodeArgs(ctypes.Structure):
         ("read_idx", ctypes.c_void_p), ("write_idx", ctypes.c_void_p),
         ("inter", ctypes.c_void_p),
         ("out", ctypes.c_void_p), ("so", ActStrides),
+        ("token_slots", ctypes.c_void_p),
+        ("token_slots_stride", ctypes.c_int64),
+        ("num_accepted", ctypes.c_void_p),
     ]
 
 
@@ -85,6 +88,10 @@ def lib() -> ctypes.CDLL:
         L.la_check_indices.argtypes = [ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p]
+        L.la_check_token_slots.restype = ctypes.c_int
+        L.la_check_token_slots.argtypes = [
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.la_status_string.restype = ctypes.c_char_p
         L.la_status_string.argtypes = [ctypes.c_int]
         L.la_version.restype = ctypes.c_int32
@@ -136,8 +143,21 @@ def _idx(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _slot_table(t, B, T):
+    """[B, >=T] int32 table with unit inner stride -> (pointer, row stride)."""
+    if t.dtype != torch.int32 or t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("token_slots must be a 2-D int32 [B, >=T] table "
+                         "with unit inner stride")
+    if t.shape[0] != B or t.shape[1] < T:
+        raise ValueError("token_slots shape %s does not cover [%d, %d]"
+                         % (tuple(t.shape), B, T))
+    stride = t.stride(0) if B > 1 else max(t.stride(0), t.shape[1])
+    return ctypes.c_void_p(t.data_ptr()), stride
+
+
 def build_args(variant: str, q, k, v, g, beta, pool, read_idx, write_idx,
-               out, inter, flags: int) -> DecodeArgs:
+               out, inter, flags: int, token_slots=None,
+               num_accepted=None) -> DecodeArgs:
     if q.dim() != 4 or v.dim() != 4:
         raise ValueError("q must be [B,T,H,K] and v [B,T,HV,V]")
     B, T, H, K = q.shape
@@ -148,7 +168,11 @@ def build_args(variant: str, q, k, v, g, beta, pool, read_idx, write_idx,
     # The library sees raw pointers: every extent it will index is checked
     # here against the tensors that back it.
     want = {"k": (k, (B, T, H, K)), "v": (v, (B, T, HV, V)),
-            "out": (out, (B, T, HV, V)), "read_idx": (read_idx, (B,))}
+            "out": (out, (B, T, HV, V))}
+    if read_idx is not None:
+        want["read_idx"] = (read_idx, (B,))
+    if num_accepted is not None:
+        want["num_accepted"] = (num_accepted, (B,))
     if tuple(pool.shape[1:]) != (HV, V, K):
         raise ValueError("pool shape %s does not match [*, %d, %d, %d]"
                          % (tuple(pool.shape), HV, V, K))
@@ -211,11 +235,18 @@ def build_args(variant: str, q, k, v, g, beta, pool, read_idx, write_idx,
             raise ValueError("inter must be contiguous float32 [B,T,HV,V,K]")
         a.inter = ctypes.c_void_p(inter.data_ptr())
     a.out, a.so = _act(out, 4, "out")
+    if token_slots is not None:
+        if token_slots.device != dev:
+            raise ValueError("token_slots is on %s, pool on %s"
+                             % (token_slots.device, dev))
+        a.token_slots, a.token_slots_stride = _slot_table(token_slots, B, T)
+    a.num_accepted = _idx(num_accepted)
     return a
 
 
 def _run(variant, entry, q, k, v, g, beta, pool, read_idx, write_idx, out,
-         inter, flags, out_dtype, stream):
+         inter, flags, out_dtype, stream, token_slots=None,
+         num_accepted=None):
     B, T = q.shape[0], q.shape[1]
     HV, V, K = v.shape[2], v.shape[3], q.shape[3]
     if out is None:
@@ -226,41 +257,51 @@ def _run(variant, entry, q, k, v, g, beta, pool, read_idx, write_idx, out,
     elif inter is False:
         inter = None
     args = build_args(variant, q, k, v, g, beta, pool, read_idx, write_idx,
-                      out, inter, flags)
+                      out, inter, flags, token_slots, num_accepted)
     st = call(entry, args, stream)
     if st != LA_OK:
         raise LaDecodeError(st, entry)
     return out, inter
 
 
-def la_decode(q, k, v, pool, read_idx, write_idx=None, *, lam=None, out=None,
-              inter=None, out_dtype=torch.float32, stream=None):
+# Every decode entry point takes either read_idx (+ optional write_idx) or,
+# for paged speculative decoding, token_slots ([B, >=T] int32 table) and
+# num_accepted ([B] int32) with read_idx=None.
+
+def la_decode(q, k, v, pool, read_idx=None, write_idx=None, *, lam=None,
+              out=None, inter=None, out_dtype=torch.float32, stream=None,
+              token_slots=None, num_accepted=None):
     """Lightning decode. lam: optional float32 [HV] decay factors (default:
     exp(-2^(-8(h+1)/HV)) per value head). Returns (out, inter)."""
     return _run("lightning", "la_decode", q, k, v, lam, None, pool, read_idx,
-                write_idx, out, inter, 0, out_dtype, stream)
+                write_idx, out, inter, 0, out_dtype, stream, token_slots,
+                num_accepted)
 
 
-def gdn_decode_mtp(q, k, v, g, beta, pool, read_idx, write_idx=None, *,
+def gdn_decode_mtp(q, k, v, g, beta, pool, read_idx=None, write_idx=None, *,
                    out=None, inter=None, l2norm_qk=False, beta_logit=False,
-                   out_dtype=torch.float32, stream=None):
+                   out_dtype=torch.float32, stream=None, token_slots=None,
+                   num_accepted=None):
     """Gated delta rule decode over T tokens. g: [B,T,HV] log-decay;
     beta: [B,T,HV] (logits if beta_logit). Returns (out, inter)."""
     flags = (LA_F_L2NORM_QK if l2norm_qk else 0) | \
         (LA_F_BETA_LOGIT if beta_logit else 0)
     return _run("gdn", "gdn_decode_mtp", q, k, v, g, beta, pool, read_idx,
-                write_idx, out, inter, flags, out_dtype, stream)
+                write_idx, out, inter, flags, out_dtype, stream, token_slots,
+                num_accepted)
 
 
-def kda_decode_mtp(q, k, v, g, beta, pool, read_idx, write_idx=None, *,
+def kda_decode_mtp(q, k, v, g, beta, pool, read_idx=None, write_idx=None, *,
                    out=None, inter=None, l2norm_qk=False, beta_logit=False,
-                   out_dtype=torch.float32, stream=None):
+                   out_dtype=torch.float32, stream=None, token_slots=None,
+                   num_accepted=None):
     """KDA decode over T tokens. g: [B,T,HV,K] per-key-channel log-decay.
     Returns (out, inter)."""
     flags = (LA_F_L2NORM_QK if l2norm_qk else 0) | \
         (LA_F_BETA_LOGIT if beta_logit else 0)
     return _run("kda", "kda_decode_mtp", q, k, v, g, beta, pool, read_idx,
-                write_idx, out, inter, flags, out_dtype, stream)
+                write_idx, out, inter, flags, out_dtype, stream, token_slots,
+                num_accepted)
 
 
 def check_indices(read_idx, write_idx, pool_size, result=None, stream=None):
@@ -275,4 +316,24 @@ def check_indices(read_idx, write_idx, pool_size, result=None, stream=None):
                                 _stream_handle(stream))
     if st != LA_OK:
         raise LaDecodeError(st, "la_check_indices")
+    return result
+
+
+def check_token_slots(token_slots, num_accepted, pool_size, T, result=None,
+                      stream=None):
+    """Launch the paged slot-table validator; returns the device int32 result
+    (bits: 1 seed out of range, 2 entry out of range, 4 slot written by two
+    requests, 8 slot written over another request's seed, 16 accepted count
+    outside [1, T])."""
+    B = num_accepted.shape[0]
+    ptr, stride = _slot_table(token_slots, B, T)
+    if result is None:
+        result = torch.empty((1,), dtype=torch.int32,
+                             device=num_accepted.device)
+    st = lib().la_check_token_slots(B, T, pool_size, ptr, stride,
+                                    _idx(num_accepted),
+                                    ctypes.c_void_p(result.data_ptr()),
+                                    _stream_handle(stream))
+    if st != LA_OK:
+        raise LaDecodeError(st, "la_check_token_slots")
     return result

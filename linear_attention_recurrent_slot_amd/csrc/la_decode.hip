@@ -79,6 +79,9 @@ struct Params {
     float *inter;
     void *out;
     int64_t so_b, so_t, so_h;
+    const int32_t *tslots;  // paged per-token slot table, or null
+    int64_t ts_stride;
+    const int32_t *naccept;
 };
 
 // ---------------------------------------------------------------- helpers
@@ -341,8 +344,19 @@ decode_kernel(const Params p)
     const int rs = lane >> 3;
     const int T = p.T;
 
-    const int r = __builtin_amdgcn_readfirstlane(p.ridx[b]);
-    const int w = __builtin_amdgcn_readfirstlane(p.widx ? p.widx[b] : r);
+    int r, w;
+    if (p.tslots) {
+        // paged slots: seed = entry of the last accepted token; the state is
+        // written after every token instead of once at the end
+        const int na = __builtin_amdgcn_readfirstlane(p.naccept[b]);
+        r = (na >= 1 && na <= T)
+                ? __builtin_amdgcn_readfirstlane(p.tslots[b * p.ts_stride + na - 1])
+                : -1;
+        w = -1;
+    } else {
+        r = __builtin_amdgcn_readfirstlane(p.ridx[b]);
+        w = __builtin_amdgcn_readfirstlane(p.widx ? p.widx[b] : r);
+    }
 
     // Output row written by this lane (lanes with c8 < RPL cover the wave's
     // rows exactly once): row R wave + 8 c8 + rs.
@@ -486,6 +500,23 @@ decode_kernel(const Params p)
             if (olane)
                 store_out<BF16OUT>(p.out, obase + t * p.so_t, mine);
 
+            if (p.tslots) {
+                const int ws = __builtin_amdgcn_readfirstlane(
+                    p.tslots[b * p.ts_stride + t]);
+                if (ws >= 0) {
+                    const BufRsrc dst = make_rsrc(
+                        p.pool + ws * p.sp_slot + hv * p.sp_head, tile_bytes);
+#pragma unroll
+                    for (int i = 0; i < RPL; ++i) {
+                        const uint32_t row0 =
+                            (wave * kRowsPerWave + i * 8) * row_bytes;
+#pragma unroll
+                        for (int m = 0; m < CPL; ++m)
+                            buf_store(dst, lane_off + m * 128u, row0, S[i][m]);
+                    }
+                }
+            }
+
             if (p.inter) {
                 // contiguous [B, T, HV, V, K] cache: rows are K floats apart
                 const BufRsrc dst = make_rsrc(
@@ -547,6 +578,58 @@ check_indices_kernel(int32_t B, int32_t pool_size, const int32_t *ridx,
                 f |= 4;
             if (rj == w)
                 f |= 8;
+        }
+    }
+    if (f)
+        atomicOr(&flags, f);
+    __syncthreads();
+    if (threadIdx.x == 0)
+        *result = flags;
+}
+
+// Validator of the paged per-token slot table (one workgroup).
+__global__ void __launch_bounds__(1024)
+check_token_slots_kernel(int32_t B, int32_t T, int32_t pool_size,
+                         const int32_t *tab, int64_t stride,
+                         const int32_t *nacc, int32_t *result)
+{
+    __shared__ int32_t flags;
+    if (threadIdx.x == 0)
+        flags = 0;
+    __syncthreads();
+    int32_t f = 0;
+    for (int i = threadIdx.x; i < B; i += blockDim.x) {
+        const int32_t na = nacc[i];
+        if (na < 1 || na > T) {
+            f |= 16;
+            continue;
+        }
+        const int32_t seed = tab[i * stride + na - 1];
+        if (seed >= pool_size)
+            f |= 1;
+        if (seed < 0)
+            continue;
+        for (int t = 0; t < T; ++t) {
+            const int32_t s = tab[i * stride + t];
+            if (s >= pool_size)
+                f |= 2;
+            if (s < 0)
+                continue;
+            for (int j = 0; j < B; ++j) {
+                if (j == i)
+                    continue;
+                const int32_t nj = nacc[j];
+                if (nj < 1 || nj > T)
+                    continue;
+                const int32_t sj = tab[j * stride + nj - 1];
+                if (sj < 0)
+                    continue;
+                if (sj == s)
+                    f |= 8;
+                for (int u = 0; u < T; ++u)
+                    if (tab[j * stride + u] == s)
+                        f |= 4;
+            }
         }
     }
     if (f)
@@ -647,7 +730,23 @@ la_status validate(const la_decode_args *a, int var)
     if (a->B == 0)
         return LA_OK;
 
-    if (!a->q || !a->k || !a->v || !a->pool || !a->read_idx || !a->out)
+    if (a->token_slots) {
+        // paged mode: the table replaces the read/write slot arrays
+        if (a->read_idx || a->write_idx)
+            return LA_ERR_ARG;
+        if (!a->num_accepted)
+            return LA_ERR_NULL;
+        if (a->token_slots_stride < a->T)
+            return LA_ERR_STRIDE;
+        if (!aligned(a->token_slots, 4) || !aligned(a->num_accepted, 4))
+            return LA_ERR_ALIGN;
+    } else {
+        if (!a->read_idx)
+            return LA_ERR_NULL;
+        if (a->num_accepted)
+            return LA_ERR_ARG;
+    }
+    if (!a->q || !a->k || !a->v || !a->pool || !a->out)
         return LA_ERR_NULL;
     if (var != VAR_LA && (!a->g || !a->beta))
         return LA_ERR_NULL;
@@ -711,7 +810,8 @@ la_status launch(const la_decode_args *a, void *stream, int var)
     // Streaming (nontemporal) state loads, except where cached loads
     // measured faster on MI355X: calls that also write the per-token cache,
     // and delta-rule calls of one or two tokens.
-    p.stream_loads = !(a->inter || (var != VAR_LA && a->T <= 2));
+    p.stream_loads =
+        !(a->inter || a->token_slots || (var != VAR_LA && a->T <= 2));
     p.q = a->q;
     p.sq_b = a->sq.b;
     p.sq_t = a->sq.t;
@@ -743,6 +843,9 @@ la_status launch(const la_decode_args *a, void *stream, int var)
     p.so_b = a->so.b;
     p.so_t = a->so.t;
     p.so_h = a->so.h;
+    p.tslots = a->token_slots;
+    p.ts_stride = a->token_slots_stride;
+    p.naccept = a->num_accepted;
 
     const bool bi = a->qkv_dtype == LA_BF16, bo = a->out_dtype == LA_BF16;
     KernelFn fn = var == VAR_LA    ? pick<VAR_LA>(a->K, a->V, bi, bo)
@@ -793,6 +896,29 @@ la_status la_check_indices(int32_t B, int32_t pool_size,
     void *kargs[] = {&B, &pool_size, &read_idx, &write_idx, &dev_result};
     const hipError_t e = hipLaunchKernel(
         reinterpret_cast<const void *>(check_indices_kernel), dim3(1),
+        dim3(1024), kargs, 0, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
+}
+
+la_status la_check_token_slots(int32_t B, int32_t T, int32_t pool_size,
+                               const int32_t *token_slots,
+                               int64_t table_stride,
+                               const int32_t *num_accepted,
+                               int32_t *dev_result, void *stream)
+{
+    if (B < 0 || T < 1 || pool_size < 1)
+        return LA_ERR_SHAPE;
+    if (table_stride < T)
+        return LA_ERR_STRIDE;
+    if (!dev_result || (B > 0 && (!token_slots || !num_accepted)))
+        return LA_ERR_NULL;
+    if (!aligned(dev_result, 4) || !aligned(token_slots, 4) ||
+        !aligned(num_accepted, 4))
+        return LA_ERR_ALIGN;
+    void *kargs[] = {&B, &T, &pool_size, &token_slots, &table_stride,
+                     &num_accepted, &dev_result};
+    const hipError_t e = hipLaunchKernel(
+        reinterpret_cast<const void *>(check_token_slots_kernel), dim3(1),
         dim3(1024), kargs, 0, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
 }

@@ -58,7 +58,7 @@ def _load():
         lib.oracle_decode.restype = ctypes.c_int
         lib.oracle_decode.argtypes = (
             [ctypes.c_int] * 8 + [dp] * 5 + [ctypes.c_int, dp, dp, ip, ip,
-                                             dp, dp])
+                                             dp, dp, ip, ctypes.c_int, ip])
         _lib = lib
     return _lib
 
@@ -87,12 +87,14 @@ def _ptr(a, ctype):
 
 
 def decode(variant, q, k, v, g, beta, pool, read_idx, write_idx=None,
-           flags=0, inter=False):
+           flags=0, inter=False, token_slots=None, num_accepted=None):
     """Run the fp64 recurrence.
 
     q, k: [B,T,H,K]; v: [B,T,HV,V]; g: Lightning [HV] decay factors or None,
     GDN [B,T,HV], KDA [B,T,HV,K] log-decay; beta: [B,T,HV] or None
     (Lightning); pool: logical [pool_size,HV,V,K]; read_idx/write_idx: [B].
+    token_slots: optional [B, >=T] per-token slot table (then read_idx and
+    write_idx are ignored and num_accepted [B] is required).
 
     Returns a dict with ``out`` [B,T,HV,V], ``pool`` (the pool after the
     call, float64) and ``inter`` ([B,T,HV,V,K] or None).
@@ -118,6 +120,17 @@ def decode(variant, q, k, v, g, beta, pool, read_idx, write_idx=None,
         raise ValueError("g shape %s != %s" % (g.shape, expect_g[variant]))
     if beta is not None and variant != LIGHTNING and beta.shape != (B, T, HV):
         raise ValueError("beta shape")
+    slots = _i32(token_slots)
+    acc = _i32(num_accepted)
+    stride = 0
+    if slots is not None:
+        if slots.ndim != 2 or slots.shape[0] != B or slots.shape[1] < T:
+            raise ValueError("token_slots must be [B, >=T]")
+        if acc is None or acc.shape != (B,):
+            raise ValueError("num_accepted must be [B]")
+        stride = slots.shape[1]
+        ridx = np.full((B,), -1, dtype=np.int32)
+        widx = None
     pool_out = pool_in.copy()
     # NaN until the oracle writes it: a position it skips cannot pass as 0
     out = np.full((B, T, HV, V), np.nan, dtype=np.float64)
@@ -128,7 +141,8 @@ def decode(variant, q, k, v, g, beta, pool, read_idx, write_idx=None,
         _ptr(v, dp), _ptr(g, dp),
         _ptr(beta if variant != LIGHTNING else None, dp), pool_size,
         _ptr(pool_in, dp), _ptr(pool_out, dp), _ptr(ridx, ctypes.c_int32),
-        _ptr(widx, ctypes.c_int32), _ptr(out, dp), _ptr(inter_a, dp))
+        _ptr(widx, ctypes.c_int32), _ptr(out, dp), _ptr(inter_a, dp),
+        _ptr(slots, ctypes.c_int32), stride, _ptr(acc, ctypes.c_int32))
     if rc != 0:
         raise ValueError("oracle_decode rejected its arguments (rc=%d)" % rc)
     return {"out": out, "pool": pool_out, "inter": inter_a}

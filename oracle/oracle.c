@@ -47,6 +47,15 @@
  *    written for every active request whatever its write slot.
  *  - All reads see the pool as it was before the call (pool_in); all writes
  *    go to pool_out.
+ *
+ * Paged per-token slots (aiter KDA page, advisory review: paged per-token
+ * state slots for speculative decoding, the seed slot being the table entry
+ * of the last accepted token, and the reviewer's demand that the table be
+ * two-dimensional and the accepted count at least one): with a slot table
+ * given, request b reads its state from slot table[b][num_accepted[b] - 1]
+ * and, after each token t, writes the state to slot table[b][t] when that
+ * entry is not negative. A request whose accepted count is outside [1, T]
+ * or whose seed entry is negative is padding, as above.
  */
 #include <math.h>
 #include <stddef.h>
@@ -95,18 +104,23 @@ static double lightning_decay(int head, int num_heads)
  *   read_idx, write_idx  [B]; write_idx may be NULL (= read_idx)
  *   out       [B][T][HV][V]
  *   inter     [B][T][HV][V][K] or NULL
+ *   slots     [B][slots_stride] per-token slot table, or NULL; when given,
+ *             read_idx and write_idx are ignored and accepted[B] is used
  */
 int oracle_decode(int variant, int B, int T, int H, int HV, int K, int V,
                   int flags, const double *q, const double *k, const double *v,
                   const double *g, const double *beta, int pool_size,
                   const double *pool_in, double *pool_out,
                   const int32_t *read_idx, const int32_t *write_idx,
-                  double *out, double *inter)
+                  double *out, double *inter, const int32_t *slots,
+                  int slots_stride, const int32_t *accepted)
 {
     if (B < 0 || T < 1 || H < 1 || HV < 1 || K < 1 || V < 1 || HV % H != 0)
         return -1;
     if (variant != ORACLE_LIGHTNING && variant != ORACLE_GDN &&
         variant != ORACLE_KDA)
+        return -1;
+    if (slots && (slots_stride < T || !accepted))
         return -1;
 
     const size_t tile = (size_t)V * (size_t)K;
@@ -122,8 +136,23 @@ int oracle_decode(int variant, int B, int T, int H, int HV, int K, int V,
     const int group = HV / H;
 
     for (int b = 0; b < B; ++b) {
-        const int r = read_idx[b];
-        const int w = write_idx ? write_idx[b] : r;
+        int r, w;
+        if (slots) {
+            const int na = accepted[b];
+            r = (na >= 1 && na <= T) ? slots[(size_t)b * slots_stride + na - 1]
+                                     : -1;
+            w = -1; /* per-token writes instead of one final write */
+            for (int t = 0; t < T; ++t)
+                if (slots[(size_t)b * slots_stride + t] >= pool_size) {
+                    free(S);
+                    free(qv);
+                    free(kv);
+                    return -1;
+                }
+        } else {
+            r = read_idx[b];
+            w = write_idx ? write_idx[b] : r;
+        }
         if (r >= pool_size || w >= pool_size) {
             free(S);
             free(qv);
@@ -196,6 +225,12 @@ int oracle_decode(int variant, int B, int T, int H, int HV, int K, int V,
                 }
                 if (inter)
                     memcpy(inter + bt * tile, S, tile * sizeof(double));
+                if (slots) {
+                    const int ws = slots[(size_t)b * slots_stride + t];
+                    if (ws >= 0)
+                        memcpy(pool_out + ((size_t)ws * HV + hv) * tile, S,
+                               tile * sizeof(double));
+                }
             }
             if (w >= 0)
                 memcpy(pool_out + ((size_t)w * HV + hv) * tile, S,

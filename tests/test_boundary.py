@@ -168,6 +168,23 @@ REJECT = [
     ("inter_misaligned", _mut(inter=FAKE + 0x2000008), "kda", 4),
     ("bf16_q_odd_address", _mut(q=FAKE + 1), "gdn", 4),
     ("read_idx_misaligned", _mut(read_idx=FAKE + 0x500002), "gdn", 4),
+    # paged per-token slots: the table replaces read/write slots, needs the
+    # accepted counts and an explicit row stride covering T
+    ("paged_with_read_idx", _mut(token_slots=FAKE + 0x700000,
+                                 num_accepted=FAKE + 0x700100,
+                                 token_slots_stride=2), "gdn", 6),
+    ("paged_without_num_accepted", _mut(token_slots=FAKE + 0x700000,
+                                        read_idx=None, write_idx=None,
+                                        token_slots_stride=2), "kda", 1),
+    ("paged_flat_table", _mut(token_slots=FAKE + 0x700000, read_idx=None,
+                              write_idx=None, num_accepted=FAKE + 0x700100,
+                              token_slots_stride=1), "kda", 3),
+    ("paged_misaligned_table", _mut(token_slots=FAKE + 0x700002,
+                                    read_idx=None, write_idx=None,
+                                    num_accepted=FAKE + 0x700100,
+                                    token_slots_stride=2), "lightning", 4),
+    ("num_accepted_without_table", _mut(num_accepted=FAKE + 0x700100),
+     "gdn", 6),
 ]
 
 
@@ -198,6 +215,16 @@ def test_check_indices_host_rejections(lib):
     assert L.la_check_indices(4, 4, FAKE, None, None, None) == 1
     assert L.la_check_indices(4, 4, None, None, FAKE, None) == 1
     assert L.la_check_indices(4, 4, FAKE, None, FAKE + 2, None) == 4
+
+
+def test_check_token_slots_host_rejections(lib):
+    L = lib
+    assert L.la_check_token_slots(-1, 2, 4, FAKE, 2, FAKE, FAKE, None) == 2
+    assert L.la_check_token_slots(4, 0, 4, FAKE, 2, FAKE, FAKE, None) == 2
+    assert L.la_check_token_slots(4, 2, 4, FAKE, 1, FAKE, FAKE, None) == 3
+    assert L.la_check_token_slots(4, 2, 4, None, 2, FAKE, FAKE, None) == 1
+    assert L.la_check_token_slots(4, 2, 4, FAKE, 2, None, FAKE, None) == 1
+    assert L.la_check_token_slots(4, 2, 4, FAKE, 2, FAKE, FAKE + 1, None) == 4
 
 
 def test_valid_call_without_gpu_reports_launch_failure():

@@ -37,6 +37,12 @@ MUTATIONS = {
         "u += S[(size_t)i * K + j] / (variant == ORACLE_GDN ? exp(g[bt]) "
         ": exp(g[bt * (size_t)K + j])) * kv[j];"),
     "l2norm_skipped_for_k": ("l2_normalise(kv, K);", ";"),
+    "paged_seed_off_by_one": (
+        "r = (na >= 1 && na <= T) ? slots[(size_t)b * slots_stride + na - 1]",
+        "r = (na >= 1 && na <= T) ? slots[(size_t)b * slots_stride + na % T]"),
+    "paged_write_wrong_token": (
+        "const int ws = slots[(size_t)b * slots_stride + t];",
+        "const int ws = slots[(size_t)b * slots_stride + T - 1 - t];"),
 }
 
 

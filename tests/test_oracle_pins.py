@@ -61,18 +61,32 @@ def test_hand_worked_examples(case):
                        for t in toks]])
         beta = np.array([[[float(_frac(t["beta"]))] for t in toks]])
     pool = np.random.default_rng(0).normal(size=(case["pool_size"], 1, V, K))
-    r, w = case["read_idx"][0], case["write_idx"][0]
-    pool[r, 0] = S0
-    res = oracle.decode(VARIANTS[var], q, k, v, g, beta, pool,
-                        case["read_idx"], case["write_idx"], inter=True)
     want_out = np.array([[float(_frac(x)) for x in o] for o in case["outputs"]])
     want_S = np.array([[float(_frac(x)) for x in row]
                        for row in case["final_state"]])
+    if "token_slots" in case:
+        table = case["token_slots"]
+        seed = table[0][case["num_accepted"][0] - 1]
+        pool[seed, 0] = S0
+        res = oracle.decode(VARIANTS[var], q, k, v, g, beta, pool, [0],
+                            inter=True, token_slots=table,
+                            num_accepted=case["num_accepted"])
+        S1 = np.array([[float(_frac(x)) for x in row]
+                       for row in case["state_after_token0"]])
+        assert _rel(res["pool"][table[0][0], 0], S1) < 1e-14
+        written = set(table[0])
+        w = table[0][T - 1]
+    else:
+        r, w = case["read_idx"][0], case["write_idx"][0]
+        pool[r, 0] = S0
+        res = oracle.decode(VARIANTS[var], q, k, v, g, beta, pool,
+                            case["read_idx"], case["write_idx"], inter=True)
+        written = {w}
     assert _rel(res["out"][0, :, 0, :], want_out) < 1e-14
     assert _rel(res["pool"][w, 0], want_S) < 1e-14
     assert _rel(res["inter"][0, T - 1, 0], want_S) < 1e-14
     for s in range(case["pool_size"]):
-        if s != w:
+        if s not in written:
             assert np.array_equal(res["pool"][s], pool[s])
 
 
@@ -390,3 +404,111 @@ def test_l2norm_of_zero_vectors_stays_finite():
     assert not res["out"].any()
     alpha = math.exp(c["g"][0, 0, 0])
     assert _rel(res["pool"][2, 0], alpha * c["pool"][2, 0]) < 1e-15
+
+
+# ---------------------------------------------- paged per-token state slots
+
+
+@pytest.mark.parametrize("variant", ["lightning", "gdn", "kda"])
+def test_paged_slots_rational_brute_force(variant):
+    """Per-token slot table against the exact product form: the seed comes
+    from the slot of the last accepted token and every token's state lands
+    in its own slot (negative entries skip)."""
+    rng = np.random.default_rng(77 + len(variant))
+    B, T, H, HV, V, K, pool_size = 3, 3, 1, 2, 3, 4, 12
+    table = [[4, 0, 7], [2, -1, 9], [5, 11, 1]]
+    accepted = [2, 1, 3]
+    pool = _dyadic(rng, (pool_size, HV, V, K))
+    q = _dyadic(rng, (B, T, H, K))
+    k = _dyadic(rng, (B, T, H, K), lo=-8, hi=9)
+    v = _dyadic(rng, (B, T, HV, V))
+    if variant == "lightning":
+        lam = rng.integers(1, 17, size=HV) / 16
+        g, beta = lam, None
+    elif variant == "gdn":
+        alpha = rng.integers(1, 17, size=(B, T, HV)) / 16
+        g, beta = np.log(alpha), rng.integers(0, 9, size=(B, T, HV)) / 8
+    else:
+        e = rng.integers(1, 17, size=(B, T, HV, K)) / 16
+        g, beta = np.log(e), rng.integers(0, 9, size=(B, T, HV)) / 8
+    res = oracle.decode(VARIANTS[variant], q, k, v, g, beta, pool, [0] * B,
+                        token_slots=table, num_accepted=accepted)
+    written = set()
+    for b in range(B):
+        seed = table[b][accepted[b] - 1]
+        for hv in range(HV):
+            toks = []
+            for t in range(T):
+                tok = dict(q=_to_frac(q[b, t, 0]), k=_to_frac(k[b, t, 0]),
+                           v=_to_frac(v[b, t, hv]))
+                if variant == "lightning":
+                    tok["lam"] = F(float(lam[hv]))
+                elif variant == "gdn":
+                    tok["alpha"] = F(float(alpha[b, t, hv]))
+                    tok["beta"] = F(float(beta[b, t, hv]))
+                else:
+                    tok["e"] = _to_frac(e[b, t, hv])
+                    tok["beta"] = F(float(beta[b, t, hv]))
+                toks.append(tok)
+            outs, states = br.run(variant, _to_frac(pool[seed, hv]), toks)
+            for t in range(T):
+                o = np.array([float(x) for x in outs[t]])
+                assert np.max(np.abs(res["out"][b, t, hv] - o)) <= 1e-12
+                if table[b][t] >= 0:
+                    st = np.array([[float(x) for x in row] for row in states[t]])
+                    assert np.max(np.abs(res["pool"][table[b][t], hv] - st)) <= 1e-12
+                    written.add(table[b][t])
+    for s in range(pool_size):
+        if s not in written:
+            np.testing.assert_array_equal(res["pool"][s], pool[s])
+
+
+def test_paged_slots_equal_scattered_cache():
+    """Paged mode = classic mode reading the seed slot with the per-token
+    cache on, the cache rows scattered to the table's slots."""
+    rng = np.random.default_rng(78)
+    c = _random_case(rng, oracle.KDA, B=3, T=4, pool_size=16)
+    table = np.array([[3, 8, 9, 10], [12, 0, -1, 13], [5, 6, 7, 14]])
+    accepted = np.array([4, 1, 2])
+    paged = oracle.decode(oracle.KDA, c["q"], c["k"], c["v"], c["g"],
+                          c["beta"], c["pool"], [0, 0, 0],
+                          flags=oracle.L2NORM_QK | oracle.BETA_LOGIT,
+                          token_slots=table, num_accepted=accepted)
+    seeds = [table[b, accepted[b] - 1] for b in range(3)]
+    dense = oracle.decode(oracle.KDA, c["q"], c["k"], c["v"], c["g"],
+                          c["beta"], c["pool"], seeds, [-1, -1, -1],
+                          flags=oracle.L2NORM_QK | oracle.BETA_LOGIT,
+                          inter=True)
+    np.testing.assert_array_equal(paged["out"], dense["out"])
+    want = c["pool"].copy()
+    for b in range(3):
+        for t in range(4):
+            if table[b, t] >= 0:
+                want[table[b, t]] = dense["inter"][b, t]
+    np.testing.assert_array_equal(paged["pool"], want)
+
+
+@pytest.mark.parametrize("bad", [0, 5, -2])
+def test_paged_slots_out_of_range_accepted_count_is_padding(bad):
+    """An accepted count outside [1, T] (the aiter reviewer's zero-accepted
+    case) never indexes the table: the request is padding."""
+    rng = np.random.default_rng(79)
+    c = _random_case(rng, oracle.GDN, B=2, T=4, pool_size=10)
+    table = [[1, 2, 3, 4], [5, 6, 7, 8]]
+    res = oracle.decode(oracle.GDN, c["q"], c["k"], c["v"], c["g"],
+                        c["beta"], c["pool"], [0, 0], token_slots=table,
+                        num_accepted=[2, bad])
+    assert not res["out"][1].any()
+    for s in (5, 6, 7, 8):
+        np.testing.assert_array_equal(res["pool"][s], c["pool"][s])
+    assert np.abs(res["out"][0]).max() > 0
+
+
+def test_paged_slots_negative_seed_is_padding():
+    rng = np.random.default_rng(80)
+    c = _random_case(rng, oracle.GDN, B=1, T=2, pool_size=4)
+    res = oracle.decode(oracle.GDN, c["q"], c["k"], c["v"], c["g"],
+                        c["beta"], c["pool"], [0], token_slots=[[-1, 3]],
+                        num_accepted=[1])
+    assert not res["out"].any()
+    np.testing.assert_array_equal(res["pool"], c["pool"])

@@ -194,10 +194,16 @@ SAMPLE = {"gdn_small_k64": None, "lightning_b33_h64": None,
           "kda_b256_t1": range(0, 256, 9), "kda_b256_t8": range(0, 256, 17)}
 
 
-@pytest.mark.parametrize("name", list(W.NAMED))
+@pytest.mark.parametrize("name", [n for n in W.NAMED if "paged" not in n])
 def test_named_workload_parity(name):
     wl = W.named(name)
     run_and_check(wl, SAMPLE[name])
+
+
+def test_named_paged_workload_parity():
+    wl = W.named("gdn_paged_b64_t4")
+    got = gpu_run_paged(wl, wl.token_slots, wl.num_accepted)
+    check_paged(wl, wl.token_slots, wl.num_accepted, got)
 
 
 def test_small_workload_host_normalised_inputs():
@@ -506,6 +512,12 @@ def test_workload_index_sets_are_valid():
     lad = _lad()
     for name in W.NAMED:
         wl = W.named(name)
+        if wl.token_slots is not None:
+            res = lad.check_token_slots(wl.token_slots.to(DEV),
+                                        wl.num_accepted.to(DEV),
+                                        wl.pool_size, wl.T)
+            assert int(res.item()) == 0, name
+            continue
         r = wl.read_idx.to(DEV)
         w = None if wl.write_idx is None else wl.write_idx.to(DEV)
         assert int(lad.check_indices(r, w, wl.pool_size).item()) == 0, name
@@ -520,3 +532,156 @@ def test_side_stream():
     with torch.cuda.stream(s):
         got = gpu_run(wl, stream=s)
     check_parity(wl, got, before)
+
+
+# ------------------------------------------------ paged per-token state slots
+
+
+def _paged_case(variant, seed, B=4, T=3, HV=4, K=128, V=128, inter=False):
+    """A workload plus a [B, T+2] slot table (wider than T: the row stride is
+    explicit), accepted counts in [1, T], disjoint rows, some -1 entries."""
+    pool_size = B * T + 5
+    wl = W.make("paged", variant, B=B, T=T, H=2, HV=HV, K=K, V=V,
+                pool_size=pool_size, seed=seed, inter=inter)
+    gen = torch.Generator().manual_seed(seed + 1)
+    perm = torch.randperm(pool_size, generator=gen).to(torch.int32)
+    table = torch.full((B, T + 2), 99, dtype=torch.int32)  # padding columns
+    table[:, :T] = perm[: B * T].view(B, T)
+    accepted = torch.randint(1, T + 1, (B,), generator=gen, dtype=torch.int32)
+    # a skipped snapshot on a token that is not any request's seed
+    for b in range(B):
+        t = (int(accepted[b]) % T)
+        if t != int(accepted[b]) - 1:
+            table[b, t] = -1
+            break
+    return wl, table, accepted
+
+
+def gpu_run_paged(wl, table, accepted, inter_fill=float("nan")):
+    lad = _lad()
+    d = wl.to(DEV)
+    tab, acc = table.to(DEV), accepted.to(DEV)
+    bad = lad.check_token_slots(tab, acc, wl.pool_size, wl.T)
+    assert int(bad.item()) in (0, 16), "invalid slot table in a test case"
+    pool = d.backing[:: wl.stride_mult]
+    inter = None
+    if wl.inter:
+        inter = torch.full((wl.B, wl.T, wl.HV, wl.V, wl.K), inter_fill,
+                           dtype=torch.float32, device=DEV)
+    kw = dict(inter=inter, out_dtype=wl.out_dtype, token_slots=tab,
+              num_accepted=acc)
+    if wl.variant == W.LIGHTNING:
+        out, _ = lad.la_decode(d.q, d.k, d.v, pool, lam=d.g, **kw)
+    else:
+        fn = lad.gdn_decode_mtp if wl.variant == W.GDN else lad.kda_decode_mtp
+        out, _ = fn(d.q, d.k, d.v, d.g, d.beta, pool, l2norm_qk=wl.l2norm,
+                    beta_logit=wl.beta_logit, **kw)
+    torch.cuda.synchronize()
+    return {"out": out.cpu(), "backing": d.backing.cpu(),
+            "inter": None if inter is None else inter.cpu()}
+
+
+def check_paged(wl, table, accepted, got):
+    ref = oracle.decode(VARIANT_CODE[wl.variant], wl.q, wl.k, wl.v, wl.g,
+                        wl.beta, wl.pool(), [0] * wl.B, flags=_flags(wl),
+                        inter=wl.inter, token_slots=table[:, : wl.T],
+                        num_accepted=accepted)
+    kind, tol_out, tol_state = _tol(wl)
+    assert _err(kind, got["out"].numpy(), ref["out"]) <= tol_out
+    written = set()
+    for b in range(wl.B):
+        na = int(accepted[b])
+        if not 1 <= na <= wl.T or int(table[b, na - 1]) < 0:
+            assert not got["out"][b].any()
+            if wl.inter:
+                assert torch.isnan(got["inter"][b]).all()
+            continue
+        for t in range(wl.T):
+            s = int(table[b, t])
+            if s >= 0:
+                written.add(s)
+        if wl.inter:
+            assert _err(kind, got["inter"][b].numpy(), ref["inter"][b]) <= tol_state
+    for s in sorted(written):
+        assert _err(kind, got["backing"][s].numpy(), ref["pool"][s]) <= tol_state
+    keep = torch.ones(wl.backing.shape[0], dtype=torch.bool)
+    if written:
+        keep[torch.tensor(sorted(written))] = False
+    assert torch.equal(got["backing"].view(torch.int32)[keep],
+                       wl.backing.view(torch.int32)[keep])
+
+
+@pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN, W.KDA])
+@pytest.mark.parametrize("T", [1, 3, 9])
+def test_paged_slots_parity(variant, T):
+    wl, table, accepted = _paged_case(variant, 300 + T, T=T, inter=True)
+    got = gpu_run_paged(wl, table, accepted)
+    check_paged(wl, table, accepted, got)
+
+
+@pytest.mark.parametrize("variant", [W.GDN, W.KDA])
+def test_paged_slots_equal_scattered_cache_bitwise(variant):
+    """Paged mode = classic mode reading the seed slot with the cache on,
+    cache rows scattered to the table's slots, bit for bit."""
+    wl, table, accepted = _paged_case(variant, 310, B=5, T=4)
+    got = gpu_run_paged(wl, table, accepted)
+    seeds = [int(table[b, int(accepted[b]) - 1]) for b in range(wl.B)]
+    dense = W.make("paged", variant, B=5, T=4, H=2, HV=4, K=128, V=128,
+                   pool_size=wl.pool_size, seed=310, inter=True,
+                   read_idx=seeds, write_idx=[-1] * wl.B)
+    dgot = gpu_run(dense)
+    assert torch.equal(got["out"], dgot["out"])
+    want = wl.backing.clone()
+    for b in range(wl.B):
+        for t in range(wl.T):
+            s = int(table[b, t])
+            if s >= 0:
+                want[s] = dgot["inter"][b, t]
+    assert torch.equal(got["backing"], want)
+
+
+def test_paged_slots_out_of_range_accepted_is_padding():
+    wl, table, accepted = _paged_case(W.KDA, 320, B=4, T=3, inter=True)
+    accepted[1] = 0
+    accepted[3] = 4
+    got = gpu_run_paged(wl, table, accepted)
+    check_paged(wl, table, accepted, got)
+    lad = _lad()
+    res = lad.check_token_slots(table.to(DEV), accepted.to(DEV),
+                                wl.pool_size, wl.T)
+    assert int(res.item()) == 16
+
+
+def test_paged_slots_flat_table_rejected():
+    """A flat table cannot be read as [B, T]: the explicit stride must cover
+    T (the aiter reviewer's corruption case is refused, not guessed)."""
+    lad = _lad()
+    wl, table, accepted = _paged_case(W.GDN, 330, B=2, T=2)
+    d = wl.to(DEV)
+    flat = table[:, :2].reshape(-1).to(DEV)
+    narrow = flat.as_strided((2, 2), (1, 1))  # rows overlapping: stride 1
+    with pytest.raises(lad.LaDecodeError):
+        lad.gdn_decode_mtp(d.q, d.k, d.v, d.g, d.beta, d.pool(),
+                           token_slots=narrow, num_accepted=accepted.to(DEV))
+    with pytest.raises(lad.LaDecodeError):
+        lad.gdn_decode_mtp(d.q, d.k, d.v, d.g, d.beta, d.pool(), d.read_idx,
+                           token_slots=table.to(DEV),
+                           num_accepted=accepted.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(d.backing.cpu(), wl.backing)
+
+
+@pytest.mark.parametrize("tab,acc,expect", [
+    ([[0, 1], [2, 3]], [1, 2], 0),
+    ([[0, 9], [2, 3]], [1, 2], 2),
+    ([[9, 1], [2, 3]], [1, 2], 3),
+    ([[0, 1], [1, 3]], [2, 2], 12),   # slot 1: both write it, it seeds 0
+    ([[0, 1], [2, 1]], [1, 1], 4),
+    ([[0, 1], [2, 3]], [0, 2], 16),
+    ([[0, -1], [2, 3]], [1, 1], 0),
+])
+def test_check_token_slots(tab, acc, expect):
+    lad = _lad()
+    t = torch.tensor(tab, dtype=torch.int32, device=DEV)
+    a = torch.tensor(acc, dtype=torch.int32, device=DEV)
+    assert int(lad.check_token_slots(t, a, 6, 2).item()) == expect

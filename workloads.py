@@ -49,6 +49,10 @@ class Workload:
     write_idx: Optional[torch.Tensor]  # int32 [B] or None (= read_idx)
     inter: bool                # cache the state after every token
     out_dtype: torch.dtype = torch.float32
+    # paged per-token slots: [B, T] table and [B] accepted counts; when set
+    # the call uses them instead of read_idx/write_idx
+    token_slots: Optional[torch.Tensor] = None
+    num_accepted: Optional[torch.Tensor] = None
 
     def pool(self, backing: Optional[torch.Tensor] = None) -> torch.Tensor:
         """The logical pool [pool_size, HV, V, K]: every stride_mult-th slot
@@ -73,6 +77,17 @@ class Workload:
         write per active (request, value head) tile, plus one cache write
         per token when intermediate states are kept."""
         tile = self.V * self.K * 4
+        if self.token_slots is not None:
+            reads = writes = 0
+            for row, na in zip(self.token_slots.tolist(),
+                               self.num_accepted.tolist()):
+                if 1 <= na <= self.T and row[na - 1] >= 0:
+                    reads += 1
+                    writes += sum(1 for s in row[: self.T] if s >= 0)
+            total = (reads + writes) * self.HV * tile
+            if self.inter:
+                total += reads * self.T * self.HV * tile
+            return total
         ridx = self.read_idx.tolist()
         widx = self.write_idx.tolist() if self.write_idx is not None else ridx
         reads = sum(1 for r in ridx if r >= 0)
@@ -96,7 +111,10 @@ class Workload:
             n += HV * 4
         if self.beta is not None:
             n += B * T * HV * 4
-        n += B * 4 * (2 if self.write_idx is not None else 1)
+        if self.token_slots is not None:
+            n += B * T * 4 + B * 4
+        else:
+            n += B * 4 * (2 if self.write_idx is not None else 1)
         out_size = torch.empty((), dtype=self.out_dtype).element_size()
         n += B * T * HV * V * out_size
         return n
@@ -110,8 +128,13 @@ def make(name, variant, B, T, H, HV, K, V, pool_size, *, seed,
          act_dtype=torch.bfloat16, pool_std=0.05, g_low=-1.0, g_high=0.0,
          l2norm=True, beta_logit=True, stride_mult=1, read_idx=None,
          write_idx=None, separate_write=False, write_skip=0.0,
-         inter=False, lightning_decay=None, out_dtype=torch.float32):
+         inter=False, lightning_decay=None, out_dtype=torch.float32,
+         paged=False):
     """Draw one workload.
+
+    paged: draw a [B, T] per-token slot table of distinct slots and accepted
+    counts uniform in [1, T] (needs pool_size >= B*T); read_idx/write_idx
+    then hold the seed slots and -1 (informational only).
 
     read_idx: explicit list, or None for ``randperm(pool_size)[:B]``.
     write_idx: explicit list, or None: equal to read_idx unless
@@ -132,6 +155,22 @@ def make(name, variant, B, T, H, HV, K, V, pool_size, *, seed,
         g = g_low + (g_high - g_low) * torch.rand(gshape, generator=gen)
         beta = torch.randn((B, T, HV), generator=gen)
     perm = _randperm(pool_size, gen)
+    if paged:
+        if pool_size < B * T:
+            raise ValueError("need pool_size >= B*T for a paged table")
+        table = perm[: B * T].view(B, T).to(torch.int32).contiguous()
+        accepted = torch.randint(1, T + 1, (B,), generator=gen,
+                                 dtype=torch.int32)
+        seeds = table[torch.arange(B), accepted.long() - 1]
+        return Workload(name=name, variant=variant, B=B, T=T, H=H, HV=HV,
+                        K=K, V=V, pool_size=pool_size,
+                        l2norm=l2norm if variant != LIGHTNING else False,
+                        beta_logit=beta_logit if variant != LIGHTNING else False,
+                        q=q, k=k, v=v, g=g, beta=beta, backing=backing,
+                        stride_mult=stride_mult, read_idx=seeds.contiguous(),
+                        write_idx=torch.full((B,), -1, dtype=torch.int32),
+                        inter=inter, out_dtype=out_dtype, token_slots=table,
+                        num_accepted=accepted)
     if read_idx is None:
         if B > pool_size:
             raise ValueError("need pool_size >= B for distinct slots")
@@ -209,6 +248,16 @@ def kda_b256(T, seed=5):
                 V=128, pool_size=512, seed=seed, g_low=-1.0, g_high=0.0)
 
 
+def gdn_paged_b64_t4(seed=6):
+    """GDN speculative verify with paged per-token state slots: B=64, T=4,
+    H=16, HV=32, K=V=128; each request owns 4 slots of a 256-slot pool, its
+    seed is the slot of its last accepted token (accepted ~U{1..4}) and the
+    state after every token is written to that token's slot."""
+    return make("gdn_paged_b64_t4", GDN, B=64, T=4, H=16, HV=32, K=128,
+                V=128, pool_size=256, seed=seed, g_low=-0.5, g_high=0.0,
+                paged=True)
+
+
 NAMED = {
     "gdn_small_k64": gdn_small_k64,
     "lightning_b33_h64": lightning_b33_h64,
@@ -216,6 +265,7 @@ NAMED = {
     "gdn_mtp_b32_t4": gdn_mtp_b32_t4,
     "kda_b256_t1": lambda seed=5: kda_b256(1, seed),
     "kda_b256_t8": lambda seed=5: kda_b256(8, seed),
+    "gdn_paged_b64_t4": gdn_paged_b64_t4,
 }
 
 
