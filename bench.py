@@ -81,7 +81,7 @@ def make_copies(wl, R, dev):
         d = wl.to(dev)
         if i > 0:
             gen = torch.Generator(device=dev).manual_seed(1000 + i)
-            std = float(wl.backing.std())
+            std = float(wl.backing.float().std())
             d.backing.normal_(0.0, std, generator=gen)
             for name in ("q", "k", "v"):
                 t = getattr(d, name)
@@ -89,7 +89,7 @@ def make_copies(wl, R, dev):
         inter = None
         if wl.inter:
             inter = torch.empty((wl.B, wl.T, wl.HV, wl.V, wl.K),
-                                dtype=torch.float32, device=dev)
+                                dtype=wl.backing.dtype, device=dev)
         out = torch.empty((wl.B, wl.T, wl.HV, wl.V), dtype=wl.out_dtype,
                           device=dev)
         copies.append((d, inter, out))
@@ -210,7 +210,7 @@ def main():
     stream = torch.cuda.current_stream(dev)
     wl = workloads.named(args.workload)
     per_call = wl.state_bytes() + wl.io_bytes()
-    pool_bytes = wl.backing.numel() * 4
+    pool_bytes = wl.backing.numel() * wl.backing.element_size()
     R = args.rotate or max(1, math.ceil((1 << 30) / per_call))
     print("[bench] workload %s: B=%d T=%d H=%d HV=%d K=%d V=%d pool=%d, "
           "%.1f MB per call, rotating %d copies (%.2f GB of pools)"
@@ -271,7 +271,8 @@ def main():
                    "T": wl.T, "H": wl.H, "HV": wl.HV, "K": wl.K, "V": wl.V,
                    "pool_size": wl.pool_size, "qkv_dtype":
                    str(wl.q.dtype).replace("torch.", ""),
-                   "state_dtype": "float32", "stride_mult": wl.stride_mult,
+                   "state_dtype": str(wl.backing.dtype).replace("torch.", ""),
+                   "stride_mult": wl.stride_mult,
                    "inter_cache": wl.inter,
                    "paged_slots": wl.token_slots is not None, "rotation": R},
         "roofline": {"bound": "hbm", "achieved": achieved,

@@ -7,7 +7,8 @@
  *   1. r = read_idx[b], w = write_idx ? write_idx[b] : r.
  *      r < 0 marks a padded request: its outputs are set to 0 and neither
  *      the pool nor the intermediate cache is read or written.
- *   2. S = pool[r, hv] (a V x K fp32 tile, k contiguous).
+ *   2. S = pool[r, hv] (a V x K tile, k contiguous, fp32 or bf16 in the
+ *      pool, fp32 in the computation).
  *   3. For t = 0..T-1 (tokens in order), with q/k head h = hv / (HV / H):
  *        Lightning:  S <- lambda[hv] * S + v_t k_t^T
  *        GDN:        S <- exp(g[b,t,hv]) * S
@@ -75,8 +76,9 @@ typedef enum la_status {
     LA_ERR_STRIDE = 3,      /* negative stride, innermost stride != 1,
                                overlapping pool tiles or outputs, or a tile
                                whose rows span 2 GiB or more                 */
-    LA_ERR_ALIGN = 4,       /* pool / cache row not 16-byte aligned, or an
-                               activation not aligned to its element size    */
+    LA_ERR_ALIGN = 4,       /* pool / cache row not aligned to four state
+                               elements, or an activation not aligned to its
+                               element size                                  */
     LA_ERR_DTYPE = 5,       /* unknown dtype code                            */
     LA_ERR_ARG = 6,         /* argument inconsistent with the entry point
                                (e.g. beta or flags given to la_decode, an
@@ -115,6 +117,9 @@ typedef struct la_decode_args {
     uint32_t flags;    /* LA_F_* bits                                       */
     la_dtype qkv_dtype; /* dtype of q, k, v                                 */
     la_dtype out_dtype; /* dtype of out                                     */
+    la_dtype state_dtype; /* dtype of pool and inter: LA_F32, or LA_BF16
+                             (widened exactly to fp32 on load; all math in
+                             fp32; rounded to nearest even on store)        */
 
     const void *q;     /* [B, T, H, K]   */
     la_act_strides sq;
@@ -134,12 +139,13 @@ typedef struct la_decode_args {
     const float *beta;
     la_act_strides sbeta;
 
-    float *pool;       /* [pool_size, HV, V, K] fp32, updated in place;
-                          base and every row start 16-byte aligned         */
+    void *pool;        /* [pool_size, HV, V, K] in state_dtype, updated in
+                          place; base and every row start aligned to four
+                          elements (16 B fp32, 8 B bf16)                   */
     la_pool_strides sp;
     const int32_t *read_idx;  /* [B] contiguous                             */
     const int32_t *write_idx; /* [B] contiguous, or NULL (= read_idx)       */
-    float *inter;      /* [B, T, HV, V, K] contiguous fp32, or NULL         */
+    void *inter;       /* [B, T, HV, V, K] contiguous, state_dtype, or NULL */
     void *out;         /* [B, T, HV, V] in out_dtype                        */
     la_act_strides so;
 
@@ -199,7 +205,8 @@ la_status la_check_token_slots(int32_t B, int32_t T, int32_t pool_size,
 /* Static description of a status code; never NULL. */
 const char *la_status_string(la_status status);
 
-/* Library version as major * 10000 + minor * 100 + patch. */
+/* Library version as major * 100 + minor (2.00: state_dtype and paged
+ * per-token slots in la_decode_args). */
 int32_t la_version(void);
 
 #ifdef __cplusplus

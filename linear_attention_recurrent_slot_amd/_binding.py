@@ -45,6 +45,7 @@ class DecodeArgs(ctypes.Structure):
         ("HV", ctypes.c_int32), ("K", ctypes.c_int32), ("V", ctypes.c_int32),
         ("pool_size", ctypes.c_int32), ("flags", ctypes.c_uint32),
         ("qkv_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+        ("state_dtype", ctypes.c_int),
         ("q", ctypes.c_void_p), ("sq", ActStrides),
         ("k", ctypes.c_void_p), ("sk", ActStrides),
         ("v", ctypes.c_void_p), ("sv", ActStrides),
@@ -162,9 +163,11 @@ def build_args(variant: str, q, k, v, g, beta, pool, read_idx, write_idx,
         raise ValueError("q must be [B,T,H,K] and v [B,T,HV,V]")
     B, T, H, K = q.shape
     HV, V = v.shape[2], v.shape[3]
-    if pool.dim() != 4 or pool.dtype != torch.float32 or pool.stride(3) != 1:
-        raise ValueError("pool must be a float32 [pool_size, HV, V, K] tensor "
-                         "with unit innermost stride")
+    if (pool.dim() != 4 or pool.dtype not in (torch.float32, torch.bfloat16)
+            or pool.stride(3) != 1):
+        raise ValueError("pool must be a float32 or bfloat16 "
+                         "[pool_size, HV, V, K] tensor with unit innermost "
+                         "stride")
     # The library sees raw pointers: every extent it will index is checked
     # here against the tensors that back it.
     want = {"k": (k, (B, T, H, K)), "v": (v, (B, T, HV, V)),
@@ -203,6 +206,7 @@ def build_args(variant: str, q, k, v, g, beta, pool, read_idx, write_idx,
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k and v must share one dtype")
     a.out_dtype = _dtype_code(out, "out")
+    a.state_dtype = _dtype_code(pool, "pool")
     a.q, a.sq = _act(q, 4, "q")
     a.k, a.sk = _act(k, 4, "k")
     a.v, a.sv = _act(v, 4, "v")
@@ -230,9 +234,10 @@ def build_args(variant: str, q, k, v, g, beta, pool, read_idx, write_idx,
     a.read_idx = _idx(read_idx)
     a.write_idx = _idx(write_idx)
     if inter is not None:
-        if (inter.dtype != torch.float32 or not inter.is_contiguous()
+        if (inter.dtype != pool.dtype or not inter.is_contiguous()
                 or tuple(inter.shape) != (B, T, HV, V, K)):
-            raise ValueError("inter must be contiguous float32 [B,T,HV,V,K]")
+            raise ValueError("inter must be a contiguous [B,T,HV,V,K] tensor "
+                             "of the pool's dtype")
         a.inter = ctypes.c_void_p(inter.data_ptr())
     a.out, a.so = _act(out, 4, "out")
     if token_slots is not None:
@@ -252,7 +257,7 @@ def _run(variant, entry, q, k, v, g, beta, pool, read_idx, write_idx, out,
     if out is None:
         out = torch.empty((B, T, HV, V), dtype=out_dtype, device=q.device)
     if inter is True:
-        inter = torch.empty((B, T, HV, V, K), dtype=torch.float32,
+        inter = torch.empty((B, T, HV, V, K), dtype=pool.dtype,
                             device=q.device)
     elif inter is False:
         inter = None

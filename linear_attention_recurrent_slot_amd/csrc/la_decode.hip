@@ -72,11 +72,11 @@ struct Params {
     int64_t sg_b, sg_t, sg_h;
     const float *beta;
     int64_t sb_b, sb_t, sb_h;
-    float *pool;
+    void *pool;  // fp32 or bf16 elements (state dtype)
     int64_t sp_slot, sp_head, sp_row;
     const int32_t *ridx;
     const int32_t *widx;
-    float *inter;
+    void *inter;  // state dtype
     void *out;
     int64_t so_b, so_t, so_h;
     const int32_t *tslots;  // paged per-token slot table, or null
@@ -166,28 +166,63 @@ constexpr int kBufDword3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format
 constexpr int kStreamPolicy = 2;  // nontemporal: the tile is used once
 constexpr int kCachedPolicy = 0;
 
-__device__ __forceinline__ BufRsrc make_rsrc(const float *base, uint32_t bytes)
+__device__ __forceinline__ BufRsrc make_rsrc(const void *base, uint32_t bytes)
 {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base),
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base),
                                              static_cast<short>(0),
                                              static_cast<int>(bytes),
                                              kBufDword3);
 }
 
-template <int POLICY>
-__device__ __forceinline__ f4 buf_load(BufRsrc r, uint32_t voff,
-                                       uint32_t soff)
-{
-    return __builtin_bit_cast(
-        f4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, POLICY));
-}
+typedef unsigned u2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+typedef float f2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ void buf_store(BufRsrc r, uint32_t voff,
-                                          uint32_t soff, f4 x)
-{
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, x), r, voff,
-                                           soff, kStreamPolicy);
-}
+// State tile I/O in the pool's element type. A lane's chunk is always four
+// consecutive columns: 16 bytes of fp32 or 8 bytes of bf16. bf16 widens
+// exactly to fp32 on load and rounds to nearest even (v_cvt_pk_bf16_f32)
+// on store; all arithmetic stays fp32.
+template <bool BF16S>
+struct StateIO {
+    static constexpr uint32_t ES = BF16S ? 2u : 4u;  // bytes per element
+
+    template <int POLICY>
+    static __device__ __forceinline__ f4 load(BufRsrc r, uint32_t voff,
+                                              uint32_t soff)
+    {
+        if constexpr (BF16S) {
+            const u2 h = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff,
+                                                              POLICY);
+            f4 x;
+            x.x = __uint_as_float(h.x << 16);
+            x.y = __uint_as_float(h.x & 0xffff0000u);
+            x.z = __uint_as_float(h.y << 16);
+            x.w = __uint_as_float(h.y & 0xffff0000u);
+            return x;
+        } else {
+            return __builtin_bit_cast(
+                f4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff,
+                                                          POLICY));
+        }
+    }
+
+    static __device__ __forceinline__ void store(BufRsrc r, uint32_t voff,
+                                                 uint32_t soff, f4 x)
+    {
+        if constexpr (BF16S) {
+            const f2 lo = {x.x, x.y}, hi = {x.z, x.w};
+            u2 h;
+            h.x = __builtin_bit_cast(unsigned, __builtin_convertvector(lo, bf2));
+            h.y = __builtin_bit_cast(unsigned, __builtin_convertvector(hi, bf2));
+            __builtin_amdgcn_raw_buffer_store_b64(h, r, voff, soff,
+                                                  kStreamPolicy);
+        } else {
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, x),
+                                                   r, voff, soff,
+                                                   kStreamPolicy);
+        }
+    }
+};
 
 // LDS-only barrier: orders LDS traffic across the workgroup without
 // waiting for outstanding global loads (the state tile may still be in
@@ -321,10 +356,14 @@ __device__ __forceinline__ void prologue_finish(const Params &p, int hv,
 #define LA_OCCUPANCY
 #endif
 
-template <int VAR, int K, int V, bool BF16IN, bool BF16OUT>
+template <int VAR, int K, int V, bool BF16IN, bool BF16OUT, bool BF16S>
 __global__ void __launch_bounds__((V / kRowsPerWave) * 64) LA_OCCUPANCY
 decode_kernel(const Params p)
 {
+    using IO = StateIO<BF16S>;
+    constexpr uint32_t ES = IO::ES;
+    constexpr uint32_t kChunk = 4 * ES;        // bytes of one lane chunk
+    constexpr uint32_t kChunkStep = 32 * ES;   // bytes between chunks m, m+1
     extern __shared__ f4 lds_raw[];
     float *lds = reinterpret_cast<float *>(lds_raw);
     using L = TokLayout<VAR, K, V>;
@@ -373,12 +412,13 @@ decode_kernel(const Params p)
 
     // Gather the tile rows this lane owns: 128-bit buffer loads from the
     // read tile; the lane's part of the address is one 32-bit offset.
-    const uint32_t row_bytes = static_cast<uint32_t>(p.sp_row) * 4u;
+    const uint32_t row_bytes = static_cast<uint32_t>(p.sp_row) * ES;
     const uint32_t tile_bytes = static_cast<uint32_t>(
-        (static_cast<int64_t>(V - 1) * p.sp_row + K) * 4);
-    const uint32_t lane_off = rs * row_bytes + c8 * 16u;
-    const BufRsrc src = make_rsrc(p.pool + r * p.sp_slot + hv * p.sp_head,
-                                  tile_bytes);
+        (static_cast<int64_t>(V - 1) * p.sp_row + K) * ES);
+    const uint32_t lane_off = rs * row_bytes + c8 * kChunk;
+    char *const pool = static_cast<char *>(p.pool);
+    const BufRsrc src = make_rsrc(
+        pool + (r * p.sp_slot + hv * p.sp_head) * ES, tile_bytes);
     f4 S[RPL][CPL];
     if (p.stream_loads) {
 #pragma unroll
@@ -386,8 +426,8 @@ decode_kernel(const Params p)
             const uint32_t row0 = (wave * kRowsPerWave + i * 8) * row_bytes;
 #pragma unroll
             for (int m = 0; m < CPL; ++m)
-                S[i][m] = buf_load<kStreamPolicy>(src, lane_off + m * 128u,
-                                                  row0);
+                S[i][m] = IO::template load<kStreamPolicy>(
+                    src, lane_off + m * kChunkStep, row0);
         }
     } else {
 #pragma unroll
@@ -395,8 +435,8 @@ decode_kernel(const Params p)
             const uint32_t row0 = (wave * kRowsPerWave + i * 8) * row_bytes;
 #pragma unroll
             for (int m = 0; m < CPL; ++m)
-                S[i][m] = buf_load<kCachedPolicy>(src, lane_off + m * 128u,
-                                                  row0);
+                S[i][m] = IO::template load<kCachedPolicy>(
+                    src, lane_off + m * kChunkStep, row0);
         }
     }
 
@@ -505,14 +545,16 @@ decode_kernel(const Params p)
                     p.tslots[b * p.ts_stride + t]);
                 if (ws >= 0) {
                     const BufRsrc dst = make_rsrc(
-                        p.pool + ws * p.sp_slot + hv * p.sp_head, tile_bytes);
+                        pool + (ws * p.sp_slot + hv * p.sp_head) * ES,
+                        tile_bytes);
 #pragma unroll
                     for (int i = 0; i < RPL; ++i) {
                         const uint32_t row0 =
                             (wave * kRowsPerWave + i * 8) * row_bytes;
 #pragma unroll
                         for (int m = 0; m < CPL; ++m)
-                            buf_store(dst, lane_off + m * 128u, row0, S[i][m]);
+                            IO::store(dst, lane_off + m * kChunkStep, row0,
+                                      S[i][m]);
                     }
                 }
             }
@@ -520,30 +562,32 @@ decode_kernel(const Params p)
             if (p.inter) {
                 // contiguous [B, T, HV, V, K] cache: rows are K floats apart
                 const BufRsrc dst = make_rsrc(
-                    p.inter + ((static_cast<int64_t>(b) * T + t) * p.HV + hv) *
-                                  static_cast<int64_t>(V * K),
-                    V * K * 4);
-                const uint32_t ioff = rs * (K * 4u) + c8 * 16u;
+                    static_cast<char *>(p.inter) +
+                        ((static_cast<int64_t>(b) * T + t) * p.HV + hv) *
+                            static_cast<int64_t>(V * K * ES),
+                    V * K * ES);
+                const uint32_t ioff = rs * (K * ES) + c8 * kChunk;
 #pragma unroll
                 for (int i = 0; i < RPL; ++i) {
-                    const uint32_t row0 = (wave * kRowsPerWave + i * 8) * K * 4u;
+                    const uint32_t row0 =
+                        (wave * kRowsPerWave + i * 8) * K * ES;
 #pragma unroll
                     for (int m = 0; m < CPL; ++m)
-                        buf_store(dst, ioff + m * 128u, row0, S[i][m]);
+                        IO::store(dst, ioff + m * kChunkStep, row0, S[i][m]);
                 }
             }
         }
     }
 
     if (w >= 0) {  // in-place writeback to the write slot
-        const BufRsrc dst = make_rsrc(p.pool + w * p.sp_slot + hv * p.sp_head,
-                                      tile_bytes);
+        const BufRsrc dst = make_rsrc(
+            pool + (w * p.sp_slot + hv * p.sp_head) * ES, tile_bytes);
 #pragma unroll
         for (int i = 0; i < RPL; ++i) {
             const uint32_t row0 = (wave * kRowsPerWave + i * 8) * row_bytes;
 #pragma unroll
             for (int m = 0; m < CPL; ++m)
-                buf_store(dst, lane_off + m * 128u, row0, S[i][m]);
+                IO::store(dst, lane_off + m * kChunkStep, row0, S[i][m]);
         }
     }
 }
@@ -643,24 +687,32 @@ check_token_slots_kernel(int32_t B, int32_t T, int32_t pool_size,
 
 typedef void (*KernelFn)(const Params);
 
-template <int VAR, int K, int V>
-KernelFn pick_dtype(bool bf16_in, bool bf16_out)
+template <int VAR, int K, int V, bool BF16S>
+KernelFn pick_io(bool bf16_in, bool bf16_out)
 {
     if (bf16_in)
-        return bf16_out ? decode_kernel<VAR, K, V, true, true>
-                        : decode_kernel<VAR, K, V, true, false>;
-    return bf16_out ? decode_kernel<VAR, K, V, false, true>
-                    : decode_kernel<VAR, K, V, false, false>;
+        return bf16_out ? decode_kernel<VAR, K, V, true, true, BF16S>
+                        : decode_kernel<VAR, K, V, true, false, BF16S>;
+    return bf16_out ? decode_kernel<VAR, K, V, false, true, BF16S>
+                    : decode_kernel<VAR, K, V, false, false, BF16S>;
+}
+
+template <int VAR, int K, int V>
+KernelFn pick_dtype(bool bf16_in, bool bf16_out, bool bf16_state)
+{
+    return bf16_state ? pick_io<VAR, K, V, true>(bf16_in, bf16_out)
+                      : pick_io<VAR, K, V, false>(bf16_in, bf16_out);
 }
 
 template <int VAR>
-KernelFn pick(int K, int V, bool bf16_in, bool bf16_out)
+KernelFn pick(int K, int V, bool bf16_in, bool bf16_out, bool bf16_state)
 {
     if (K == 128)
-        return V == 128 ? pick_dtype<VAR, 128, 128>(bf16_in, bf16_out)
-                        : pick_dtype<VAR, 128, 64>(bf16_in, bf16_out);
-    return V == 128 ? pick_dtype<VAR, 64, 128>(bf16_in, bf16_out)
-                    : pick_dtype<VAR, 64, 64>(bf16_in, bf16_out);
+        return V == 128
+                   ? pick_dtype<VAR, 128, 128>(bf16_in, bf16_out, bf16_state)
+                   : pick_dtype<VAR, 128, 64>(bf16_in, bf16_out, bf16_state);
+    return V == 128 ? pick_dtype<VAR, 64, 128>(bf16_in, bf16_out, bf16_state)
+                    : pick_dtype<VAR, 64, 64>(bf16_in, bf16_out, bf16_state);
 }
 
 int lds_floats_per_token(int var, int K, int V)
@@ -716,7 +768,8 @@ la_status validate(const la_decode_args *a, int var)
     if ((a->K != 64 && a->K != 128) || (a->V != 64 && a->V != 128))
         return LA_ERR_UNSUPPORTED;
     if ((a->qkv_dtype != LA_F32 && a->qkv_dtype != LA_BF16) ||
-        (a->out_dtype != LA_F32 && a->out_dtype != LA_BF16))
+        (a->out_dtype != LA_F32 && a->out_dtype != LA_BF16) ||
+        (a->state_dtype != LA_F32 && a->state_dtype != LA_BF16))
         return LA_ERR_DTYPE;
     if (var == VAR_LA) {
         if (a->flags != 0 || a->beta != nullptr)
@@ -767,7 +820,8 @@ la_status validate(const la_decode_args *a, int var)
             return LA_ERR_STRIDE;
     }
     // a tile is addressed with 32-bit byte offsets from its first row
-    if ((static_cast<int64_t>(a->V - 1) * a->sp.row + a->K) * 4 > INT32_MAX)
+    const int64_t es = a->state_dtype == LA_BF16 ? 2 : 4;
+    if ((static_cast<int64_t>(a->V - 1) * a->sp.row + a->K) * es > INT32_MAX)
         return LA_ERR_STRIDE;
     // outputs must not overlap each other
     {
@@ -787,10 +841,11 @@ la_status validate(const la_decode_args *a, int var)
         return LA_ERR_ALIGN;
     if (a->beta && !aligned(a->beta, 4))
         return LA_ERR_ALIGN;
-    if (!aligned(a->pool, 16) || (a->sp.slot % 4) || (a->sp.head % 4) ||
+    // a lane chunk is four state elements: 16 B (fp32) or 8 B (bf16)
+    if (!aligned(a->pool, 4 * es) || (a->sp.slot % 4) || (a->sp.head % 4) ||
         (a->sp.row % 4))
         return LA_ERR_ALIGN;
-    if (a->inter && !aligned(a->inter, 16))
+    if (a->inter && !aligned(a->inter, 4 * es))
         return LA_ERR_ALIGN;
     return LA_OK;
 }
@@ -848,9 +903,10 @@ la_status launch(const la_decode_args *a, void *stream, int var)
     p.naccept = a->num_accepted;
 
     const bool bi = a->qkv_dtype == LA_BF16, bo = a->out_dtype == LA_BF16;
-    KernelFn fn = var == VAR_LA    ? pick<VAR_LA>(a->K, a->V, bi, bo)
-                  : var == VAR_GDN ? pick<VAR_GDN>(a->K, a->V, bi, bo)
-                                   : pick<VAR_KDA>(a->K, a->V, bi, bo);
+    const bool bs = a->state_dtype == LA_BF16;
+    KernelFn fn = var == VAR_LA    ? pick<VAR_LA>(a->K, a->V, bi, bo, bs)
+                  : var == VAR_GDN ? pick<VAR_GDN>(a->K, a->V, bi, bo, bs)
+                                   : pick<VAR_KDA>(a->K, a->V, bi, bo, bs);
     const int chunk = a->T < kTokChunk ? a->T : kTokChunk;
     const size_t lds = static_cast<size_t>(chunk) *
                        lds_floats_per_token(var, a->K, a->V) * sizeof(float);
@@ -948,6 +1004,6 @@ const char *la_status_string(la_status s)
     return "unknown status";
 }
 
-int32_t la_version(void) { return 100; }
+int32_t la_version(void) { return 200; }
 
 }  // extern "C"

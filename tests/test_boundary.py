@@ -168,6 +168,11 @@ REJECT = [
     ("inter_misaligned", _mut(inter=FAKE + 0x2000008), "kda", 4),
     ("bf16_q_odd_address", _mut(q=FAKE + 1), "gdn", 4),
     ("read_idx_misaligned", _mut(read_idx=FAKE + 0x500002), "gdn", 4),
+    ("state_dtype_code", _mut(state_dtype=9), "kda", 5),
+    ("bf16_pool_misaligned", _mut(state_dtype=1, pool=FAKE + 0x1000004),
+     "gdn", 4),
+    ("bf16_inter_misaligned", _mut(state_dtype=1, inter=FAKE + 0x2000004),
+     "lightning", 4),
     # paged per-token slots: the table replaces read/write slots, needs the
     # accepted counts and an explicit row stride covering T
     ("paged_with_read_idx", _mut(token_slots=FAKE + 0x700000,

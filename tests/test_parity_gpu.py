@@ -9,6 +9,9 @@ Tolerances (max over a tensor of |gpu - oracle|):
   fp32 q/k/v: relative to max |oracle|, <= 1e-4 for outputs and states;
   bf16 q/k/v with the fp32 state: absolute <= 2e-3 (outputs), <= 1e-3
   (states and cached intermediates).
+  bf16 state pool: stored states within one bf16 step of the oracle rounded
+  to bf16, on top of the tolerance above (the kernel computes in fp32 and
+  rounds to nearest even only when it stores).
 """
 import numpy as np
 import pytest
@@ -57,7 +60,7 @@ def gpu_run(wl, *, q=None, k=None, v=None, backing=None, stream=None,
     inter = None
     if wl.inter:
         inter = torch.full((wl.B, wl.T, wl.HV, wl.V, wl.K), inter_fill,
-                           dtype=torch.float32, device=DEV)
+                           dtype=wl.backing.dtype, device=DEV)
     if wl.variant == W.LIGHTNING:
         out, _ = lad.la_decode(q, k, v, pool, d.read_idx, d.write_idx,
                                lam=d.g, inter=inter, out_dtype=wl.out_dtype,
@@ -126,6 +129,24 @@ def _err(kind, got, ref):
     return e
 
 
+def _state_err(wl, kind, tol_state, got, ref):
+    """Error of a stored state; for a bf16 pool, the excess over one bf16
+    step of the oracle rounded to nearest even (0 when within it)."""
+    if wl.backing.dtype != torch.bfloat16:
+        return _err(kind, got, ref)
+    g = torch.as_tensor(np.asarray(got, dtype=np.float64))
+    rb = torch.as_tensor(np.asarray(ref, dtype=np.float64)).to(
+        torch.bfloat16).double()
+    assert torch.isfinite(g).all(), "non-finite GPU values"
+    floor = tol_state if kind == "abs" else tol_state * float(rb.abs().max())
+    excess = (g - rb).abs() - rb.abs() * 2.0 ** -7 - floor
+    return max(float(excess.max()), 0.0)
+
+
+def _bits(t):
+    return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)
+
+
 def check_parity(wl, got, before_backing, reqs=None):
     """Compare the sampled requests with the oracle; check every untouched
     byte of the backing buffer over the whole pool."""
@@ -151,24 +172,26 @@ def check_parity(wl, got, before_backing, reqs=None):
         if ridx[b] < 0:
             assert not np.any(out[b]), "padded request must output zeros"
             if wl.inter:
-                assert torch.isnan(got["inter"][b]).all(), \
+                assert torch.isnan(got["inter"][b].float()).all(), \
                     "padded request must not touch the cache"
             continue
         if wl.inter:
-            errs["inter"] = max(errs["inter"], _err(
-                kind, got["inter"][b].numpy(), ref["inter"][i]))
+            errs["inter"] = max(errs["inter"], _state_err(
+                wl, kind, tol_state, got["inter"][b].float().numpy(),
+                ref["inter"][i]))
         if widx[b] >= 0:
-            errs["state"] = max(errs["state"], _err(
-                kind, got["backing"][m * widx[b]].numpy(),
+            errs["state"] = max(errs["state"], _state_err(
+                wl, kind, tol_state, got["backing"][m * widx[b]].float().numpy(),
                 ref["pool"][ref["mini_write"][i]]))
+    bf = wl.backing.dtype == torch.bfloat16
     assert errs["out"] <= tol_out, errs
-    assert errs["state"] <= tol_state, errs
-    assert errs["inter"] <= tol_state, errs
+    assert errs["state"] <= (0.0 if bf else tol_state), errs
+    assert errs["inter"] <= (0.0 if bf else tol_state), errs
     # bytewise: only the backing slots of non-negative write slots of active
     # requests may change
     written = {m * w for r, w in zip(ridx, widx) if r >= 0 and w >= 0}
-    a = got["backing"].view(torch.int32)
-    b0 = before_backing.view(torch.int32)
+    a = _bits(got["backing"])
+    b0 = _bits(before_backing)
     keep = torch.ones(a.shape[0], dtype=torch.bool)
     if written:
         keep[torch.tensor(sorted(written))] = False
@@ -190,6 +213,7 @@ def run_and_check(wl, reqs=None):
 # Sampled requests for the large workloads: the oracle checks these one by
 # one; the untouched-byte check still covers the whole pool.
 SAMPLE = {"gdn_small_k64": None, "lightning_b33_h64": None,
+          "gdn_gva_b64_bf16_state": range(0, 64, 3),
           "gdn_gva_b64": range(0, 64, 3), "gdn_mtp_b32_t4": range(32),
           "kda_b256_t1": range(0, 256, 9), "kda_b256_t8": range(0, 256, 17)}
 
@@ -537,12 +561,14 @@ def test_side_stream():
 # ------------------------------------------------ paged per-token state slots
 
 
-def _paged_case(variant, seed, B=4, T=3, HV=4, K=128, V=128, inter=False):
+def _paged_case(variant, seed, B=4, T=3, HV=4, K=128, V=128, inter=False,
+                state_dtype=torch.float32):
     """A workload plus a [B, T+2] slot table (wider than T: the row stride is
     explicit), accepted counts in [1, T], disjoint rows, some -1 entries."""
     pool_size = B * T + 5
     wl = W.make("paged", variant, B=B, T=T, H=2, HV=HV, K=K, V=V,
-                pool_size=pool_size, seed=seed, inter=inter)
+                pool_size=pool_size, seed=seed, inter=inter,
+                state_dtype=state_dtype)
     gen = torch.Generator().manual_seed(seed + 1)
     perm = torch.randperm(pool_size, generator=gen).to(torch.int32)
     table = torch.full((B, T + 2), 99, dtype=torch.int32)  # padding columns
@@ -567,7 +593,7 @@ def gpu_run_paged(wl, table, accepted, inter_fill=float("nan")):
     inter = None
     if wl.inter:
         inter = torch.full((wl.B, wl.T, wl.HV, wl.V, wl.K), inter_fill,
-                           dtype=torch.float32, device=DEV)
+                           dtype=wl.backing.dtype, device=DEV)
     kw = dict(inter=inter, out_dtype=wl.out_dtype, token_slots=tab,
               num_accepted=acc)
     if wl.variant == W.LIGHTNING:
@@ -587,6 +613,7 @@ def check_paged(wl, table, accepted, got):
                         inter=wl.inter, token_slots=table[:, : wl.T],
                         num_accepted=accepted)
     kind, tol_out, tol_state = _tol(wl)
+    bf = wl.backing.dtype == torch.bfloat16
     assert _err(kind, got["out"].numpy(), ref["out"]) <= tol_out
     written = set()
     for b in range(wl.B):
@@ -594,21 +621,24 @@ def check_paged(wl, table, accepted, got):
         if not 1 <= na <= wl.T or int(table[b, na - 1]) < 0:
             assert not got["out"][b].any()
             if wl.inter:
-                assert torch.isnan(got["inter"][b]).all()
+                assert torch.isnan(got["inter"][b].float()).all()
             continue
         for t in range(wl.T):
             s = int(table[b, t])
             if s >= 0:
                 written.add(s)
         if wl.inter:
-            assert _err(kind, got["inter"][b].numpy(), ref["inter"][b]) <= tol_state
+            e = _state_err(wl, kind, tol_state, got["inter"][b].float().numpy(),
+                           ref["inter"][b])
+            assert e <= (0.0 if bf else tol_state)
     for s in sorted(written):
-        assert _err(kind, got["backing"][s].numpy(), ref["pool"][s]) <= tol_state
+        e = _state_err(wl, kind, tol_state, got["backing"][s].float().numpy(),
+                       ref["pool"][s])
+        assert e <= (0.0 if bf else tol_state)
     keep = torch.ones(wl.backing.shape[0], dtype=torch.bool)
     if written:
         keep[torch.tensor(sorted(written))] = False
-    assert torch.equal(got["backing"].view(torch.int32)[keep],
-                       wl.backing.view(torch.int32)[keep])
+    assert torch.equal(_bits(got["backing"])[keep], _bits(wl.backing)[keep])
 
 
 @pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN, W.KDA])
@@ -685,3 +715,52 @@ def test_check_token_slots(tab, acc, expect):
     t = torch.tensor(tab, dtype=torch.int32, device=DEV)
     a = torch.tensor(acc, dtype=torch.int32, device=DEV)
     assert int(lad.check_token_slots(t, a, 6, 2).item()) == expect
+
+
+# --------------------------------------------------------- bf16 state pool
+
+
+@pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN, W.KDA])
+@pytest.mark.parametrize("K,V", SHAPES)
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16],
+                         ids=["f32", "bf16"])
+@pytest.mark.parametrize("T", [1, 3, 9])
+def test_bf16_state_pool(variant, K, V, dtype, T):
+    seed = (2000 + 100 * [W.LIGHTNING, W.GDN, W.KDA].index(variant)
+            + 10 * SHAPES.index((K, V)) + T
+            + (500 if dtype == torch.bfloat16 else 0))
+    wl = W.make("bf16state", variant, B=3, T=T, H=2, HV=4, K=K, V=V,
+                pool_size=7, seed=seed, act_dtype=dtype, pool_std=0.1,
+                separate_write=True, write_skip=0.34, inter=True,
+                state_dtype=torch.bfloat16)
+    run_and_check(wl)
+
+
+@pytest.mark.parametrize("mult", [1, 3])
+def test_bf16_state_pool_strided_and_padded(mult):
+    wl = W.make("bf16pad", W.GDN, B=6, T=2, H=2, HV=2, K=128, V=128,
+                pool_size=9, seed=2900 + mult, stride_mult=mult,
+                read_idx=[3, -1, 0, 8, -1, 5], write_idx=[1, 2, -1, 7, 4, -1],
+                inter=True, state_dtype=torch.bfloat16)
+    got = run_and_check(wl)
+    assert not got["out"][1].any() and not got["out"][4].any()
+
+
+def test_bf16_state_pool_paged():
+    wl, table, accepted = _paged_case(W.KDA, 2950, T=4, inter=True,
+                                      state_dtype=torch.bfloat16)
+    got = gpu_run_paged(wl, table, accepted)
+    check_paged(wl, table, accepted, got)
+
+
+def test_bf16_state_roundtrip_is_exact_when_unchanged():
+    """beta = 0 and g = 0 leave the state unchanged: widening bf16 to fp32
+    and rounding back must reproduce the stored bits exactly."""
+    wl = W.make("bf16id", W.GDN, B=3, T=2, H=1, HV=2, K=128, V=128,
+                pool_size=4, seed=2960, act_dtype=torch.float32,
+                beta_logit=False, state_dtype=torch.bfloat16)
+    wl.g = torch.zeros_like(wl.g)
+    wl.beta = torch.zeros_like(wl.beta)
+    before = wl.backing.clone()
+    got = gpu_run(wl)
+    assert torch.equal(_bits(got["backing"]), _bits(before))

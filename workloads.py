@@ -43,7 +43,8 @@ class Workload:
     g: Optional[torch.Tensor]  # lightning [HV] decay factors or None;
     #                            gdn [B,T,HV]; kda [B,T,HV,K] (log-decay)
     beta: Optional[torch.Tensor]  # [B,T,HV] (logits when beta_logit)
-    backing: torch.Tensor      # fp32 [stride_mult*pool_size, HV, V, K]
+    backing: torch.Tensor      # [stride_mult*pool_size, HV, V, K], fp32 or
+    #                            bf16 (the state dtype)
     stride_mult: int
     read_idx: torch.Tensor     # int32 [B]
     write_idx: Optional[torch.Tensor]  # int32 [B] or None (= read_idx)
@@ -76,7 +77,7 @@ class Workload:
         """Algorithmic state bytes one call must move: one read and one
         write per active (request, value head) tile, plus one cache write
         per token when intermediate states are kept."""
-        tile = self.V * self.K * 4
+        tile = self.V * self.K * self.backing.element_size()
         if self.token_slots is not None:
             reads = writes = 0
             for row, na in zip(self.token_slots.tolist(),
@@ -129,7 +130,7 @@ def make(name, variant, B, T, H, HV, K, V, pool_size, *, seed,
          l2norm=True, beta_logit=True, stride_mult=1, read_idx=None,
          write_idx=None, separate_write=False, write_skip=0.0,
          inter=False, lightning_decay=None, out_dtype=torch.float32,
-         paged=False):
+         paged=False, state_dtype=torch.float32):
     """Draw one workload.
 
     paged: draw a [B, T] per-token slot table of distinct slots and accepted
@@ -142,8 +143,9 @@ def make(name, variant, B, T, H, HV, K, V, pool_size, *, seed,
     and a ``write_skip`` fraction of them set to -1).
     """
     gen = torch.Generator().manual_seed(seed)
-    backing = torch.randn((stride_mult * pool_size, HV, V, K),
-                          generator=gen, dtype=torch.float32) * pool_std
+    backing = (torch.randn((stride_mult * pool_size, HV, V, K),
+                           generator=gen, dtype=torch.float32)
+               * pool_std).to(state_dtype)
     q = torch.randn((B, T, H, K), generator=gen).to(act_dtype)
     k = torch.randn((B, T, H, K), generator=gen).to(act_dtype)
     v = torch.randn((B, T, HV, V), generator=gen).to(act_dtype)
@@ -258,6 +260,14 @@ def gdn_paged_b64_t4(seed=6):
                 paged=True)
 
 
+def gdn_gva_b64_bf16_state(seed=3):
+    """The grouped-value GDN decode (B=64, 16 q/k heads, 32 value heads,
+    K=V=128, T=1, pool 128) with the state pool stored in bf16."""
+    return make("gdn_gva_b64_bf16_state", GDN, B=64, T=1, H=16, HV=32, K=128,
+                V=128, pool_size=128, seed=seed, g_low=-0.5, g_high=0.0,
+                state_dtype=torch.bfloat16)
+
+
 NAMED = {
     "gdn_small_k64": gdn_small_k64,
     "lightning_b33_h64": lightning_b33_h64,
@@ -266,6 +276,7 @@ NAMED = {
     "kda_b256_t1": lambda seed=5: kda_b256(1, seed),
     "kda_b256_t8": lambda seed=5: kda_b256(8, seed),
     "gdn_paged_b64_t4": gdn_paged_b64_t4,
+    "gdn_gva_b64_bf16_state": gdn_gva_b64_bf16_state,
 }
 
 
