@@ -92,6 +92,11 @@ def make_copies(wl, R, dev):
                                 dtype=wl.backing.dtype, device=dev)
         out = torch.empty((wl.B, wl.T, wl.HV, wl.V), dtype=wl.out_dtype,
                           device=dev)
+        if wl.replay_tokens is not None:
+            d.records = torch.empty((wl.B, wl.T, wl.HV, wl.record_floats),
+                                    dtype=torch.float32, device=dev)
+            d.nowrite = torch.full((wl.B,), -1, dtype=torch.int32,
+                                   device=dev)
         copies.append((d, inter, out))
     return copies
 
@@ -110,6 +115,13 @@ def make_call(wl, d, inter, out, stream):
         args = bnd.build_args(wl.variant, d.q, d.k, d.v, d.g, d.beta,
                               d.pool(), None, None, out, inter, flags,
                               d.token_slots, d.num_accepted)
+    elif d.replay_tokens is not None:
+        # verify: no writeback, one update record per token
+        args = bnd.build_args(wl.variant, d.q, d.k, d.v, d.g, d.beta,
+                              d.pool(), d.read_idx, d.nowrite, out, inter,
+                              flags, factors=d.records)
+        rargs = bnd.build_replay_args(d.records, d.pool(), d.read_idx,
+                                      d.write_idx, d.replay_tokens)
     else:
         args = bnd.build_args(wl.variant, d.q, d.k, d.v, d.g, d.beta,
                               d.pool(), d.read_idx, d.write_idx, out, inter,
@@ -120,6 +132,21 @@ def make_call(wl, d, inter, out, stream):
     ref = ctypes.byref(args)
     handle = ctypes.c_void_p(stream.cuda_stream)
     keep = (args, d, inter, out)
+
+    if d.replay_tokens is not None:
+        rref = ctypes.byref(rargs)
+        replay = bnd.lib().la_replay
+        keep = keep + (rargs,)
+
+        def step():
+            st = entry(ref, handle)
+            if st != 0:
+                raise bnd.LaDecodeError(st, "decode call")
+            st = replay(rref, handle)
+            if st != 0:
+                raise bnd.LaDecodeError(st, "replay call")
+            return keep
+        return step
 
     def call():
         st = entry(ref, handle)
@@ -274,7 +301,9 @@ def main():
                    "state_dtype": str(wl.backing.dtype).replace("torch.", ""),
                    "stride_mult": wl.stride_mult,
                    "inter_cache": wl.inter,
-                   "paged_slots": wl.token_slots is not None, "rotation": R},
+                   "paged_slots": wl.token_slots is not None,
+                   "spec_records_replay": wl.replay_tokens is not None,
+                   "rotation": R},
         "roofline": {"bound": "hbm", "achieved": achieved,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic},

@@ -163,7 +163,37 @@ typedef struct la_decode_args {
     const int32_t *token_slots;
     int64_t token_slots_stride;
     const int32_t *num_accepted;
+
+    /* Per-token update records (aiter KDA page, advisory review: "cached
+     * (a,k,err) state updates" instead of full per-token states), or NULL:
+     * [B, T, HV, 2K + V] fp32, contiguous, 16-byte aligned. Record t of
+     * (b, hv) holds a_t[K] (the decay: the KDA factors exp(g), or the GDN /
+     * Lightning scalar repeated K times), k_t[K] (the key as used, after
+     * l2norm) and err_t[V] (the rank-1 coefficient: beta (v - S k) for
+     * GDN/KDA, v for Lightning), so that S_t = S_{t-1} diag(a_t) +
+     * err_t k_t^T exactly as the kernel computed it. la_replay rebuilds S_t
+     * from the seed state; 2K + V floats per token instead of V K. Written
+     * for active requests only. */
+    float *factors;
 } la_decode_args;
+
+/* Arguments of la_replay. */
+typedef struct la_replay_args {
+    int32_t B;          /* requests, >= 0                                    */
+    int32_t T;          /* records per request in `factors`, >= 1            */
+    int32_t HV;         /* value heads, >= 1                                 */
+    int32_t K;          /* 64 or 128                                         */
+    int32_t V;          /* 64 or 128                                         */
+    int32_t pool_size;  /* >= 1                                              */
+    la_dtype state_dtype;
+    const float *factors;       /* [B, T, HV, 2K + V] fp32, contiguous      */
+    void *pool;                 /* [pool_size, HV, V, K], as in la_decode   */
+    la_pool_strides sp;
+    const int32_t *read_idx;    /* [B] seed slots; negative: skip request   */
+    const int32_t *write_idx;   /* [B] or NULL (= read_idx); negative: skip */
+    const int32_t *num_tokens;  /* [B] records to apply; a value outside
+                                   [0, T] skips the request                 */
+} la_replay_args;
 
 /* Lightning decode (cuLA page): S <- lambda_h S + v k^T, o = S q.
  * Requires beta == NULL and flags == 0. */
@@ -176,6 +206,16 @@ la_status gdn_decode_mtp(const la_decode_args *args, void *stream);
 /* KDA decode (aiter KDA page): per-key-channel decay exp(g[:]) then the
  * delta update. */
 la_status kda_decode_mtp(const la_decode_args *args, void *stream);
+
+/* Rebuild states from per-token update records (aiter KDA page: cached
+ * (a,k,err) updates, the state pool written only for the accepted tokens).
+ * For every request b and value head hv: S = pool[read_idx[b], hv]; for
+ * t < num_tokens[b]: S <- S diag(a_t) + err_t k_t^T (the records that
+ * la_decode, gdn_decode_mtp or kda_decode_mtp wrote); then
+ * pool[write_idx[b], hv] = S when the write slot is not negative. Same
+ * device preconditions on the slots as the decode calls; on fp32 pools the
+ * result equals the per-token cache of the decode call bit for bit. */
+la_status la_replay(const la_replay_args *args, void *stream);
 
 /* Debug validator of the device preconditions above (the aiter review's
  * failure modes: slots out of range, snapshots written into other

@@ -2,13 +2,14 @@
 
 Hand-written gfx950 HIP kernels behind a C ABI (include/la_decode.h), with a
 thin ctypes binding. Entry points: la_decode (Lightning), gdn_decode_mtp
-(gated delta rule), kda_decode_mtp (Kimi delta attention), and the index
-validators check_indices and check_token_slots.
+(gated delta rule), kda_decode_mtp (Kimi delta attention), replay (rebuild
+states from per-token update records), and the index validators
+check_indices and check_token_slots.
 """
-from ._binding import (DecodeArgs, LaDecodeError, check_indices,
+from ._binding import (DecodeArgs, LaDecodeError, ReplayArgs, check_indices,
                        check_token_slots, gdn_decode_mtp, kda_decode_mtp,
-                       la_decode, lib)
+                       la_decode, lib, replay)
 
-__all__ = ["DecodeArgs", "LaDecodeError", "check_indices",
+__all__ = ["DecodeArgs", "LaDecodeError", "ReplayArgs", "check_indices",
            "check_token_slots", "gdn_decode_mtp", "kda_decode_mtp",
-           "la_decode", "lib"]
+           "la_decode", "lib", "replay"]

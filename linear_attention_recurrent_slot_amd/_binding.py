@@ -58,6 +58,19 @@ class DecodeArgs(ctypes.Structure):
         ("token_slots", ctypes.c_void_p),
         ("token_slots_stride", ctypes.c_int64),
         ("num_accepted", ctypes.c_void_p),
+        ("factors", ctypes.c_void_p),
+    ]
+
+
+class ReplayArgs(ctypes.Structure):
+    """Mirror of la_replay_args."""
+    _fields_ = [
+        ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("HV", ctypes.c_int32),
+        ("K", ctypes.c_int32), ("V", ctypes.c_int32),
+        ("pool_size", ctypes.c_int32), ("state_dtype", ctypes.c_int),
+        ("factors", ctypes.c_void_p), ("pool", ctypes.c_void_p),
+        ("sp", PoolStrides), ("read_idx", ctypes.c_void_p),
+        ("write_idx", ctypes.c_void_p), ("num_tokens", ctypes.c_void_p),
     ]
 
 
@@ -85,6 +98,8 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.restype = ctypes.c_int
             fn.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]
+        L.la_replay.restype = ctypes.c_int
+        L.la_replay.argtypes = [ctypes.POINTER(ReplayArgs), ctypes.c_void_p]
         L.la_check_indices.restype = ctypes.c_int
         L.la_check_indices.argtypes = [ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_void_p, ctypes.c_void_p,
@@ -156,9 +171,19 @@ def _slot_table(t, B, T):
     return ctypes.c_void_p(t.data_ptr()), stride
 
 
+def _factors(f, shape, dev):
+    if f is None:
+        return None
+    if (f.dtype != torch.float32 or not f.is_contiguous()
+            or tuple(f.shape) != shape or f.device != dev):
+        raise ValueError("factors must be a contiguous float32 %s tensor on "
+                         "%s" % (shape, dev))
+    return ctypes.c_void_p(f.data_ptr())
+
+
 def build_args(variant: str, q, k, v, g, beta, pool, read_idx, write_idx,
                out, inter, flags: int, token_slots=None,
-               num_accepted=None) -> DecodeArgs:
+               num_accepted=None, factors=None) -> DecodeArgs:
     if q.dim() != 4 or v.dim() != 4:
         raise ValueError("q must be [B,T,H,K] and v [B,T,HV,V]")
     B, T, H, K = q.shape
@@ -246,12 +271,13 @@ def build_args(variant: str, q, k, v, g, beta, pool, read_idx, write_idx,
                              % (token_slots.device, dev))
         a.token_slots, a.token_slots_stride = _slot_table(token_slots, B, T)
     a.num_accepted = _idx(num_accepted)
+    a.factors = _factors(factors, (B, T, HV, 2 * K + V), dev)
     return a
 
 
 def _run(variant, entry, q, k, v, g, beta, pool, read_idx, write_idx, out,
          inter, flags, out_dtype, stream, token_slots=None,
-         num_accepted=None):
+         num_accepted=None, factors=None):
     B, T = q.shape[0], q.shape[1]
     HV, V, K = v.shape[2], v.shape[3], q.shape[3]
     if out is None:
@@ -262,7 +288,7 @@ def _run(variant, entry, q, k, v, g, beta, pool, read_idx, write_idx, out,
     elif inter is False:
         inter = None
     args = build_args(variant, q, k, v, g, beta, pool, read_idx, write_idx,
-                      out, inter, flags, token_slots, num_accepted)
+                      out, inter, flags, token_slots, num_accepted, factors)
     st = call(entry, args, stream)
     if st != LA_OK:
         raise LaDecodeError(st, entry)
@@ -271,42 +297,44 @@ def _run(variant, entry, q, k, v, g, beta, pool, read_idx, write_idx, out,
 
 # Every decode entry point takes either read_idx (+ optional write_idx) or,
 # for paged speculative decoding, token_slots ([B, >=T] int32 table) and
-# num_accepted ([B] int32) with read_idx=None.
+# num_accepted ([B] int32) with read_idx=None. `factors` is an optional
+# caller-allocated float32 [B, T, HV, 2K + V] tensor that receives the
+# per-token update records (see replay()).
 
 def la_decode(q, k, v, pool, read_idx=None, write_idx=None, *, lam=None,
               out=None, inter=None, out_dtype=torch.float32, stream=None,
-              token_slots=None, num_accepted=None):
+              token_slots=None, num_accepted=None, factors=None):
     """Lightning decode. lam: optional float32 [HV] decay factors (default:
     exp(-2^(-8(h+1)/HV)) per value head). Returns (out, inter)."""
     return _run("lightning", "la_decode", q, k, v, lam, None, pool, read_idx,
                 write_idx, out, inter, 0, out_dtype, stream, token_slots,
-                num_accepted)
+                num_accepted, factors)
 
 
 def gdn_decode_mtp(q, k, v, g, beta, pool, read_idx=None, write_idx=None, *,
                    out=None, inter=None, l2norm_qk=False, beta_logit=False,
                    out_dtype=torch.float32, stream=None, token_slots=None,
-                   num_accepted=None):
+                   num_accepted=None, factors=None):
     """Gated delta rule decode over T tokens. g: [B,T,HV] log-decay;
     beta: [B,T,HV] (logits if beta_logit). Returns (out, inter)."""
     flags = (LA_F_L2NORM_QK if l2norm_qk else 0) | \
         (LA_F_BETA_LOGIT if beta_logit else 0)
     return _run("gdn", "gdn_decode_mtp", q, k, v, g, beta, pool, read_idx,
                 write_idx, out, inter, flags, out_dtype, stream, token_slots,
-                num_accepted)
+                num_accepted, factors)
 
 
 def kda_decode_mtp(q, k, v, g, beta, pool, read_idx=None, write_idx=None, *,
                    out=None, inter=None, l2norm_qk=False, beta_logit=False,
                    out_dtype=torch.float32, stream=None, token_slots=None,
-                   num_accepted=None):
+                   num_accepted=None, factors=None):
     """KDA decode over T tokens. g: [B,T,HV,K] per-key-channel log-decay.
     Returns (out, inter)."""
     flags = (LA_F_L2NORM_QK if l2norm_qk else 0) | \
         (LA_F_BETA_LOGIT if beta_logit else 0)
     return _run("kda", "kda_decode_mtp", q, k, v, g, beta, pool, read_idx,
                 write_idx, out, inter, flags, out_dtype, stream, token_slots,
-                num_accepted)
+                num_accepted, factors)
 
 
 def check_indices(read_idx, write_idx, pool_size, result=None, stream=None):
@@ -342,3 +370,46 @@ def check_token_slots(token_slots, num_accepted, pool_size, T, result=None,
     if st != LA_OK:
         raise LaDecodeError(st, "la_check_token_slots")
     return result
+
+
+def build_replay_args(factors, pool, read_idx, write_idx,
+                      num_tokens) -> ReplayArgs:
+    if factors.dim() != 4:
+        raise ValueError("factors must be [B, T, HV, 2K + V]")
+    B, T, HV, R = factors.shape
+    if (pool.dim() != 4 or pool.dtype not in (torch.float32, torch.bfloat16)
+            or pool.stride(3) != 1):
+        raise ValueError("pool must be a float32 or bfloat16 "
+                         "[pool_size, HV, V, K] tensor with unit innermost "
+                         "stride")
+    V, K = pool.shape[2], pool.shape[3]
+    if pool.shape[1] != HV or R != 2 * K + V:
+        raise ValueError("factors %s do not match pool %s"
+                         % (tuple(factors.shape), tuple(pool.shape)))
+    dev = pool.device
+    for name, t in (("read_idx", read_idx), ("write_idx", write_idx),
+                    ("num_tokens", num_tokens)):
+        if t is not None and (tuple(t.shape) != (B,) or t.device != dev):
+            raise ValueError("%s must be [%d] on %s" % (name, B, dev))
+    a = ReplayArgs()
+    a.B, a.T, a.HV, a.K, a.V = B, T, HV, K, V
+    a.pool_size = pool.shape[0]
+    a.state_dtype = _dtype_code(pool, "pool")
+    a.factors = _factors(factors, (B, T, HV, R), dev)
+    a.pool = ctypes.c_void_p(pool.data_ptr())
+    a.sp = PoolStrides(*pool.stride()[:3])
+    a.read_idx = _idx(read_idx)
+    a.write_idx = _idx(write_idx)
+    a.num_tokens = _idx(num_tokens)
+    return a
+
+
+def replay(factors, pool, read_idx, write_idx, num_tokens, stream=None):
+    """Rebuild states from per-token update records (written by a decode call
+    with factors=...): request b starts from pool[read_idx[b]], applies its
+    first num_tokens[b] records and stores the result in write_idx[b]
+    (None: the read slot; negative: skip)."""
+    args = build_replay_args(factors, pool, read_idx, write_idx, num_tokens)
+    st = lib().la_replay(ctypes.byref(args), _stream_handle(stream))
+    if st != LA_OK:
+        raise LaDecodeError(st, "la_replay")

@@ -82,6 +82,7 @@ struct Params {
     const int32_t *tslots;  // paged per-token slot table, or null
     int64_t ts_stride;
     const int32_t *naccept;
+    float *factors;  // [B, T, HV, 2K + V] per-token records, or null
 };
 
 // ---------------------------------------------------------------- helpers
@@ -295,12 +296,13 @@ __device__ __forceinline__ void prologue_load(const Params &p, int b, int hv,
     }
 }
 
-// Second half: l2norm, k.q, sigmoid, exp; writes the LDS record `rec`.
+// Second half: l2norm, k.q, sigmoid, exp; writes the LDS record `rec` and,
+// when `frec` is set, the decay and key of the token's update record.
 template <int VAR, int K, int V>
 __device__ __forceinline__ void prologue_finish(const Params &p, int hv,
                                                 int lane,
                                                 const TokRaw<K, V> &raw,
-                                                float *rec)
+                                                float *rec, float *frec)
 {
     using L = TokLayout<VAR, K, V>;
     constexpr int EPL = K / 64;
@@ -320,34 +322,53 @@ __device__ __forceinline__ void prologue_finish(const Params &p, int hv,
         rq = __frsqrt_rn(ssq + kL2Eps);
         rk = __frsqrt_rn(ssk + kL2Eps);
     }
+    // the scalar decay (GDN, Lightning), identical in every lane
+    float decay;
+    if constexpr (VAR == VAR_LA)
+        decay = p.g ? raw.g
+                    : __expf(-exp2f(-8.f * static_cast<float>(hv + 1) /
+                                    static_cast<float>(p.HV)));
+    else
+        decay = (VAR == VAR_GDN) ? __expf(raw.g) : 1.f;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int j = lane * EPL + i;
-        rec[L::kOff + j] = raw.k[i] * rk;
+        const float kn = raw.k[i] * rk;
+        rec[L::kOff + j] = kn;
         rec[L::qOff + j] = raw.q[i] * rq;
-        if constexpr (VAR == VAR_KDA)
-            rec[L::eOff + j] = __expf(raw.e[i]);
+        float a = decay;
+        if constexpr (VAR == VAR_KDA) {
+            a = __expf(raw.e[i]);
+            rec[L::eOff + j] = a;
+        }
+        if (frec) {
+            frec[j] = a;
+            frec[K + j] = kn;
+        }
     }
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
         rec[L::vOff + v_slot(lane * VPL + i)] = raw.v[i];
     if (lane == 0) {
-        float beta = 1.f, decay;
-        if constexpr (VAR == VAR_LA) {
-            decay = p.g ? raw.g
-                        : __expf(-exp2f(-8.f * static_cast<float>(hv + 1) /
-                                        static_cast<float>(p.HV)));
-        } else {
+        float beta = 1.f;
+        if constexpr (VAR != VAR_LA)
             beta = (p.flags & LA_F_BETA_LOGIT)
                        ? 1.f / (1.f + __expf(-raw.beta))
                        : raw.beta;
-            decay = (VAR == VAR_GDN) ? __expf(raw.g) : 1.f;
-        }
         rec[L::sOff + 0] = beta;
         rec[L::sOff + 1] = decay;
         rec[L::sOff + 2] = qk * rq * rk;
         rec[L::sOff + 3] = 0.f;
     }
+}
+
+// Start of the update record of token t of (request b, value head hv).
+template <int K, int V>
+__device__ __forceinline__ float *factor_record(const Params &p, int b, int t,
+                                                int hv)
+{
+    return p.factors + ((static_cast<int64_t>(b) * p.T + t) * p.HV + hv) *
+                           static_cast<int64_t>(2 * K + V);
 }
 
 #if LA_WAVES_PER_EU > 0
@@ -356,7 +377,10 @@ __device__ __forceinline__ void prologue_finish(const Params &p, int hv,
 #define LA_OCCUPANCY
 #endif
 
-template <int VAR, int K, int V, bool BF16IN, bool BF16OUT, bool BF16S>
+// REC: also write the per-token update records (a separate instantiation so
+// that the ordinary path carries none of their register cost).
+template <int VAR, int K, int V, bool BF16IN, bool BF16OUT, bool BF16S,
+          bool REC>
 __global__ void __launch_bounds__((V / kRowsPerWave) * 64) LA_OCCUPANCY
 decode_kernel(const Params p)
 {
@@ -447,7 +471,9 @@ decode_kernel(const Params p)
         for (int tt = wave; tt < nt; tt += NW) {
             TokRaw<K, V> rw;
             prologue_load<VAR, K, V, BF16IN>(p, b, hv, t0 + tt, lane, rw);
-            prologue_finish<VAR, K, V>(p, hv, lane, rw, lds + tt * L::size);
+            prologue_finish<VAR, K, V>(
+                p, hv, lane, rw, lds + tt * L::size,
+                REC ? factor_record<K, V>(p, b, t0 + tt, hv) : nullptr);
         }
         lds_barrier();
 
@@ -539,6 +565,15 @@ decode_kernel(const Params p)
                 mine = (c8 == i) ? o[i] : mine;
             if (olane)
                 store_out<BF16OUT>(p.out, obase + t * p.so_t, mine);
+            if constexpr (REC) {
+                // lane (c8 = i, rs) stores err of its row R w + 8 i + rs
+                float *ferr = factor_record<K, V>(p, b, t, hv) + 2 * K +
+                              wave * kRowsPerWave + rs;
+#pragma unroll
+                for (int i = 0; i < RPL; ++i)
+                    if (c8 == i)
+                        ferr[i * 8] = c[i];
+            }
 
             if (p.tslots) {
                 const int ws = __builtin_amdgcn_readfirstlane(
@@ -580,6 +615,114 @@ decode_kernel(const Params p)
     }
 
     if (w >= 0) {  // in-place writeback to the write slot
+        const BufRsrc dst = make_rsrc(
+            pool + (w * p.sp_slot + hv * p.sp_head) * ES, tile_bytes);
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            const uint32_t row0 = (wave * kRowsPerWave + i * 8) * row_bytes;
+#pragma unroll
+            for (int m = 0; m < CPL; ++m)
+                IO::store(dst, lane_off + m * kChunkStep, row0, S[i][m]);
+        }
+    }
+}
+
+struct ReplayParams {
+    int32_t B, T, HV;
+    int32_t pad_;
+    const float *factors;
+    void *pool;
+    int64_t sp_slot, sp_head, sp_row;
+    const int32_t *ridx;
+    const int32_t *widx;
+    const int32_t *ntok;
+};
+
+// Rebuild the state of (request, value head) from its update records:
+// S <- S diag(a_t) + err_t k_t^T for t < ntok. Same tile mapping as the
+// decode kernel; the records of up to 8 tokens are staged in LDS.
+template <int K, int V, bool BF16S>
+__global__ void __launch_bounds__((V / kRowsPerWave) * 64)
+replay_kernel(const ReplayParams p)
+{
+    using IO = StateIO<BF16S>;
+    constexpr uint32_t ES = IO::ES;
+    constexpr uint32_t kChunk = 4 * ES;
+    constexpr uint32_t kChunkStep = 32 * ES;
+    constexpr int NW = V / kRowsPerWave;
+    constexpr int RPL = kRowsPerWave / 8;
+    constexpr int CPL = K / 32;
+    constexpr int RS = 2 * K + V;  // floats per record
+    __shared__ f4 recs[kTokChunk * RS / 4];
+    const float *lrec = reinterpret_cast<const float *>(recs);
+
+    const int pair = blockIdx.x;
+    const int b = pair / p.HV;
+    const int hv = pair - b * p.HV;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c8 = lane & 7;
+    const int rs = lane >> 3;
+    const int r = __builtin_amdgcn_readfirstlane(p.ridx[b]);
+    const int w = __builtin_amdgcn_readfirstlane(p.widx ? p.widx[b] : r);
+    const int n = __builtin_amdgcn_readfirstlane(p.ntok[b]);
+    if (r < 0 || n < 0 || n > p.T)
+        return;
+
+    const uint32_t row_bytes = static_cast<uint32_t>(p.sp_row) * ES;
+    const uint32_t tile_bytes = static_cast<uint32_t>(
+        (static_cast<int64_t>(V - 1) * p.sp_row + K) * ES);
+    const uint32_t lane_off = rs * row_bytes + c8 * kChunk;
+    char *const pool = static_cast<char *>(p.pool);
+    const BufRsrc src = make_rsrc(
+        pool + (r * p.sp_slot + hv * p.sp_head) * ES, tile_bytes);
+    f4 S[RPL][CPL];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+        const uint32_t row0 = (wave * kRowsPerWave + i * 8) * row_bytes;
+#pragma unroll
+        for (int m = 0; m < CPL; ++m)
+            S[i][m] = IO::template load<kStreamPolicy>(
+                src, lane_off + m * kChunkStep, row0);
+    }
+
+    const f4 *grec = reinterpret_cast<const f4 *>(
+        p.factors + (static_cast<int64_t>(b) * p.T * p.HV + hv) * RS);
+    const int64_t tstride4 = static_cast<int64_t>(p.HV) * RS / 4;
+    for (int t0 = 0; t0 < n; t0 += kTokChunk) {
+        const int nt = min(kTokChunk, n - t0);
+        if (t0 > 0)
+            lds_barrier();
+        for (int i = threadIdx.x; i < nt * (RS / 4); i += NW * 64) {
+            const int tt = i / (RS / 4), e = i - tt * (RS / 4);
+            recs[i] = grec[(t0 + tt) * tstride4 + e];
+        }
+        lds_barrier();
+        for (int tt = 0; tt < nt; ++tt) {
+            const float *rec = lrec + tt * RS;
+            float err[RPL];
+#pragma unroll
+            for (int i = 0; i < RPL; ++i)
+                err[i] = rec[2 * K + wave * kRowsPerWave + i * 8 + rs];
+#pragma unroll
+            for (int m = 0; m < CPL; ++m) {
+                const f4 a = *reinterpret_cast<const f4 *>(
+                    rec + 4 * (c8 + 8 * m));
+                const f4 kk = *reinterpret_cast<const f4 *>(
+                    rec + K + 4 * (c8 + 8 * m));
+#pragma unroll
+                for (int i = 0; i < RPL; ++i) {
+                    S[i][m] *= a;
+                    S[i][m].x = fmaf(err[i], kk.x, S[i][m].x);
+                    S[i][m].y = fmaf(err[i], kk.y, S[i][m].y);
+                    S[i][m].z = fmaf(err[i], kk.z, S[i][m].z);
+                    S[i][m].w = fmaf(err[i], kk.w, S[i][m].w);
+                }
+            }
+        }
+    }
+
+    if (w >= 0) {
         const BufRsrc dst = make_rsrc(
             pool + (w * p.sp_slot + hv * p.sp_head) * ES, tile_bytes);
 #pragma unroll
@@ -687,32 +830,34 @@ check_token_slots_kernel(int32_t B, int32_t T, int32_t pool_size,
 
 typedef void (*KernelFn)(const Params);
 
-template <int VAR, int K, int V, bool BF16S>
+template <int VAR, int K, int V, bool BF16S, bool REC>
 KernelFn pick_io(bool bf16_in, bool bf16_out)
 {
     if (bf16_in)
-        return bf16_out ? decode_kernel<VAR, K, V, true, true, BF16S>
-                        : decode_kernel<VAR, K, V, true, false, BF16S>;
-    return bf16_out ? decode_kernel<VAR, K, V, false, true, BF16S>
-                    : decode_kernel<VAR, K, V, false, false, BF16S>;
+        return bf16_out ? decode_kernel<VAR, K, V, true, true, BF16S, REC>
+                        : decode_kernel<VAR, K, V, true, false, BF16S, REC>;
+    return bf16_out ? decode_kernel<VAR, K, V, false, true, BF16S, REC>
+                    : decode_kernel<VAR, K, V, false, false, BF16S, REC>;
 }
 
 template <int VAR, int K, int V>
-KernelFn pick_dtype(bool bf16_in, bool bf16_out, bool bf16_state)
+KernelFn pick_dtype(bool bf16_in, bool bf16_out, bool bf16_state, bool rec)
 {
-    return bf16_state ? pick_io<VAR, K, V, true>(bf16_in, bf16_out)
-                      : pick_io<VAR, K, V, false>(bf16_in, bf16_out);
+    if (rec)
+        return bf16_state ? pick_io<VAR, K, V, true, true>(bf16_in, bf16_out)
+                          : pick_io<VAR, K, V, false, true>(bf16_in, bf16_out);
+    return bf16_state ? pick_io<VAR, K, V, true, false>(bf16_in, bf16_out)
+                      : pick_io<VAR, K, V, false, false>(bf16_in, bf16_out);
 }
 
 template <int VAR>
-KernelFn pick(int K, int V, bool bf16_in, bool bf16_out, bool bf16_state)
+KernelFn pick(int K, int V, bool bi, bool bo, bool bs, bool rec)
 {
     if (K == 128)
-        return V == 128
-                   ? pick_dtype<VAR, 128, 128>(bf16_in, bf16_out, bf16_state)
-                   : pick_dtype<VAR, 128, 64>(bf16_in, bf16_out, bf16_state);
-    return V == 128 ? pick_dtype<VAR, 64, 128>(bf16_in, bf16_out, bf16_state)
-                    : pick_dtype<VAR, 64, 64>(bf16_in, bf16_out, bf16_state);
+        return V == 128 ? pick_dtype<VAR, 128, 128>(bi, bo, bs, rec)
+                        : pick_dtype<VAR, 128, 64>(bi, bo, bs, rec);
+    return V == 128 ? pick_dtype<VAR, 64, 128>(bi, bo, bs, rec)
+                    : pick_dtype<VAR, 64, 64>(bi, bo, bs, rec);
 }
 
 int lds_floats_per_token(int var, int K, int V)
@@ -847,6 +992,8 @@ la_status validate(const la_decode_args *a, int var)
         return LA_ERR_ALIGN;
     if (a->inter && !aligned(a->inter, 4 * es))
         return LA_ERR_ALIGN;
+    if (a->factors && !aligned(a->factors, 16))
+        return LA_ERR_ALIGN;
     return LA_OK;
 }
 
@@ -901,12 +1048,15 @@ la_status launch(const la_decode_args *a, void *stream, int var)
     p.tslots = a->token_slots;
     p.ts_stride = a->token_slots_stride;
     p.naccept = a->num_accepted;
+    p.factors = a->factors;
 
     const bool bi = a->qkv_dtype == LA_BF16, bo = a->out_dtype == LA_BF16;
     const bool bs = a->state_dtype == LA_BF16;
-    KernelFn fn = var == VAR_LA    ? pick<VAR_LA>(a->K, a->V, bi, bo, bs)
-                  : var == VAR_GDN ? pick<VAR_GDN>(a->K, a->V, bi, bo, bs)
-                                   : pick<VAR_KDA>(a->K, a->V, bi, bo, bs);
+    const bool rec = a->factors != nullptr;
+    KernelFn fn = var == VAR_LA ? pick<VAR_LA>(a->K, a->V, bi, bo, bs, rec)
+                  : var == VAR_GDN
+                      ? pick<VAR_GDN>(a->K, a->V, bi, bo, bs, rec)
+                      : pick<VAR_KDA>(a->K, a->V, bi, bo, bs, rec);
     const int chunk = a->T < kTokChunk ? a->T : kTokChunk;
     const size_t lds = static_cast<size_t>(chunk) *
                        lds_floats_per_token(var, a->K, a->V) * sizeof(float);
@@ -936,6 +1086,75 @@ la_status gdn_decode_mtp(const la_decode_args *args, void *stream)
 la_status kda_decode_mtp(const la_decode_args *args, void *stream)
 {
     return launch(args, stream, VAR_KDA);
+}
+
+la_status la_replay(const la_replay_args *a, void *stream)
+{
+    if (!a)
+        return LA_ERR_NULL;
+    if (a->B < 0 || a->T < 1 || a->HV < 1 || a->pool_size < 1)
+        return LA_ERR_SHAPE;
+    if ((a->K != 64 && a->K != 128) || (a->V != 64 && a->V != 128))
+        return LA_ERR_UNSUPPORTED;
+    if (a->state_dtype != LA_F32 && a->state_dtype != LA_BF16)
+        return LA_ERR_DTYPE;
+    if (static_cast<int64_t>(a->B) * a->HV > INT32_MAX)
+        return LA_ERR_SHAPE;
+    if (a->B == 0)
+        return LA_OK;
+    if (!a->factors || !a->pool || !a->read_idx || !a->num_tokens)
+        return LA_ERR_NULL;
+    if (a->sp.slot < 0 || a->sp.head < 0 || a->sp.row < 0)
+        return LA_ERR_STRIDE;
+    {
+        const int64_t st[3] = {a->sp.row, a->sp.head, a->sp.slot};
+        const int64_t ex[3] = {a->V, a->HV, a->pool_size};
+        if (!no_overlap(3, st, ex, a->K))
+            return LA_ERR_STRIDE;
+    }
+    const int64_t es = a->state_dtype == LA_BF16 ? 2 : 4;
+    if ((static_cast<int64_t>(a->V - 1) * a->sp.row + a->K) * es > INT32_MAX)
+        return LA_ERR_STRIDE;
+    if (!aligned(a->pool, 4 * es) || (a->sp.slot % 4) || (a->sp.head % 4) ||
+        (a->sp.row % 4))
+        return LA_ERR_ALIGN;
+    if (!aligned(a->factors, 16) || !aligned(a->read_idx, 4) ||
+        !aligned(a->write_idx, 4) || !aligned(a->num_tokens, 4))
+        return LA_ERR_ALIGN;
+
+    ReplayParams p;
+    p.B = a->B;
+    p.T = a->T;
+    p.HV = a->HV;
+    p.pad_ = 0;
+    p.factors = a->factors;
+    p.pool = a->pool;
+    p.sp_slot = a->sp.slot;
+    p.sp_head = a->sp.head;
+    p.sp_row = a->sp.row;
+    p.ridx = a->read_idx;
+    p.widx = a->write_idx;
+    p.ntok = a->num_tokens;
+    const bool bs = a->state_dtype == LA_BF16;
+    typedef void (*ReplayFn)(const ReplayParams);
+    ReplayFn fn;
+    if (a->K == 128)
+        fn = a->V == 128 ? (bs ? replay_kernel<128, 128, true>
+                               : replay_kernel<128, 128, false>)
+                         : (bs ? replay_kernel<128, 64, true>
+                               : replay_kernel<128, 64, false>);
+    else
+        fn = a->V == 128 ? (bs ? replay_kernel<64, 128, true>
+                               : replay_kernel<64, 128, false>)
+                         : (bs ? replay_kernel<64, 64, true>
+                               : replay_kernel<64, 64, false>);
+    void *kargs[] = {&p};
+    const hipError_t e = hipLaunchKernel(
+        reinterpret_cast<const void *>(fn),
+        dim3(static_cast<unsigned>(a->B) * a->HV),
+        dim3((a->V / kRowsPerWave) * 64), kargs, 0,
+        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
 }
 
 la_status la_check_indices(int32_t B, int32_t pool_size,

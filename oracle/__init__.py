@@ -17,7 +17,7 @@ import subprocess
 import numpy as np
 
 __all__ = ["LIGHTNING", "GDN", "KDA", "L2NORM_QK", "BETA_LOGIT", "build",
-           "decode", "lib_path"]
+           "decode", "replay", "lib_path"]
 
 LIGHTNING, GDN, KDA = 0, 1, 2
 L2NORM_QK, BETA_LOGIT = 1, 2
@@ -58,7 +58,11 @@ def _load():
         lib.oracle_decode.restype = ctypes.c_int
         lib.oracle_decode.argtypes = (
             [ctypes.c_int] * 8 + [dp] * 5 + [ctypes.c_int, dp, dp, ip, ip,
-                                             dp, dp, ip, ctypes.c_int, ip])
+                                             dp, dp, ip, ctypes.c_int, ip,
+                                             dp])
+        lib.oracle_replay.restype = ctypes.c_int
+        lib.oracle_replay.argtypes = (
+            [ctypes.c_int] * 5 + [dp, ctypes.c_int, dp, dp, ip, ip, ip])
         _lib = lib
     return _lib
 
@@ -87,7 +91,8 @@ def _ptr(a, ctype):
 
 
 def decode(variant, q, k, v, g, beta, pool, read_idx, write_idx=None,
-           flags=0, inter=False, token_slots=None, num_accepted=None):
+           flags=0, inter=False, token_slots=None, num_accepted=None,
+           factors=False):
     """Run the fp64 recurrence.
 
     q, k: [B,T,H,K]; v: [B,T,HV,V]; g: Lightning [HV] decay factors or None,
@@ -95,6 +100,7 @@ def decode(variant, q, k, v, g, beta, pool, read_idx, write_idx=None,
     (Lightning); pool: logical [pool_size,HV,V,K]; read_idx/write_idx: [B].
     token_slots: optional [B, >=T] per-token slot table (then read_idx and
     write_idx are ignored and num_accepted [B] is required).
+    factors: also return the per-token records [B,T,HV,2K+V] (a | k | err).
 
     Returns a dict with ``out`` [B,T,HV,V], ``pool`` (the pool after the
     call, float64) and ``inter`` ([B,T,HV,V,K] or None).
@@ -135,6 +141,8 @@ def decode(variant, q, k, v, g, beta, pool, read_idx, write_idx=None,
     # NaN until the oracle writes it: a position it skips cannot pass as 0
     out = np.full((B, T, HV, V), np.nan, dtype=np.float64)
     inter_a = np.zeros((B, T, HV, V, K), dtype=np.float64) if inter else None
+    fac = (np.full((B, T, HV, 2 * K + V), np.nan, dtype=np.float64)
+           if factors else None)
     dp = ctypes.c_double
     rc = _load().oracle_decode(
         variant, B, T, H, HV, K, V, flags, _ptr(q, dp), _ptr(k, dp),
@@ -142,7 +150,35 @@ def decode(variant, q, k, v, g, beta, pool, read_idx, write_idx=None,
         _ptr(beta if variant != LIGHTNING else None, dp), pool_size,
         _ptr(pool_in, dp), _ptr(pool_out, dp), _ptr(ridx, ctypes.c_int32),
         _ptr(widx, ctypes.c_int32), _ptr(out, dp), _ptr(inter_a, dp),
-        _ptr(slots, ctypes.c_int32), stride, _ptr(acc, ctypes.c_int32))
+        _ptr(slots, ctypes.c_int32), stride, _ptr(acc, ctypes.c_int32),
+        _ptr(fac, dp))
     if rc != 0:
         raise ValueError("oracle_decode rejected its arguments (rc=%d)" % rc)
-    return {"out": out, "pool": pool_out, "inter": inter_a}
+    return {"out": out, "pool": pool_out, "inter": inter_a, "factors": fac}
+
+
+def replay(factors, pool, read_idx, write_idx, num_tokens):
+    """Rebuild states from factor records [B,T,HV,2K+V]: request b starts
+    from pool[read_idx[b]] and applies its first num_tokens[b] records;
+    the result goes to write_idx[b] (None: the read slot). Returns the pool
+    after the call (float64)."""
+    fac = _f64(factors)
+    pool_in = _f64(pool)
+    ridx, widx, ntok = _i32(read_idx), _i32(write_idx), _i32(num_tokens)
+    B, T, HV, R = fac.shape
+    V, K = pool_in.shape[2], pool_in.shape[3]
+    if R != 2 * K + V or pool_in.shape[1] != HV:
+        raise ValueError("factor records do not match the pool")
+    if ridx.shape != (B,) or ntok.shape != (B,) or (
+            widx is not None and widx.shape != (B,)):
+        raise ValueError("index shape")
+    pool_out = pool_in.copy()
+    dp = ctypes.c_double
+    rc = _load().oracle_replay(B, T, HV, K, V, _ptr(fac, dp),
+                               pool_in.shape[0], _ptr(pool_in, dp),
+                               _ptr(pool_out, dp), _ptr(ridx, ctypes.c_int32),
+                               _ptr(widx, ctypes.c_int32),
+                               _ptr(ntok, ctypes.c_int32))
+    if rc != 0:
+        raise ValueError("oracle_replay rejected its arguments (rc=%d)" % rc)
+    return pool_out

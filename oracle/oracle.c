@@ -56,6 +56,15 @@
  * and, after each token t, writes the state to slot table[b][t] when that
  * entry is not negative. A request whose accepted count is outside [1, T]
  * or whose seed entry is negative is padding, as above.
+ *
+ * Factor records (aiter KDA page, advisory review: "cached (a,k,err) state
+ * updates"; its benchmark note: not writing every per-token state saves
+ * runtime as tokens and batch grow): instead of the state after token t, a
+ * record [a | k | err] of 2K + V values lets the state be rebuilt as
+ * S_t = S_{t-1} diag(a_t) + err_t k_t^T. Here a_t is the token's decay (the
+ * KDA factors, or the GDN/Lightning scalar repeated K times), k_t the key as
+ * used (after l2norm) and err_t the rank-1 coefficient: beta (v - S k) for
+ * the delta rules, v for Lightning. oracle_replay applies n such records.
  */
 #include <math.h>
 #include <stddef.h>
@@ -106,6 +115,7 @@ static double lightning_decay(int head, int num_heads)
  *   inter     [B][T][HV][V][K] or NULL
  *   slots     [B][slots_stride] per-token slot table, or NULL; when given,
  *             read_idx and write_idx are ignored and accepted[B] is used
+ *   factors   [B][T][HV][2K + V] per-token records, or NULL
  */
 int oracle_decode(int variant, int B, int T, int H, int HV, int K, int V,
                   int flags, const double *q, const double *k, const double *v,
@@ -113,7 +123,7 @@ int oracle_decode(int variant, int B, int T, int H, int HV, int K, int V,
                   const double *pool_in, double *pool_out,
                   const int32_t *read_idx, const int32_t *write_idx,
                   double *out, double *inter, const int32_t *slots,
-                  int slots_stride, const int32_t *accepted)
+                  int slots_stride, const int32_t *accepted, double *factors)
 {
     if (B < 0 || T < 1 || H < 1 || HV < 1 || K < 1 || V < 1 || HV % H != 0)
         return -1;
@@ -183,8 +193,18 @@ int oracle_decode(int variant, int B, int T, int H, int HV, int K, int V,
                 }
                 const double *vv = v + v_off;
 
+                double *rec =
+                    factors ? factors + bt * (size_t)(2 * K + V) : NULL;
+                if (rec)
+                    memcpy(rec + K, kv, (size_t)K * sizeof(double));
                 if (variant == ORACLE_LIGHTNING) {
                     const double lam = g ? g[hv] : lightning_decay(hv, HV);
+                    if (rec) {
+                        for (int j = 0; j < K; ++j)
+                            rec[j] = lam;
+                        for (int i = 0; i < V; ++i)
+                            rec[2 * K + i] = vv[i];
+                    }
                     /* S <- lambda * S + v k^T */
                     for (int i = 0; i < V; ++i)
                         for (int j = 0; j < K; ++j)
@@ -199,11 +219,17 @@ int oracle_decode(int variant, int B, int T, int H, int HV, int K, int V,
                         const double alpha = exp(g[bt]);
                         for (size_t e = 0; e < tile; ++e)
                             S[e] *= alpha;
+                        if (rec)
+                            for (int j = 0; j < K; ++j)
+                                rec[j] = alpha;
                     } else {
                         const double *gk = g + bt * (size_t)K;
                         for (int i = 0; i < V; ++i)
                             for (int j = 0; j < K; ++j)
                                 S[(size_t)i * K + j] *= exp(gk[j]);
+                        if (rec)
+                            for (int j = 0; j < K; ++j)
+                                rec[j] = exp(gk[j]);
                     }
                     /* delta rule: S <- S + beta (v - S k) k^T, one row at a
                      * time (row i's read-out uses only row i) */
@@ -214,6 +240,8 @@ int oracle_decode(int variant, int B, int T, int H, int HV, int K, int V,
                         const double c = bb * (vv[i] - u);
                         for (int j = 0; j < K; ++j)
                             S[(size_t)i * K + j] += c * kv[j];
+                        if (rec)
+                            rec[2 * K + i] = c;
                     }
                 }
                 /* o = S q with the updated state */
@@ -240,5 +268,57 @@ int oracle_decode(int variant, int B, int T, int H, int HV, int K, int V,
     free(S);
     free(qv);
     free(kv);
+    return 0;
+}
+
+/*
+ * Rebuild states from factor records: for each request b with
+ * 0 <= ntok[b] <= T and read slot r = read_idx[b] >= 0, start from
+ * pool_in[r, hv] and apply records t = 0 .. ntok[b] - 1 of that request,
+ * S <- S diag(a_t) + err_t k_t^T; then write S to pool_out[w, hv] with
+ * w = write_idx ? write_idx[b] : r when w >= 0. Requests with a negative
+ * read slot or ntok outside [0, T] are skipped.
+ * factors: [B][T][HV][2K + V]. Returns 0, or -1 on a bad argument.
+ */
+int oracle_replay(int B, int T, int HV, int K, int V, const double *factors,
+                  int pool_size, const double *pool_in, double *pool_out,
+                  const int32_t *read_idx, const int32_t *write_idx,
+                  const int32_t *ntok)
+{
+    if (B < 0 || T < 1 || HV < 1 || K < 1 || V < 1)
+        return -1;
+    const size_t tile = (size_t)V * (size_t)K;
+    const size_t rsz = (size_t)(2 * K + V);
+    double *S = (double *)malloc(tile * sizeof(double));
+    if (!S)
+        return -2;
+    for (int b = 0; b < B; ++b) {
+        const int r = read_idx[b];
+        const int w = write_idx ? write_idx[b] : r;
+        const int n = ntok[b];
+        if (r >= pool_size || w >= pool_size) {
+            free(S);
+            return -1;
+        }
+        if (r < 0 || n < 0 || n > T)
+            continue;
+        for (int hv = 0; hv < HV; ++hv) {
+            memcpy(S, pool_in + ((size_t)r * HV + hv) * tile,
+                   tile * sizeof(double));
+            for (int t = 0; t < n; ++t) {
+                const double *rec =
+                    factors + (((size_t)b * T + t) * HV + hv) * rsz;
+                const double *a = rec, *kk = rec + K, *err = rec + 2 * K;
+                for (int i = 0; i < V; ++i)
+                    for (int j = 0; j < K; ++j)
+                        S[(size_t)i * K + j] =
+                            S[(size_t)i * K + j] * a[j] + err[i] * kk[j];
+            }
+            if (w >= 0)
+                memcpy(pool_out + ((size_t)w * HV + hv) * tile, S,
+                       tile * sizeof(double));
+        }
+    }
+    free(S);
     return 0;
 }

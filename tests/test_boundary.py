@@ -36,8 +36,9 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ("la_decode", "gdn_decode_mtp", "kda_decode_mtp",
-              "la_check_indices", "la_status_string", "la_version"):
+    for n in ("la_decode", "gdn_decode_mtp", "kda_decode_mtp", "la_replay",
+              "la_check_indices", "la_check_token_slots", "la_status_string",
+              "la_version"):
         assert n in names
 
 
@@ -250,3 +251,78 @@ def test_valid_call_without_gpu_reports_launch_failure():
                           text=True, timeout=120)
     assert proc.returncode == 0, proc.stderr
     assert proc.stdout.strip().splitlines()[-1] == "8"
+
+
+# ------------------------------------------------------------ la_replay
+
+
+def test_replay_struct_layout_matches_ctypes(tmp_path):
+    fields = [f for f, _ in bnd.ReplayArgs._fields_]
+    body = "\n".join(
+        '  printf("%s %%zu\\n", offsetof(la_replay_args, %s));' % (f, f)
+        for f in fields)
+    src = tmp_path / "layout.c"
+    src.write_text(
+        "#include <stdio.h>\n#include <stddef.h>\n#include \"la_decode.h\"\n"
+        "int main(void){\n  printf(\"size %%zu\\n\", sizeof(la_replay_args));\n"
+        "%s\n  return 0;\n}\n" % body)
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(exe)], check=True)
+    got = dict(ln.split() for ln in
+               subprocess.run([str(exe)], capture_output=True, text=True,
+                              check=True).stdout.splitlines())
+    assert int(got["size"]) == ctypes.sizeof(bnd.ReplayArgs)
+    for f in fields:
+        assert int(got[f]) == getattr(bnd.ReplayArgs, f).offset, f
+
+
+def _valid_replay(B=4, T=3, HV=4, K=128, V=128, pool_size=16):
+    a = bnd.ReplayArgs()
+    a.B, a.T, a.HV, a.K, a.V, a.pool_size = B, T, HV, K, V, pool_size
+    a.state_dtype = bnd.LA_F32
+    a.factors = FAKE + 0x800000
+    a.pool = FAKE + 0x1000000
+    a.sp = bnd.PoolStrides(HV * V * K, V * K, K)
+    a.read_idx = FAKE + 0x500000
+    a.write_idx = FAKE + 0x500100
+    a.num_tokens = FAKE + 0x500200
+    return a
+
+
+REPLAY_REJECT = [
+    ("T_zero", _mut(T=0), 2),
+    ("B_negative", _mut(B=-1), 2),
+    ("K_96", _mut(K=96), 7),
+    ("state_dtype_code", _mut(state_dtype=4), 5),
+    ("null_factors", _mut(factors=None), 1),
+    ("null_pool", _mut(pool=None), 1),
+    ("null_read_idx", _mut(read_idx=None), 1),
+    ("null_num_tokens", _mut(num_tokens=None), 1),
+    ("pool_heads_overlap", _mut(sp=bnd.PoolStrides(4 * 128 * 128, 64 * 128,
+                                                   128)), 3),
+    ("factors_misaligned", _mut(factors=FAKE + 0x800008), 4),
+    ("pool_misaligned", _mut(pool=FAKE + 0x1000008), 4),
+    ("num_tokens_misaligned", _mut(num_tokens=FAKE + 0x500202), 4),
+]
+
+
+@pytest.mark.parametrize("name,mutate,code", REPLAY_REJECT,
+                         ids=[r[0] for r in REPLAY_REJECT])
+def test_replay_host_validation_rejects(lib, name, mutate, code):
+    a = _valid_replay()
+    mutate(a)
+    assert lib.la_replay(ctypes.byref(a), None) == code, name
+
+
+def test_replay_rejects_null_and_empty_is_noop(lib):
+    assert lib.la_replay(None, None) == 1
+    a = _valid_replay(B=0)
+    a.factors = a.pool = a.read_idx = a.num_tokens = None
+    assert lib.la_replay(ctypes.byref(a), None) == 0
+
+
+def test_decode_factors_must_be_16_byte_aligned(lib):
+    a = _valid_args("kda")
+    a.factors = FAKE + 0x900008
+    assert _status("kda", a) == 4

@@ -40,6 +40,11 @@ MUTATIONS = {
     "paged_seed_off_by_one": (
         "r = (na >= 1 && na <= T) ? slots[(size_t)b * slots_stride + na - 1]",
         "r = (na >= 1 && na <= T) ? slots[(size_t)b * slots_stride + na % T]"),
+    "replay_decay_after_update": (
+        "S[(size_t)i * K + j] * a[j] + err[i] * kk[j];",
+        "(S[(size_t)i * K + j] + err[i] * kk[j]) * a[j];"),
+    "factor_err_missing_beta": ("rec[2 * K + i] = c;",
+                                "rec[2 * K + i] = vv[i] - u;"),
     "paged_write_wrong_token": (
         "const int ws = slots[(size_t)b * slots_stride + t];",
         "const int ws = slots[(size_t)b * slots_stride + T - 1 - t];"),

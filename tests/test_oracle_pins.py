@@ -512,3 +512,60 @@ def test_paged_slots_negative_seed_is_padding():
                         num_accepted=[1])
     assert not res["out"].any()
     np.testing.assert_array_equal(res["pool"], c["pool"])
+
+
+# ------------------------------------------------- factor records and replay
+
+
+@pytest.mark.parametrize("variant", [oracle.LIGHTNING, oracle.GDN, oracle.KDA])
+def test_factor_records_rebuild_every_token_state(variant):
+    """Replaying the first n records from the seed gives the state after
+    token n-1 (the per-token cache), for every n; a record's decay, key and
+    coefficient are the ones the update used."""
+    rng = np.random.default_rng(90 + variant)
+    B, T, HV, K, V = 3, 4, 2, 6, 5
+    c = _random_case(rng, variant, B=B, T=T, H=1, HV=HV, K=K, V=V,
+                     pool_size=7)
+    flags = 0 if variant == oracle.LIGHTNING else (
+        oracle.L2NORM_QK | oracle.BETA_LOGIT)
+    ridx = [5, 0, 3]
+    res = oracle.decode(variant, c["q"], c["k"], c["v"], c["g"], c["beta"],
+                        c["pool"], ridx, [-1, -1, -1], flags=flags,
+                        inter=True, factors=True)
+    fac = res["factors"]
+    assert np.isfinite(fac).all()
+    for n in range(0, T + 1):
+        rebuilt = oracle.replay(fac, c["pool"], ridx, [1, 2, 4], [n] * B)
+        for b in range(B):
+            want = c["pool"][ridx[b]] if n == 0 else res["inter"][b, n - 1]
+            assert _rel(rebuilt[[1, 2, 4][b]], want) < 1e-13
+    # the records themselves
+    a, kk, err = fac[..., :K], fac[..., K:2 * K], fac[..., 2 * K:]
+    if variant == oracle.KDA:
+        np.testing.assert_allclose(a, np.exp(c["g"]), rtol=1e-15)
+    elif variant == oracle.GDN:
+        np.testing.assert_allclose(a, np.exp(c["g"])[..., None].repeat(K, -1),
+                                   rtol=1e-15)
+    else:
+        np.testing.assert_allclose(a[0, 0], c["g"][:, None].repeat(K, -1),
+                                   rtol=1e-15)
+    if variant != oracle.LIGHTNING:
+        np.testing.assert_allclose(np.linalg.norm(kk, axis=-1), 1.0,
+                                   rtol=1e-6)
+    else:
+        np.testing.assert_array_equal(err, c["v"])
+
+
+def test_replay_skips_and_bounds():
+    """Zero records copy the seed to the write slot; a negative read slot or
+    a count outside [0, T] leaves the pool alone."""
+    rng = np.random.default_rng(95)
+    c = _random_case(rng, oracle.GDN, B=3, T=2, H=1, HV=1, K=4, V=3,
+                     pool_size=6)
+    res = oracle.decode(oracle.GDN, c["q"], c["k"], c["v"], c["g"], c["beta"],
+                        c["pool"], [0, 1, 2], [-1, -1, -1], factors=True)
+    out = oracle.replay(res["factors"], c["pool"], [0, -1, 2], [3, 4, 5],
+                        [0, 1, 3])
+    np.testing.assert_array_equal(out[3], c["pool"][0])
+    for s in (0, 1, 2, 4, 5):
+        np.testing.assert_array_equal(out[s], c["pool"][s])

@@ -214,6 +214,7 @@ def run_and_check(wl, reqs=None):
 # one; the untouched-byte check still covers the whole pool.
 SAMPLE = {"gdn_small_k64": None, "lightning_b33_h64": None,
           "gdn_gva_b64_bf16_state": range(0, 64, 3),
+          "kda_spec_b64_t4": range(0, 64, 5),
           "gdn_gva_b64": range(0, 64, 3), "gdn_mtp_b32_t4": range(32),
           "kda_b256_t1": range(0, 256, 9), "kda_b256_t8": range(0, 256, 17)}
 
@@ -764,3 +765,147 @@ def test_bf16_state_roundtrip_is_exact_when_unchanged():
     before = wl.backing.clone()
     got = gpu_run(wl)
     assert torch.equal(_bits(got["backing"]), _bits(before))
+
+
+# ------------------------------------------- update records and la_replay
+
+
+def _records_case(variant, seed, K=128, V=128, T=4, dtype=torch.bfloat16,
+                  state_dtype=torch.float32, B=4):
+    return W.make("rec", variant, B=B, T=T, H=2, HV=4, K=K, V=V,
+                  pool_size=2 * B + 3, seed=seed, act_dtype=dtype,
+                  pool_std=0.1, separate_write=True, inter=True,
+                  state_dtype=state_dtype)
+
+
+def _decode_with_records(wl):
+    """Decode without writeback, with the per-token cache and the records."""
+    lad = _lad()
+    d = wl.to(DEV)
+    pool = d.pool()
+    inter = torch.full((wl.B, wl.T, wl.HV, wl.V, wl.K), float("nan"),
+                       dtype=wl.backing.dtype, device=DEV)
+    fac = torch.full((wl.B, wl.T, wl.HV, 2 * wl.K + wl.V), float("nan"),
+                     dtype=torch.float32, device=DEV)
+    nowrite = torch.full((wl.B,), -1, dtype=torch.int32, device=DEV)
+    if wl.variant == W.LIGHTNING:
+        out, _ = lad.la_decode(d.q, d.k, d.v, pool, d.read_idx, nowrite,
+                               lam=d.g, inter=inter, factors=fac)
+    else:
+        fn = lad.gdn_decode_mtp if wl.variant == W.GDN else lad.kda_decode_mtp
+        out, _ = fn(d.q, d.k, d.v, d.g, d.beta, pool, d.read_idx, nowrite,
+                    inter=inter, factors=fac, l2norm_qk=wl.l2norm,
+                    beta_logit=wl.beta_logit)
+    torch.cuda.synchronize()
+    return d, out, inter, fac
+
+
+@pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN, W.KDA])
+@pytest.mark.parametrize("K,V", [(128, 128), (64, 128), (128, 64)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16],
+                         ids=["f32", "bf16"])
+def test_update_records_match_oracle(variant, K, V, dtype):
+    seed = (3000 + 100 * [W.LIGHTNING, W.GDN, W.KDA].index(variant)
+            + 10 * [(128, 128), (64, 128), (128, 64)].index((K, V))
+            + (5 if dtype == torch.bfloat16 else 0))
+    wl = _records_case(variant, seed, K=K, V=V, dtype=dtype)
+    d, out, inter, fac = _decode_with_records(wl)
+    ref = oracle.decode(VARIANT_CODE[wl.variant], wl.q, wl.k, wl.v, wl.g,
+                        wl.beta, wl.pool(), wl.read_idx, [-1] * wl.B,
+                        flags=_flags(wl), inter=True, factors=True)
+    kind, tol_out, tol_state = _tol(wl)
+    got = fac.cpu().numpy()
+    a, kk, err = (got[..., :K], got[..., K:2 * K], got[..., 2 * K:])
+    ra, rk, re_ = (ref["factors"][..., :K], ref["factors"][..., K:2 * K],
+                   ref["factors"][..., 2 * K:])
+    assert _err("rel", a, ra) <= 1e-5
+    assert _err("rel", kk, rk) <= (1e-5 if dtype == torch.float32 else 1e-3)
+    assert _err(kind, err, re_) <= tol_out
+    assert _err(kind, out.cpu().numpy(), ref["out"]) <= tol_out
+    # no writeback: the pool is untouched
+    assert torch.equal(_bits(d.backing.cpu()), _bits(wl.backing))
+
+
+@pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN, W.KDA])
+@pytest.mark.parametrize("state_dtype", [torch.float32, torch.bfloat16],
+                         ids=["f32state", "bf16state"])
+@pytest.mark.parametrize("T", [1, 4, 11])
+def test_replay_equals_per_token_cache_bitwise(variant, state_dtype, T):
+    """Replaying n records from the seed reproduces the decode's state after
+    token n-1 bit for bit (same fp32 operations on the same values)."""
+    seed = 3500 + 10 * [W.LIGHTNING, W.GDN, W.KDA].index(variant) + T + (
+        1000 if state_dtype == torch.bfloat16 else 0)
+    wl = _records_case(variant, seed, T=T, state_dtype=state_dtype)
+    lad = _lad()
+    d, out, inter, fac = _decode_with_records(wl)
+    pool = d.pool()
+    assert torch.isfinite(fac).all()
+    for n in sorted({0, 1, T // 2, T}):
+        ntok = torch.full((wl.B,), n, dtype=torch.int32, device=DEV)
+        lad.replay(fac, pool, d.read_idx, d.write_idx, ntok)
+        torch.cuda.synchronize()
+        for b in range(wl.B):
+            w = int(wl.write_idx[b])
+            if w < 0:
+                continue
+            want = (pool[int(wl.read_idx[b])] if n == 0
+                    else inter[b, n - 1])
+            assert torch.equal(_bits(pool[w]), _bits(want)), (b, n)
+    # the read slots and every slot nobody writes keep their bytes
+    written = {int(x) for x in wl.write_idx.tolist() if x >= 0}
+    keep = torch.ones(wl.pool_size, dtype=torch.bool)
+    keep[torch.tensor(sorted(written))] = False
+    assert torch.equal(_bits(pool.cpu())[keep], _bits(wl.pool())[keep])
+
+
+def test_replay_skips_out_of_range_counts_and_padding():
+    wl = _records_case(W.KDA, 3900, T=3)
+    lad = _lad()
+    d, out, inter, fac = _decode_with_records(wl)
+    pool = d.pool()
+    before = pool.cpu().clone()
+    ridx = d.read_idx.clone()
+    ridx[0] = -1
+    ntok = torch.tensor([2, -1, 4, 3], dtype=torch.int32, device=DEV)
+    lad.replay(fac, pool, ridx, d.write_idx, ntok)
+    torch.cuda.synchronize()
+    after = pool.cpu()
+    for b in range(3):  # padded read, negative count, count > T
+        w = int(wl.write_idx[b])
+        if w >= 0:
+            assert torch.equal(_bits(after[w]), _bits(before[w]))
+    w3 = int(wl.write_idx[3])
+    if w3 >= 0:
+        assert torch.equal(_bits(after[w3]), _bits(inter[3, 2].cpu()))
+
+
+def test_named_spec_step_parity():
+    """The speculative step the benchmark times: verify with records (no
+    state write), then replay the accepted tokens into the write slots;
+    compared with the oracle's records and replay."""
+    lad = _lad()
+    wl = W.named("kda_spec_b64_t4")
+    d = wl.to(DEV)
+    pool = d.pool()
+    rec = torch.full((wl.B, wl.T, wl.HV, wl.record_floats), float("nan"),
+                     dtype=torch.float32, device=DEV)
+    nowrite = torch.full((wl.B,), -1, dtype=torch.int32, device=DEV)
+    out, _ = lad.kda_decode_mtp(d.q, d.k, d.v, d.g, d.beta, pool, d.read_idx,
+                                nowrite, factors=rec, l2norm_qk=True,
+                                beta_logit=True)
+    lad.replay(rec, pool, d.read_idx, d.write_idx, d.replay_tokens)
+    torch.cuda.synchronize()
+    ref = oracle.decode(oracle.KDA, wl.q, wl.k, wl.v, wl.g, wl.beta,
+                        wl.pool(), wl.read_idx, [-1] * wl.B, flags=_flags(wl),
+                        factors=True)
+    refpool = oracle.replay(ref["factors"], wl.pool(), wl.read_idx,
+                            wl.write_idx, wl.replay_tokens)
+    kind, tol_out, tol_state = _tol(wl)
+    assert _err(kind, out.cpu().numpy(), ref["out"]) <= tol_out
+    got = pool.cpu()
+    written = [int(w) for w in wl.write_idx.tolist() if w >= 0]
+    for w in written:
+        assert _err(kind, got[w].numpy(), refpool[w]) <= tol_state
+    keep = torch.ones(wl.pool_size, dtype=torch.bool)
+    keep[torch.tensor(written)] = False
+    assert torch.equal(_bits(got)[keep], _bits(wl.pool())[keep])

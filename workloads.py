@@ -54,6 +54,14 @@ class Workload:
     # the call uses them instead of read_idx/write_idx
     token_slots: Optional[torch.Tensor] = None
     num_accepted: Optional[torch.Tensor] = None
+    # speculative step with update records: the decode reads the read slots,
+    # writes no state and records every token; then the first
+    # replay_tokens[b] records are replayed into write slot b
+    replay_tokens: Optional[torch.Tensor] = None
+
+    @property
+    def record_floats(self) -> int:
+        return 2 * self.K + self.V
 
     def pool(self, backing: Optional[torch.Tensor] = None) -> torch.Tensor:
         """The logical pool [pool_size, HV, V, K]: every stride_mult-th slot
@@ -78,6 +86,15 @@ class Workload:
         write per active (request, value head) tile, plus one cache write
         per token when intermediate states are kept."""
         tile = self.V * self.K * self.backing.element_size()
+        if self.replay_tokens is not None:
+            ridx = self.read_idx.tolist()
+            widx = self.write_idx.tolist()
+            n = self.replay_tokens.tolist()
+            active = sum(1 for r in ridx if r >= 0)
+            replayed = sum(1 for r, w, c in zip(ridx, widx, n)
+                           if r >= 0 and w >= 0 and 0 <= c <= self.T)
+            # decode reads every active tile; replay reads and writes again
+            return (active + 2 * replayed) * self.HV * tile
         if self.token_slots is not None:
             reads = writes = 0
             for row, na in zip(self.token_slots.tolist(),
@@ -118,6 +135,12 @@ class Workload:
             n += B * 4 * (2 if self.write_idx is not None else 1)
         out_size = torch.empty((), dtype=self.out_dtype).element_size()
         n += B * T * HV * V * out_size
+        if self.replay_tokens is not None:
+            rec = self.record_floats * 4 * HV
+            n += B * T * rec  # records written by the decode
+            n += sum(c for c in self.replay_tokens.tolist()
+                     if 0 <= c <= T) * rec  # and read back by the replay
+            n += B * 4 * 2  # replay's read slots and token counts
         return n
 
 
@@ -130,12 +153,14 @@ def make(name, variant, B, T, H, HV, K, V, pool_size, *, seed,
          l2norm=True, beta_logit=True, stride_mult=1, read_idx=None,
          write_idx=None, separate_write=False, write_skip=0.0,
          inter=False, lightning_decay=None, out_dtype=torch.float32,
-         paged=False, state_dtype=torch.float32):
+         paged=False, state_dtype=torch.float32, spec_replay=False):
     """Draw one workload.
 
     paged: draw a [B, T] per-token slot table of distinct slots and accepted
     counts uniform in [1, T] (needs pool_size >= B*T); read_idx/write_idx
     then hold the seed slots and -1 (informational only).
+    spec_replay: a verify step with update records followed by a replay of
+    replay_tokens[b] ~U{1..T} records into the (separate) write slots.
 
     read_idx: explicit list, or None for ``randperm(pool_size)[:B]``.
     write_idx: explicit list, or None: equal to read_idx unless
@@ -193,13 +218,20 @@ def make(name, variant, B, T, H, HV, K, V, pool_size, *, seed,
             widx[drop] = -1
     else:
         widx = None
+    replay_tokens = None
+    if spec_replay:
+        if widx is None:
+            raise ValueError("spec_replay needs separate write slots")
+        replay_tokens = torch.randint(1, T + 1, (B,), generator=gen,
+                                      dtype=torch.int32)
     return Workload(name=name, variant=variant, B=B, T=T, H=H, HV=HV, K=K,
                     V=V, pool_size=pool_size,
                     l2norm=l2norm if variant != LIGHTNING else False,
                     beta_logit=beta_logit if variant != LIGHTNING else False,
                     q=q, k=k, v=v, g=g, beta=beta, backing=backing,
                     stride_mult=stride_mult, read_idx=ridx, write_idx=widx,
-                    inter=inter, out_dtype=out_dtype)
+                    inter=inter, out_dtype=out_dtype,
+                    replay_tokens=replay_tokens)
 
 
 # The named workloads. Each is the shape, distribution and index structure of
@@ -260,6 +292,16 @@ def gdn_paged_b64_t4(seed=6):
                 paged=True)
 
 
+def kda_spec_b64_t4(seed=7):
+    """KDA speculative step with update records: B=64 requests verify T=4
+    tokens (H=HV=24, K=V=128) reading their state but writing only a
+    [a | k | err] record per token; then the records of the accepted tokens
+    (~U{1..4}) are replayed into a separate write slot (pool of 160)."""
+    return make("kda_spec_b64_t4", KDA, B=64, T=4, H=24, HV=24, K=128,
+                V=128, pool_size=160, seed=seed, separate_write=True,
+                spec_replay=True)
+
+
 def gdn_gva_b64_bf16_state(seed=3):
     """The grouped-value GDN decode (B=64, 16 q/k heads, 32 value heads,
     K=V=128, T=1, pool 128) with the state pool stored in bf16."""
@@ -277,6 +319,7 @@ NAMED = {
     "kda_b256_t8": lambda seed=5: kda_b256(8, seed),
     "gdn_paged_b64_t4": gdn_paged_b64_t4,
     "gdn_gva_b64_bf16_state": gdn_gva_b64_bf16_state,
+    "kda_spec_b64_t4": kda_spec_b64_t4,
 }
 
 
