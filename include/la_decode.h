@@ -76,9 +76,8 @@ typedef enum la_status {
     LA_ERR_STRIDE = 3,      /* negative stride, innermost stride != 1,
                                overlapping pool tiles or outputs, or a tile
                                whose rows span 2 GiB or more                 */
-    LA_ERR_ALIGN = 4,       /* pool / cache row not aligned to four state
-                               elements, or an activation not aligned to its
-                               element size                                  */
+    LA_ERR_ALIGN = 4,       /* pool / cache row not 16-byte aligned, or an
+                               activation not aligned to its element size    */
     LA_ERR_DTYPE = 5,       /* unknown dtype code                            */
     LA_ERR_ARG = 6,         /* argument inconsistent with the entry point
                                (e.g. beta or flags given to la_decode, an
@@ -140,8 +139,7 @@ typedef struct la_decode_args {
     la_act_strides sbeta;
 
     void *pool;        /* [pool_size, HV, V, K] in state_dtype, updated in
-                          place; base and every row start aligned to four
-                          elements (16 B fp32, 8 B bf16)                   */
+                          place; base and every row start 16-byte aligned  */
     la_pool_strides sp;
     const int32_t *read_idx;  /* [B] contiguous                             */
     const int32_t *write_idx; /* [B] contiguous, or NULL (= read_idx)       */

@@ -20,9 +20,10 @@
 //    held in VGPRs across all T tokens, so the pool sees one read and at most
 //    one write per pair per call.
 //  - Within a wave, 8 lanes share one row: lane (c, r) with c = lane & 7 and
-//    r = lane >> 3 holds rows {R w + 8 i + r} and the 16-byte column chunks
-//    {c + 8 m}. Each global_load_dwordx4 of the wave reads 8 whole 128-byte
-//    row segments; every byte of the tile is read once and written once.
+//    r = lane >> 3 holds rows {R w + 8 i + r} and the 16-byte chunks
+//    {c + 8 j} of each (4 fp32 or 8 bf16 columns). Each 128-bit buffer load
+//    of the wave reads 8 whole 128-byte row segments; every byte of the tile
+//    is read once and written once.
 //  - Row dot products (S k and S q) reduce over the 8 lanes of a row with
 //    three DPP butterfly adds; the butterfly leaves a bit-identical sum in
 //    all 8 lanes, so the rank-1 update needs no broadcast.
@@ -179,49 +180,75 @@ typedef unsigned u2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 typedef float f2 __attribute__((ext_vector_type(2)));
 
-// State tile I/O in the pool's element type. A lane's chunk is always four
-// consecutive columns: 16 bytes of fp32 or 8 bytes of bf16. bf16 widens
-// exactly to fp32 on load and rounds to nearest even (v_cvt_pk_bf16_f32)
-// on store; all arithmetic stays fp32.
+// State tile I/O in the pool's element type. Every lane moves whole
+// 16-byte chunks (128-bit buffer loads and stores): chunk j of lane c holds
+// elements (c + 8 j) * 16/ES ... of a row, so a wave instruction covers eight
+// full 128-byte row segments in either dtype. In registers a lane keeps its
+// columns as groups of four fp32 values: one group per chunk for fp32, two
+// for bf16 (widened exactly on load, rounded to nearest even on store by
+// v_cvt_pk_bf16_f32). All arithmetic stays fp32.
 template <bool BF16S>
 struct StateIO {
     static constexpr uint32_t ES = BF16S ? 2u : 4u;  // bytes per element
+    static constexpr int GPC = BF16S ? 2 : 1;         // 4-col groups / chunk
 
-    template <int POLICY>
-    static __device__ __forceinline__ f4 load(BufRsrc r, uint32_t voff,
-                                              uint32_t soff)
+    // first column of the lane's 4-column group m
+    static __device__ __forceinline__ int col(int m, int c8)
     {
-        if constexpr (BF16S) {
-            const u2 h = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff,
-                                                              POLICY);
-            f4 x;
-            x.x = __uint_as_float(h.x << 16);
-            x.y = __uint_as_float(h.x & 0xffff0000u);
-            x.z = __uint_as_float(h.y << 16);
-            x.w = __uint_as_float(h.y & 0xffff0000u);
-            return x;
-        } else {
-            return __builtin_bit_cast(
-                f4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff,
-                                                          POLICY));
+        return (c8 + 8 * (m / GPC)) * (4 * GPC) + 4 * (m % GPC);
+    }
+
+    // one row: `lane` = the lane's byte offset in the row, `soff` = the
+    // row's uniform offset; the groups of chunk j sit j * 128 bytes further
+    template <int POLICY, int CPL>
+    static __device__ __forceinline__ void load_row(f4 (&x)[CPL], BufRsrc r,
+                                                    uint32_t lane,
+                                                    uint32_t soff)
+    {
+#pragma unroll
+        for (int j = 0; j < CPL / GPC; ++j) {
+            const u4 h = __builtin_amdgcn_raw_buffer_load_b128(
+                r, lane + j * 128u, soff, POLICY);
+            if constexpr (BF16S) {
+                x[2 * j] = f4{__uint_as_float(h.x << 16),
+                              __uint_as_float(h.x & 0xffff0000u),
+                              __uint_as_float(h.y << 16),
+                              __uint_as_float(h.y & 0xffff0000u)};
+                x[2 * j + 1] = f4{__uint_as_float(h.z << 16),
+                                  __uint_as_float(h.z & 0xffff0000u),
+                                  __uint_as_float(h.w << 16),
+                                  __uint_as_float(h.w & 0xffff0000u)};
+            } else {
+                x[j] = __builtin_bit_cast(f4, h);
+            }
         }
     }
 
-    static __device__ __forceinline__ void store(BufRsrc r, uint32_t voff,
-                                                 uint32_t soff, f4 x)
+    template <int CPL>
+    static __device__ __forceinline__ void store_row(BufRsrc r, uint32_t lane,
+                                                     uint32_t soff,
+                                                     const f4 (&x)[CPL])
     {
-        if constexpr (BF16S) {
-            const f2 lo = {x.x, x.y}, hi = {x.z, x.w};
-            u2 h;
-            h.x = __builtin_bit_cast(unsigned, __builtin_convertvector(lo, bf2));
-            h.y = __builtin_bit_cast(unsigned, __builtin_convertvector(hi, bf2));
-            __builtin_amdgcn_raw_buffer_store_b64(h, r, voff, soff,
-                                                  kStreamPolicy);
-        } else {
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, x),
-                                                   r, voff, soff,
-                                                   kStreamPolicy);
+#pragma unroll
+        for (int j = 0; j < CPL / GPC; ++j) {
+            u4 h;
+            if constexpr (BF16S) {
+                h.x = pack(x[2 * j].x, x[2 * j].y);
+                h.y = pack(x[2 * j].z, x[2 * j].w);
+                h.z = pack(x[2 * j + 1].x, x[2 * j + 1].y);
+                h.w = pack(x[2 * j + 1].z, x[2 * j + 1].w);
+            } else {
+                h = __builtin_bit_cast(u4, x[j]);
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(h, r, lane + j * 128u,
+                                                   soff, kStreamPolicy);
         }
+    }
+
+    static __device__ __forceinline__ unsigned pack(float lo, float hi)
+    {
+        const f2 v = {lo, hi};
+        return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf2));
     }
 };
 
@@ -386,8 +413,6 @@ decode_kernel(const Params p)
 {
     using IO = StateIO<BF16S>;
     constexpr uint32_t ES = IO::ES;
-    constexpr uint32_t kChunk = 4 * ES;        // bytes of one lane chunk
-    constexpr uint32_t kChunkStep = 32 * ES;   // bytes between chunks m, m+1
     extern __shared__ f4 lds_raw[];
     float *lds = reinterpret_cast<float *>(lds_raw);
     using L = TokLayout<VAR, K, V>;
@@ -439,29 +464,21 @@ decode_kernel(const Params p)
     const uint32_t row_bytes = static_cast<uint32_t>(p.sp_row) * ES;
     const uint32_t tile_bytes = static_cast<uint32_t>(
         (static_cast<int64_t>(V - 1) * p.sp_row + K) * ES);
-    const uint32_t lane_off = rs * row_bytes + c8 * kChunk;
+    const uint32_t lane_off = rs * row_bytes + c8 * 16u;
     char *const pool = static_cast<char *>(p.pool);
     const BufRsrc src = make_rsrc(
         pool + (r * p.sp_slot + hv * p.sp_head) * ES, tile_bytes);
     f4 S[RPL][CPL];
     if (p.stream_loads) {
 #pragma unroll
-        for (int i = 0; i < RPL; ++i) {
-            const uint32_t row0 = (wave * kRowsPerWave + i * 8) * row_bytes;
-#pragma unroll
-            for (int m = 0; m < CPL; ++m)
-                S[i][m] = IO::template load<kStreamPolicy>(
-                    src, lane_off + m * kChunkStep, row0);
-        }
+        for (int i = 0; i < RPL; ++i)
+            IO::template load_row<kStreamPolicy>(
+                S[i], src, lane_off, (wave * kRowsPerWave + i * 8) * row_bytes);
     } else {
 #pragma unroll
-        for (int i = 0; i < RPL; ++i) {
-            const uint32_t row0 = (wave * kRowsPerWave + i * 8) * row_bytes;
-#pragma unroll
-            for (int m = 0; m < CPL; ++m)
-                S[i][m] = IO::template load<kCachedPolicy>(
-                    src, lane_off + m * kChunkStep, row0);
-        }
+        for (int i = 0; i < RPL; ++i)
+            IO::template load_row<kCachedPolicy>(
+                S[i], src, lane_off, (wave * kRowsPerWave + i * 8) * row_bytes);
     }
 
     for (int t0 = 0; t0 < T; t0 += kTokChunk) {
@@ -493,7 +510,7 @@ decode_kernel(const Params p)
 #pragma unroll
                 for (int m = 0; m < CPL; ++m) {
                     const f4 e = *reinterpret_cast<const f4 *>(
-                        rec + L::eOff + 4 * (c8 + 8 * m));
+                        rec + L::eOff + IO::col(m, c8));
 #pragma unroll
                     for (int i = 0; i < RPL; ++i)
                         S[i][m] *= e;
@@ -517,9 +534,9 @@ decode_kernel(const Params p)
 #pragma unroll
             for (int m = 0; m < CPL; ++m) {
                 kk[m] = *reinterpret_cast<const f4 *>(
-                    rec + L::kOff + 4 * (c8 + 8 * m));
+                    rec + L::kOff + IO::col(m, c8));
                 const f4 qq = *reinterpret_cast<const f4 *>(
-                    rec + L::qOff + 4 * (c8 + 8 * m));
+                    rec + L::qOff + IO::col(m, c8));
 #pragma unroll
                 for (int i = 0; i < RPL; ++i) {
                     if constexpr (VAR != VAR_LA) {
@@ -583,14 +600,10 @@ decode_kernel(const Params p)
                         pool + (ws * p.sp_slot + hv * p.sp_head) * ES,
                         tile_bytes);
 #pragma unroll
-                    for (int i = 0; i < RPL; ++i) {
-                        const uint32_t row0 =
-                            (wave * kRowsPerWave + i * 8) * row_bytes;
-#pragma unroll
-                        for (int m = 0; m < CPL; ++m)
-                            IO::store(dst, lane_off + m * kChunkStep, row0,
-                                      S[i][m]);
-                    }
+                    for (int i = 0; i < RPL; ++i)
+                        IO::store_row(dst, lane_off,
+                                      (wave * kRowsPerWave + i * 8) * row_bytes,
+                                      S[i]);
                 }
             }
 
@@ -601,15 +614,11 @@ decode_kernel(const Params p)
                         ((static_cast<int64_t>(b) * T + t) * p.HV + hv) *
                             static_cast<int64_t>(V * K * ES),
                     V * K * ES);
-                const uint32_t ioff = rs * (K * ES) + c8 * kChunk;
+                const uint32_t ioff = rs * (K * ES) + c8 * 16u;
 #pragma unroll
-                for (int i = 0; i < RPL; ++i) {
-                    const uint32_t row0 =
-                        (wave * kRowsPerWave + i * 8) * K * ES;
-#pragma unroll
-                    for (int m = 0; m < CPL; ++m)
-                        IO::store(dst, ioff + m * kChunkStep, row0, S[i][m]);
-                }
+                for (int i = 0; i < RPL; ++i)
+                    IO::store_row(dst, ioff,
+                                  (wave * kRowsPerWave + i * 8) * K * ES, S[i]);
             }
         }
     }
@@ -618,12 +627,9 @@ decode_kernel(const Params p)
         const BufRsrc dst = make_rsrc(
             pool + (w * p.sp_slot + hv * p.sp_head) * ES, tile_bytes);
 #pragma unroll
-        for (int i = 0; i < RPL; ++i) {
-            const uint32_t row0 = (wave * kRowsPerWave + i * 8) * row_bytes;
-#pragma unroll
-            for (int m = 0; m < CPL; ++m)
-                IO::store(dst, lane_off + m * kChunkStep, row0, S[i][m]);
-        }
+        for (int i = 0; i < RPL; ++i)
+            IO::store_row(dst, lane_off,
+                          (wave * kRowsPerWave + i * 8) * row_bytes, S[i]);
     }
 }
 
@@ -647,8 +653,6 @@ replay_kernel(const ReplayParams p)
 {
     using IO = StateIO<BF16S>;
     constexpr uint32_t ES = IO::ES;
-    constexpr uint32_t kChunk = 4 * ES;
-    constexpr uint32_t kChunkStep = 32 * ES;
     constexpr int NW = V / kRowsPerWave;
     constexpr int RPL = kRowsPerWave / 8;
     constexpr int CPL = K / 32;
@@ -672,19 +676,15 @@ replay_kernel(const ReplayParams p)
     const uint32_t row_bytes = static_cast<uint32_t>(p.sp_row) * ES;
     const uint32_t tile_bytes = static_cast<uint32_t>(
         (static_cast<int64_t>(V - 1) * p.sp_row + K) * ES);
-    const uint32_t lane_off = rs * row_bytes + c8 * kChunk;
+    const uint32_t lane_off = rs * row_bytes + c8 * 16u;
     char *const pool = static_cast<char *>(p.pool);
     const BufRsrc src = make_rsrc(
         pool + (r * p.sp_slot + hv * p.sp_head) * ES, tile_bytes);
     f4 S[RPL][CPL];
 #pragma unroll
-    for (int i = 0; i < RPL; ++i) {
-        const uint32_t row0 = (wave * kRowsPerWave + i * 8) * row_bytes;
-#pragma unroll
-        for (int m = 0; m < CPL; ++m)
-            S[i][m] = IO::template load<kStreamPolicy>(
-                src, lane_off + m * kChunkStep, row0);
-    }
+    for (int i = 0; i < RPL; ++i)
+        IO::template load_row<kStreamPolicy>(
+            S[i], src, lane_off, (wave * kRowsPerWave + i * 8) * row_bytes);
 
     const f4 *grec = reinterpret_cast<const f4 *>(
         p.factors + (static_cast<int64_t>(b) * p.T * p.HV + hv) * RS);
@@ -707,9 +707,9 @@ replay_kernel(const ReplayParams p)
 #pragma unroll
             for (int m = 0; m < CPL; ++m) {
                 const f4 a = *reinterpret_cast<const f4 *>(
-                    rec + 4 * (c8 + 8 * m));
+                    rec + IO::col(m, c8));
                 const f4 kk = *reinterpret_cast<const f4 *>(
-                    rec + K + 4 * (c8 + 8 * m));
+                    rec + K + IO::col(m, c8));
 #pragma unroll
                 for (int i = 0; i < RPL; ++i) {
                     S[i][m] *= a;
@@ -726,12 +726,9 @@ replay_kernel(const ReplayParams p)
         const BufRsrc dst = make_rsrc(
             pool + (w * p.sp_slot + hv * p.sp_head) * ES, tile_bytes);
 #pragma unroll
-        for (int i = 0; i < RPL; ++i) {
-            const uint32_t row0 = (wave * kRowsPerWave + i * 8) * row_bytes;
-#pragma unroll
-            for (int m = 0; m < CPL; ++m)
-                IO::store(dst, lane_off + m * kChunkStep, row0, S[i][m]);
-        }
+        for (int i = 0; i < RPL; ++i)
+            IO::store_row(dst, lane_off,
+                          (wave * kRowsPerWave + i * 8) * row_bytes, S[i]);
     }
 }
 
@@ -986,11 +983,12 @@ la_status validate(const la_decode_args *a, int var)
         return LA_ERR_ALIGN;
     if (a->beta && !aligned(a->beta, 4))
         return LA_ERR_ALIGN;
-    // a lane chunk is four state elements: 16 B (fp32) or 8 B (bf16)
-    if (!aligned(a->pool, 4 * es) || (a->sp.slot % 4) || (a->sp.head % 4) ||
-        (a->sp.row % 4))
+    // lanes move 16-byte chunks: every row start 16-byte aligned
+    const int64_t epc = 16 / es;  // elements per chunk
+    if (!aligned(a->pool, 16) || (a->sp.slot % epc) || (a->sp.head % epc) ||
+        (a->sp.row % epc))
         return LA_ERR_ALIGN;
-    if (a->inter && !aligned(a->inter, 4 * es))
+    if (a->inter && !aligned(a->inter, 16))
         return LA_ERR_ALIGN;
     if (a->factors && !aligned(a->factors, 16))
         return LA_ERR_ALIGN;
@@ -1115,8 +1113,9 @@ la_status la_replay(const la_replay_args *a, void *stream)
     const int64_t es = a->state_dtype == LA_BF16 ? 2 : 4;
     if ((static_cast<int64_t>(a->V - 1) * a->sp.row + a->K) * es > INT32_MAX)
         return LA_ERR_STRIDE;
-    if (!aligned(a->pool, 4 * es) || (a->sp.slot % 4) || (a->sp.head % 4) ||
-        (a->sp.row % 4))
+    const int64_t epc = 16 / es;
+    if (!aligned(a->pool, 16) || (a->sp.slot % epc) || (a->sp.head % epc) ||
+        (a->sp.row % epc))
         return LA_ERR_ALIGN;
     if (!aligned(a->factors, 16) || !aligned(a->read_idx, 4) ||
         !aligned(a->write_idx, 4) || !aligned(a->num_tokens, 4))

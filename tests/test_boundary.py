@@ -172,8 +172,13 @@ REJECT = [
     ("state_dtype_code", _mut(state_dtype=9), "kda", 5),
     ("bf16_pool_misaligned", _mut(state_dtype=1, pool=FAKE + 0x1000004),
      "gdn", 4),
-    ("bf16_inter_misaligned", _mut(state_dtype=1, inter=FAKE + 0x2000004),
+    ("bf16_inter_misaligned", _mut(state_dtype=1, inter=FAKE + 0x2000008),
      "lightning", 4),
+    ("bf16_pool_8B_aligned", _mut(state_dtype=1, pool=FAKE + 0x1000008),
+     "kda", 4),
+    ("bf16_row_stride_4_elements",
+     _mut(state_dtype=1, sp=bnd.PoolStrides(4 * 132 * 128, 132 * 128, 132)),
+     "gdn", 4),
     # paged per-token slots: the table replaces read/write slots, needs the
     # accepted counts and an explicit row stride covering T
     ("paged_with_read_idx", _mut(token_slots=FAKE + 0x700000,
