@@ -176,6 +176,21 @@ __device__ __forceinline__ BufRsrc make_rsrc(const void *base, uint32_t bytes)
                                              kBufDword3);
 }
 
+// 128-bit store of the tile: `lane` = the lane's byte offset, `soff` = a
+// uniform (row) offset. A store wider than 64 bits may read its data VGPRs
+// after it issues, so a VALU write to them needs one wait state in between.
+// The compiler inserts that wait only for buffer stores whose soffset is not
+// an SGPR, so the whole offset goes in voffset and soffset stays the constant
+// 0. The empty asm makes `soff` opaque at each store, so the VGPR sum is
+// formed there and dies there instead of being hoisted and held in a VGPR.
+__device__ __forceinline__ void store_b128(u4 x, BufRsrc r, uint32_t lane,
+                                           uint32_t soff)
+{
+    asm volatile("" : "+s"(soff));
+    __builtin_amdgcn_raw_buffer_store_b128(x, r, lane + soff, 0,
+                                           kStreamPolicy);
+}
+
 typedef unsigned u2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 typedef float f2 __attribute__((ext_vector_type(2)));
@@ -240,8 +255,7 @@ struct StateIO {
             } else {
                 h = __builtin_bit_cast(u4, x[j]);
             }
-            __builtin_amdgcn_raw_buffer_store_b128(h, r, lane + j * 128u,
-                                                   soff, kStreamPolicy);
+            store_b128(h, r, lane + j * 128u, soff);
         }
     }
 
@@ -276,9 +290,10 @@ struct TokLayout {
 
 // Position of state row `row` inside the LDS v record: the rows a lane owns
 // (R w + 8 i + r, i = 0..R/8-1, R rows per wave) sit at R w + (R/8) r + i.
+template <int R>
 __device__ __forceinline__ int v_slot(int row)
 {
-    constexpr int R = kRowsPerWave, RPL = kRowsPerWave / 8;
+    constexpr int RPL = R / 8;
     const int w = row / R, i = (row % R) / 8, r = row % 8;
     return w * R + r * RPL + i;
 }
@@ -323,9 +338,10 @@ __device__ __forceinline__ void prologue_load(const Params &p, int b, int hv,
     }
 }
 
-// Second half: l2norm, k.q, sigmoid, exp; writes the LDS record `rec` and,
-// when `frec` is set, the decay and key of the token's update record.
-template <int VAR, int K, int V>
+// Second half: l2norm, k.q, sigmoid, exp; writes the LDS record `rec` (v
+// rows placed for R rows per wave) and, when `frec` is set, the decay and
+// key of the token's update record.
+template <int VAR, int K, int V, int R = kRowsPerWave>
 __device__ __forceinline__ void prologue_finish(const Params &p, int hv,
                                                 int lane,
                                                 const TokRaw<K, V> &raw,
@@ -375,7 +391,7 @@ __device__ __forceinline__ void prologue_finish(const Params &p, int hv,
     }
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
-        rec[L::vOff + v_slot(lane * VPL + i)] = raw.v[i];
+        rec[L::vOff + v_slot<R>(lane * VPL + i)] = raw.v[i];
     if (lane == 0) {
         float beta = 1.f;
         if constexpr (VAR != VAR_LA)
@@ -633,6 +649,161 @@ decode_kernel(const Params p)
     }
 }
 
+// One token on a bf16 pool, with no per-token state writes: the tile stays
+// packed in registers (two bf16 per VGPR) and each element is widened where
+// it is used, so a wave holds 64 rows in the registers that 32 fp32 rows
+// take in decode_kernel, and twice as many tile bytes are in flight per
+// compute unit. The arithmetic and its order are those of decode_kernel for
+// T = 1 (widen, decay, dot products, rank-1 FMA, one rounding on store), so
+// the two kernels give identical bits.
+template <int VAR, int K, int V, bool BF16IN, bool BF16OUT>
+__global__ void __launch_bounds__(V) decode_packed_kernel(const Params p)
+{
+    constexpr int R = 64;        // rows per wave
+    constexpr int RPL = R / 8;   // rows per lane
+    constexpr int NCH = K / 64;  // 16-byte chunks (8 columns) per lane and row
+    constexpr uint32_t ES = 2;
+    using L = TokLayout<VAR, K, V>;
+    extern __shared__ f4 lds_raw[];
+    float *lds = reinterpret_cast<float *>(lds_raw);
+
+    const int pair = blockIdx.x;
+    const int b = pair / p.HV;
+    const int hv = pair - b * p.HV;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c8 = lane & 7;
+    const int rs = lane >> 3;
+
+    const int r = __builtin_amdgcn_readfirstlane(p.ridx[b]);
+    const int w = __builtin_amdgcn_readfirstlane(p.widx ? p.widx[b] : r);
+    // every lane writes one output row: R wave + 8 c8 + rs
+    const int64_t oidx = b * p.so_b + hv * p.so_h + wave * R + c8 * 8 + rs;
+    if (r < 0) {
+        store_out<BF16OUT>(p.out, oidx, 0.f);
+        return;
+    }
+
+    // lane (c8, rs) holds rows R wave + 8 i + rs and the 16-byte chunks
+    // c8 + 8 j of each: columns (c8 + 8 j) * 8 ... + 7
+    const uint32_t row_bytes = static_cast<uint32_t>(p.sp_row) * ES;
+    const uint32_t tile_bytes = static_cast<uint32_t>(
+        (static_cast<int64_t>(V - 1) * p.sp_row + K) * ES);
+    const uint32_t lane_off = rs * row_bytes + c8 * 16u;
+    char *const pool = static_cast<char *>(p.pool);
+    const BufRsrc src = make_rsrc(
+        pool + (r * p.sp_slot + hv * p.sp_head) * ES, tile_bytes);
+    u4 P[RPL][NCH];
+    if (p.stream_loads) {
+#pragma unroll
+        for (int i = 0; i < RPL; ++i)
+#pragma unroll
+            for (int j = 0; j < NCH; ++j)
+                P[i][j] = __builtin_amdgcn_raw_buffer_load_b128(
+                    src, lane_off + j * 128u, (wave * R + i * 8) * row_bytes,
+                    kStreamPolicy);
+    } else {
+#pragma unroll
+        for (int i = 0; i < RPL; ++i)
+#pragma unroll
+            for (int j = 0; j < NCH; ++j)
+                P[i][j] = __builtin_amdgcn_raw_buffer_load_b128(
+                    src, lane_off + j * 128u, (wave * R + i * 8) * row_bytes,
+                    kCachedPolicy);
+    }
+
+    if (wave == 0) {
+        TokRaw<K, V> rw;
+        prologue_load<VAR, K, V, BF16IN>(p, b, hv, 0, lane, rw);
+        prologue_finish<VAR, K, V, R>(p, hv, lane, rw, lds, nullptr);
+    }
+    lds_barrier();
+
+    const float beta = lds[L::sOff + 0];
+    const float decay = lds[L::sOff + 1];
+    const float kq = lds[L::sOff + 2];
+    auto colof = [&](int m) { return (c8 + 8 * (m / 2)) * 8 + 4 * (m % 2); };
+    f4 kk[2 * NCH], qq[2 * NCH], ee[2 * NCH];
+#pragma unroll
+    for (int m = 0; m < 2 * NCH; ++m) {
+        kk[m] = *reinterpret_cast<const f4 *>(lds + L::kOff + colof(m));
+        qq[m] = *reinterpret_cast<const f4 *>(lds + L::qOff + colof(m));
+        if constexpr (VAR == VAR_KDA)
+            ee[m] = *reinterpret_cast<const f4 *>(lds + L::eOff + colof(m));
+    }
+    float vr[RPL];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i)
+        vr[i] = lds[L::vOff + wave * R + rs * RPL + i];
+
+    // column group m of a row (half m % 2 of chunk m / 2), widened, decayed
+    auto widen = [&](const u4 &x, int m) -> f4 {
+        const unsigned a = (m % 2) ? x.z : x.x, c = (m % 2) ? x.w : x.y;
+        f4 s = {__uint_as_float(a << 16), __uint_as_float(a & 0xffff0000u),
+                __uint_as_float(c << 16), __uint_as_float(c & 0xffff0000u)};
+        if constexpr (VAR == VAR_KDA)
+            s *= ee[m];
+        else
+            s *= decay;
+        return s;
+    };
+
+    const BufRsrc dst = make_rsrc(
+        pool + ((w < 0 ? 0 : w) * p.sp_slot + hv * p.sp_head) * ES,
+        tile_bytes);
+    float mine = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+        float u = 0.f, wq = 0.f;
+#pragma unroll
+        for (int m = 0; m < 2 * NCH; ++m) {
+            const f4 s = widen(P[i][m / 2], m);
+            if constexpr (VAR != VAR_LA) {
+                u = fmaf(s.x, kk[m].x, u);
+                u = fmaf(s.y, kk[m].y, u);
+                u = fmaf(s.z, kk[m].z, u);
+                u = fmaf(s.w, kk[m].w, u);
+            }
+            wq = fmaf(s.x, qq[m].x, wq);
+            wq = fmaf(s.y, qq[m].y, wq);
+            wq = fmaf(s.z, qq[m].z, wq);
+            wq = fmaf(s.w, qq[m].w, wq);
+        }
+        wq = sum8(wq);
+        float c;
+        if constexpr (VAR == VAR_LA) {
+            c = vr[i];
+        } else {
+            u = sum8(u);
+            c = beta * (vr[i] - u);
+        }
+        mine = (c8 == i) ? fmaf(c, kq, wq) : mine;
+
+        if (w >= 0) {  // S <- decayed S + c k^T, rounded once, row i stored
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) {
+                f4 lo = widen(P[i][j], 2 * j), hi = widen(P[i][j], 2 * j + 1);
+                lo.x = fmaf(c, kk[2 * j].x, lo.x);
+                lo.y = fmaf(c, kk[2 * j].y, lo.y);
+                lo.z = fmaf(c, kk[2 * j].z, lo.z);
+                lo.w = fmaf(c, kk[2 * j].w, lo.w);
+                hi.x = fmaf(c, kk[2 * j + 1].x, hi.x);
+                hi.y = fmaf(c, kk[2 * j + 1].y, hi.y);
+                hi.z = fmaf(c, kk[2 * j + 1].z, hi.z);
+                hi.w = fmaf(c, kk[2 * j + 1].w, hi.w);
+                u4 h;
+                h.x = StateIO<true>::pack(lo.x, lo.y);
+                h.y = StateIO<true>::pack(lo.z, lo.w);
+                h.z = StateIO<true>::pack(hi.x, hi.y);
+                h.w = StateIO<true>::pack(hi.z, hi.w);
+                store_b128(h, dst, lane_off + j * 128u,
+                           (wave * R + i * 8) * row_bytes);
+            }
+        }
+    }
+    store_out<BF16OUT>(p.out, oidx, mine);
+}
+
 struct ReplayParams {
     int32_t B, T, HV;
     int32_t pad_;
@@ -847,6 +1018,26 @@ KernelFn pick_dtype(bool bf16_in, bool bf16_out, bool bf16_state, bool rec)
                       : pick_io<VAR, K, V, false, false>(bf16_in, bf16_out);
 }
 
+template <int VAR, int K, int V>
+KernelFn pick_packed(bool bi, bool bo)
+{
+    if (bi)
+        return bo ? decode_packed_kernel<VAR, K, V, true, true>
+                  : decode_packed_kernel<VAR, K, V, true, false>;
+    return bo ? decode_packed_kernel<VAR, K, V, false, true>
+              : decode_packed_kernel<VAR, K, V, false, false>;
+}
+
+template <int VAR>
+KernelFn pick_packed(int K, int V, bool bi, bool bo)
+{
+    if (K == 128)
+        return V == 128 ? pick_packed<VAR, 128, 128>(bi, bo)
+                        : pick_packed<VAR, 128, 64>(bi, bo);
+    return V == 128 ? pick_packed<VAR, 64, 128>(bi, bo)
+                    : pick_packed<VAR, 64, 64>(bi, bo);
+}
+
 template <int VAR>
 KernelFn pick(int K, int V, bool bi, bool bo, bool bs, bool rec)
 {
@@ -1051,15 +1242,24 @@ la_status launch(const la_decode_args *a, void *stream, int var)
     const bool bi = a->qkv_dtype == LA_BF16, bo = a->out_dtype == LA_BF16;
     const bool bs = a->state_dtype == LA_BF16;
     const bool rec = a->factors != nullptr;
-    KernelFn fn = var == VAR_LA ? pick<VAR_LA>(a->K, a->V, bi, bo, bs, rec)
-                  : var == VAR_GDN
-                      ? pick<VAR_GDN>(a->K, a->V, bi, bo, bs, rec)
-                      : pick<VAR_KDA>(a->K, a->V, bi, bo, bs, rec);
+    // one token on a bf16 pool with no per-token writes: packed tile
+    const bool packed = bs && a->T == 1 && !a->inter && !a->token_slots &&
+                        !rec;
+    KernelFn fn;
+    if (packed)
+        fn = var == VAR_LA    ? pick_packed<VAR_LA>(a->K, a->V, bi, bo)
+             : var == VAR_GDN ? pick_packed<VAR_GDN>(a->K, a->V, bi, bo)
+                              : pick_packed<VAR_KDA>(a->K, a->V, bi, bo);
+    else
+        fn = var == VAR_LA    ? pick<VAR_LA>(a->K, a->V, bi, bo, bs, rec)
+             : var == VAR_GDN ? pick<VAR_GDN>(a->K, a->V, bi, bo, bs, rec)
+                              : pick<VAR_KDA>(a->K, a->V, bi, bo, bs, rec);
     const int chunk = a->T < kTokChunk ? a->T : kTokChunk;
     const size_t lds = static_cast<size_t>(chunk) *
                        lds_floats_per_token(var, a->K, a->V) * sizeof(float);
     const dim3 grid(static_cast<unsigned>(a->B) * a->HV);
-    const dim3 block((a->V / kRowsPerWave) * 64);
+    // 64 rows per wave in the packed kernel, kRowsPerWave otherwise
+    const dim3 block(packed ? a->V : (a->V / kRowsPerWave) * 64);
     void *kargs[] = {&p};
     const hipError_t e =
         hipLaunchKernel(reinterpret_cast<const void *>(fn), grid, block,

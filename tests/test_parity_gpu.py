@@ -13,6 +13,8 @@ Tolerances (max over a tensor of |gpu - oracle|):
   to bf16, on top of the tolerance above (the kernel computes in fp32 and
   rounds to nearest even only when it stores).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -752,6 +754,52 @@ def test_bf16_state_pool_paged():
                                       state_dtype=torch.bfloat16)
     got = gpu_run_paged(wl, table, accepted)
     check_paged(wl, table, accepted, got)
+
+
+@pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN, W.KDA])
+@pytest.mark.parametrize("K,V", SHAPES)
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16],
+                         ids=["f32", "bf16"])
+def test_bf16_state_one_token_packed(variant, K, V, dtype):
+    """One token on a bf16 pool with no per-token cache: the kernel that
+    keeps the tile packed in registers."""
+    seed = (3100 + 100 * [W.LIGHTNING, W.GDN, W.KDA].index(variant)
+            + 10 * SHAPES.index((K, V))
+            + (5 if dtype == torch.bfloat16 else 0))
+    wl = W.make("bf16t1", variant, B=5, T=1, H=2, HV=4, K=K, V=V,
+                pool_size=11, seed=seed, act_dtype=dtype, pool_std=0.1,
+                separate_write=True, write_skip=0.34,
+                state_dtype=torch.bfloat16)
+    run_and_check(wl)
+
+
+@pytest.mark.parametrize("mult", [1, 3])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16],
+                         ids=["out_f32", "out_bf16"])
+def test_bf16_state_one_token_packed_strided_and_padded(mult, out_dtype):
+    wl = W.make("bf16t1pad", W.KDA, B=6, T=1, H=2, HV=2, K=128, V=128,
+                pool_size=9, seed=3050 + mult, stride_mult=mult,
+                read_idx=[3, -1, 0, 8, -1, 5], write_idx=[1, 2, -1, 7, 4, -1],
+                state_dtype=torch.bfloat16, out_dtype=out_dtype)
+    got = run_and_check(wl)
+    assert not got["out"][1].any() and not got["out"][4].any()
+
+
+@pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN, W.KDA])
+@pytest.mark.parametrize("K,V", [(128, 128), (64, 128)])
+def test_bf16_state_packed_kernel_bit_identical_to_general(variant, K, V):
+    """The packed one-token kernel and the general kernel (which runs when a
+    per-token cache is asked for) do the same fp32 operations in the same
+    order, so outputs and stored states agree bit for bit."""
+    wl = W.make("bf16same", variant, B=7, T=1, H=2, HV=4, K=K, V=V,
+                pool_size=16, seed=3200 + [W.LIGHTNING, W.GDN,
+                                           W.KDA].index(variant),
+                separate_write=True, write_skip=0.3,
+                state_dtype=torch.bfloat16)
+    packed = gpu_run(wl)
+    general = gpu_run(dataclasses.replace(wl, inter=True))
+    assert torch.equal(_bits(packed["out"]), _bits(general["out"]))
+    assert torch.equal(_bits(packed["backing"]), _bits(general["backing"]))
 
 
 def test_bf16_state_roundtrip_is_exact_when_unchanged():
