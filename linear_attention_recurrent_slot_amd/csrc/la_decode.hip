@@ -38,6 +38,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <map>
+#include <mutex>
+
 #include "la_decode.h"
 
 namespace {
@@ -1048,6 +1051,33 @@ KernelFn pick(int K, int V, bool bi, bool bo, bool bs, bool rec)
                     : pick_dtype<VAR, 64, 64>(bi, bo, bs, rec);
 }
 
+// Workgroups of `fn` that the current device holds at once (compute units
+// times workgroups per unit), looked up once per device and kernel; 0 when
+// the runtime cannot say.
+int64_t resident_blocks(KernelFn fn, int block, size_t lds)
+{
+    static std::mutex mu;
+    static std::map<std::pair<int, const void *>, int64_t> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 0;
+    const auto key = std::make_pair(dev, reinterpret_cast<const void *>(fn));
+    std::lock_guard<std::mutex> lock(mu);
+    const auto it = cache.find(key);
+    if (it != cache.end())
+        return it->second;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
+                              dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void *>(fn), block, lds) !=
+            hipSuccess)
+        return 0;
+    const int64_t n = static_cast<int64_t>(cus) * per_cu;
+    cache[key] = n;
+    return n;
+}
+
 int lds_floats_per_token(int var, int K, int V)
 {
     return (var == VAR_KDA ? 3 : 2) * K + V + 4;
@@ -1198,11 +1228,6 @@ la_status launch(const la_decode_args *a, void *stream, int var)
     p.HV = a->HV;
     p.group = a->HV / a->H;
     p.flags = a->flags;
-    // Streaming (nontemporal) state loads, except where cached loads
-    // measured faster on MI355X: calls that also write the per-token cache,
-    // and delta-rule calls of one or two tokens.
-    p.stream_loads =
-        !(a->inter || a->token_slots || (var != VAR_LA && a->T <= 2));
     p.q = a->q;
     p.sq_b = a->sq.b;
     p.sq_t = a->sq.t;
@@ -1260,6 +1285,21 @@ la_status launch(const la_decode_args *a, void *stream, int var)
     const dim3 grid(static_cast<unsigned>(a->B) * a->HV);
     // 64 rows per wave in the packed kernel, kRowsPerWave otherwise
     const dim3 block(packed ? a->V : (a->V / kRowsPerWave) * 64);
+
+    // State-load cache policy, from measurements on MI355X: streaming
+    // (nontemporal) loads, except cached loads for calls that also write
+    // per-token states and for delta-rule calls of one or two tokens whose
+    // grid is more than 1.5 rounds of resident workgroups (small grids of
+    // those calls are faster streaming). The bf16 KDA one-token kernel
+    // measured faster streaming at every size.
+    bool nt = true;
+    if (a->inter || a->token_slots)
+        nt = false;
+    else if (var != VAR_LA && a->T <= 2 && !(packed && var == VAR_KDA)) {
+        const int64_t res = resident_blocks(fn, block.x, lds);
+        nt = res > 0 && 2 * static_cast<int64_t>(grid.x) <= 3 * res;
+    }
+    p.stream_loads = nt;
     void *kargs[] = {&p};
     const hipError_t e =
         hipLaunchKernel(reinterpret_cast<const void *>(fn), grid, block,
