@@ -59,10 +59,11 @@ def _load():
         lib.oracle_decode.argtypes = (
             [ctypes.c_int] * 8 + [dp] * 5 + [ctypes.c_int, dp, dp, ip, ip,
                                              dp, dp, ip, ctypes.c_int, ip,
-                                             dp])
+                                             dp, ip, ctypes.c_int])
         lib.oracle_replay.restype = ctypes.c_int
         lib.oracle_replay.argtypes = (
-            [ctypes.c_int] * 5 + [dp, ctypes.c_int, dp, dp, ip, ip, ip])
+            [ctypes.c_int] * 5 + [dp, ctypes.c_int, dp, dp, ip, ip, ip, ip,
+                                  ctypes.c_int])
         _lib = lib
     return _lib
 
@@ -92,7 +93,7 @@ def _ptr(a, ctype):
 
 def decode(variant, q, k, v, g, beta, pool, read_idx, write_idx=None,
            flags=0, inter=False, token_slots=None, num_accepted=None,
-           factors=False):
+           factors=False, cu_seqlens=None, max_tokens=None):
     """Run the fp64 recurrence.
 
     q, k: [B,T,H,K]; v: [B,T,HV,V]; g: Lightning [HV] decay factors or None,
@@ -101,6 +102,9 @@ def decode(variant, q, k, v, g, beta, pool, read_idx, write_idx=None,
     token_slots: optional [B, >=T] per-token slot table (then read_idx and
     write_idx are ignored and num_accepted [B] is required).
     factors: also return the per-token records [B,T,HV,2K+V] (a | k | err).
+    cu_seqlens: optional [B+1] offsets of a variable-length batch; then every
+    per-token array is token-packed ([total, ...] in place of [B, T, ...]) and
+    T is max_tokens (default: the longest request).
 
     Returns a dict with ``out`` [B,T,HV,V], ``pool`` (the pool after the
     call, float64) and ``inter`` ([B,T,HV,V,K] or None).
@@ -109,22 +113,38 @@ def decode(variant, q, k, v, g, beta, pool, read_idx, write_idx=None,
     g, beta = _f64(g), _f64(beta)
     pool_in = _f64(pool)
     ridx, widx = _i32(read_idx), _i32(write_idx)
-    B, T, H, K = q.shape
-    HV, V = v.shape[2], v.shape[3]
+    cu = _i32(cu_seqlens)
+    if cu is not None:
+        # token-packed: view [total, ...] as [1, total, ...] for the checks
+        B = cu.shape[0] - 1
+        total = q.shape[0]
+        T = (int(max_tokens) if max_tokens is not None
+             else max(1, int(np.max(np.diff(cu))) if B > 0 else 1))
+        lead = (total,)
+        H, K = q.shape[1], q.shape[2]
+        HV, V = v.shape[1], v.shape[2]
+        if k.shape != q.shape or v.shape[0] != total:
+            raise ValueError("q/k/v shapes disagree")
+    else:
+        B, T, H, K = q.shape
+        HV, V = v.shape[2], v.shape[3]
+        total = 0
+        lead = (B, T)
+        if k.shape != q.shape or v.shape[:2] != (B, T):
+            raise ValueError("q/k/v shapes disagree")
     pool_size = pool_in.shape[0]
-    if k.shape != q.shape or v.shape[:2] != (B, T):
-        raise ValueError("q/k/v shapes disagree")
     if pool_in.shape[1:] != (HV, V, K):
         raise ValueError("pool shape %s != [pool_size,%d,%d,%d]"
                          % (pool_in.shape, HV, V, K))
-    if ridx.shape != (B,) or (widx is not None and widx.shape != (B,)):
+    if token_slots is None and (ridx is None or ridx.shape != (B,) or (
+            widx is not None and widx.shape != (B,))):
         raise ValueError("index shape")
     if variant != LIGHTNING and (g is None or beta is None):
         raise ValueError("GDN/KDA need g and beta")
-    expect_g = {LIGHTNING: (HV,), GDN: (B, T, HV), KDA: (B, T, HV, K)}
+    expect_g = {LIGHTNING: (HV,), GDN: lead + (HV,), KDA: lead + (HV, K)}
     if g is not None and g.shape != expect_g[variant]:
         raise ValueError("g shape %s != %s" % (g.shape, expect_g[variant]))
-    if beta is not None and variant != LIGHTNING and beta.shape != (B, T, HV):
+    if beta is not None and variant != LIGHTNING and beta.shape != lead + (HV,):
         raise ValueError("beta shape")
     slots = _i32(token_slots)
     acc = _i32(num_accepted)
@@ -139,9 +159,9 @@ def decode(variant, q, k, v, g, beta, pool, read_idx, write_idx=None,
         widx = None
     pool_out = pool_in.copy()
     # NaN until the oracle writes it: a position it skips cannot pass as 0
-    out = np.full((B, T, HV, V), np.nan, dtype=np.float64)
-    inter_a = np.zeros((B, T, HV, V, K), dtype=np.float64) if inter else None
-    fac = (np.full((B, T, HV, 2 * K + V), np.nan, dtype=np.float64)
+    out = np.full(lead + (HV, V), np.nan, dtype=np.float64)
+    inter_a = np.zeros(lead + (HV, V, K), dtype=np.float64) if inter else None
+    fac = (np.full(lead + (HV, 2 * K + V), np.nan, dtype=np.float64)
            if factors else None)
     dp = ctypes.c_double
     rc = _load().oracle_decode(
@@ -151,21 +171,31 @@ def decode(variant, q, k, v, g, beta, pool, read_idx, write_idx=None,
         _ptr(pool_in, dp), _ptr(pool_out, dp), _ptr(ridx, ctypes.c_int32),
         _ptr(widx, ctypes.c_int32), _ptr(out, dp), _ptr(inter_a, dp),
         _ptr(slots, ctypes.c_int32), stride, _ptr(acc, ctypes.c_int32),
-        _ptr(fac, dp))
+        _ptr(fac, dp), _ptr(cu, ctypes.c_int32), total)
     if rc != 0:
         raise ValueError("oracle_decode rejected its arguments (rc=%d)" % rc)
     return {"out": out, "pool": pool_out, "inter": inter_a, "factors": fac}
 
 
-def replay(factors, pool, read_idx, write_idx, num_tokens):
+def replay(factors, pool, read_idx, write_idx, num_tokens, cu_seqlens=None,
+           max_tokens=None):
     """Rebuild states from factor records [B,T,HV,2K+V]: request b starts
     from pool[read_idx[b]] and applies its first num_tokens[b] records;
-    the result goes to write_idx[b] (None: the read slot). Returns the pool
-    after the call (float64)."""
+    the result goes to write_idx[b] (None: the read slot). With cu_seqlens
+    the records are token-packed [total,HV,2K+V]. Returns the pool after the
+    call (float64)."""
     fac = _f64(factors)
     pool_in = _f64(pool)
     ridx, widx, ntok = _i32(read_idx), _i32(write_idx), _i32(num_tokens)
-    B, T, HV, R = fac.shape
+    cu = _i32(cu_seqlens)
+    total = 0
+    if cu is not None:
+        B = cu.shape[0] - 1
+        total, HV, R = fac.shape
+        T = (int(max_tokens) if max_tokens is not None
+             else max(1, int(np.max(np.diff(cu))) if B > 0 else 1))
+    else:
+        B, T, HV, R = fac.shape
     V, K = pool_in.shape[2], pool_in.shape[3]
     if R != 2 * K + V or pool_in.shape[1] != HV:
         raise ValueError("factor records do not match the pool")
@@ -178,7 +208,8 @@ def replay(factors, pool, read_idx, write_idx, num_tokens):
                                pool_in.shape[0], _ptr(pool_in, dp),
                                _ptr(pool_out, dp), _ptr(ridx, ctypes.c_int32),
                                _ptr(widx, ctypes.c_int32),
-                               _ptr(ntok, ctypes.c_int32))
+                               _ptr(ntok, ctypes.c_int32),
+                               _ptr(cu, ctypes.c_int32), total)
     if rc != 0:
         raise ValueError("oracle_replay rejected its arguments (rc=%d)" % rc)
     return pool_out

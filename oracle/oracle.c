@@ -65,6 +65,16 @@
  * KDA factors, or the GDN/Lightning scalar repeated K times), k_t the key as
  * used (after l2norm) and err_t the rank-1 coefficient: beta (v - S k) for
  * the delta rules, v for Lightning. oracle_replay applies n such records.
+ *
+ * Variable-length batches (aiter KDA page, summary: the decode kernel takes
+ * varlen batches; the pages give no layout): with cumulative offsets
+ * cu_seqlens[B + 1], request b owns tokens cu_seqlens[b] .. cu_seqlens[b+1]-1
+ * of token-packed activations, i.e. T_b = cu_seqlens[b+1] - cu_seqlens[b]
+ * tokens, and every per-token array (q, k, v, g, beta, out, inter, factors) is
+ * indexed by that flat token number instead of (b, t). T is then an upper
+ * bound on T_b. A request with T_b = 0 runs no token: its state is written to
+ * its write slot unchanged. With a slot table, the accepted count must lie in
+ * [1, T_b].
  */
 #include <math.h>
 #include <stddef.h>
@@ -116,6 +126,9 @@ static double lightning_decay(int head, int num_heads)
  *   slots     [B][slots_stride] per-token slot table, or NULL; when given,
  *             read_idx and write_idx are ignored and accepted[B] is used
  *   factors   [B][T][HV][2K + V] per-token records, or NULL
+ *   cu_seqlens  NULL, or [B + 1] non-decreasing offsets in [0, total] with
+ *             cu_seqlens[b+1] - cu_seqlens[b] <= T; then every [B][T] pair
+ *             of dimensions above is one [total] token dimension
  */
 int oracle_decode(int variant, int B, int T, int H, int HV, int K, int V,
                   int flags, const double *q, const double *k, const double *v,
@@ -123,10 +136,17 @@ int oracle_decode(int variant, int B, int T, int H, int HV, int K, int V,
                   const double *pool_in, double *pool_out,
                   const int32_t *read_idx, const int32_t *write_idx,
                   double *out, double *inter, const int32_t *slots,
-                  int slots_stride, const int32_t *accepted, double *factors)
+                  int slots_stride, const int32_t *accepted, double *factors,
+                  const int32_t *cu_seqlens, int total)
 {
     if (B < 0 || T < 1 || H < 1 || HV < 1 || K < 1 || V < 1 || HV % H != 0)
         return -1;
+    if (cu_seqlens)
+        for (int b = 0; b < B; ++b)
+            if (cu_seqlens[b] < 0 || cu_seqlens[b + 1] < cu_seqlens[b] ||
+                cu_seqlens[b + 1] > total ||
+                cu_seqlens[b + 1] - cu_seqlens[b] > T)
+                return -1;
     if (variant != ORACLE_LIGHTNING && variant != ORACLE_GDN &&
         variant != ORACLE_KDA)
         return -1;
@@ -146,11 +166,15 @@ int oracle_decode(int variant, int B, int T, int H, int HV, int K, int V,
     const int group = HV / H;
 
     for (int b = 0; b < B; ++b) {
+        /* tokens of request b and the flat number of its first token */
+        const int Tb = cu_seqlens ? cu_seqlens[b + 1] - cu_seqlens[b] : T;
+        const size_t tok0 = cu_seqlens ? (size_t)cu_seqlens[b] : (size_t)b * T;
         int r, w;
         if (slots) {
             const int na = accepted[b];
-            r = (na >= 1 && na <= T) ? slots[(size_t)b * slots_stride + na - 1]
-                                     : -1;
+            r = (na >= 1 && na <= Tb)
+                    ? slots[(size_t)b * slots_stride + na - 1]
+                    : -1;
             w = -1; /* per-token writes instead of one final write */
             for (int t = 0; t < T; ++t)
                 if (slots[(size_t)b * slots_stride + t] >= pool_size) {
@@ -172,19 +196,19 @@ int oracle_decode(int variant, int B, int T, int H, int HV, int K, int V,
         for (int hv = 0; hv < HV; ++hv) {
             if (r < 0) {
                 /* padded request: zero outputs, nothing else */
-                for (int t = 0; t < T; ++t)
+                for (int t = 0; t < Tb; ++t)
                     for (int i = 0; i < V; ++i)
-                        out[(((size_t)b * T + t) * HV + hv) * V + i] = 0.0;
+                        out[((tok0 + t) * HV + hv) * V + i] = 0.0;
                 continue;
             }
             const int h = hv / group;
             memcpy(S, pool_in + ((size_t)r * HV + hv) * tile,
                    tile * sizeof(double));
 
-            for (int t = 0; t < T; ++t) {
-                const size_t qk_off = (((size_t)b * T + t) * H + h) * K;
-                const size_t v_off = (((size_t)b * T + t) * HV + hv) * V;
-                const size_t bt = ((size_t)b * T + t) * HV + hv;
+            for (int t = 0; t < Tb; ++t) {
+                const size_t qk_off = ((tok0 + t) * H + h) * K;
+                const size_t v_off = ((tok0 + t) * HV + hv) * V;
+                const size_t bt = (tok0 + t) * HV + hv;
                 memcpy(qv, q + qk_off, (size_t)K * sizeof(double));
                 memcpy(kv, k + qk_off, (size_t)K * sizeof(double));
                 if (flags & ORACLE_L2NORM_QK) {
@@ -278,15 +302,23 @@ int oracle_decode(int variant, int B, int T, int H, int HV, int K, int V,
  * S <- S diag(a_t) + err_t k_t^T; then write S to pool_out[w, hv] with
  * w = write_idx ? write_idx[b] : r when w >= 0. Requests with a negative
  * read slot or ntok outside [0, T] are skipped.
- * factors: [B][T][HV][2K + V]. Returns 0, or -1 on a bad argument.
+ * factors: [B][T][HV][2K + V]; with cu_seqlens (as in oracle_decode),
+ * [total][HV][2K + V] by flat token number, and ntok[b] must lie in
+ * [0, T_b]. Returns 0, or -1 on a bad argument.
  */
 int oracle_replay(int B, int T, int HV, int K, int V, const double *factors,
                   int pool_size, const double *pool_in, double *pool_out,
                   const int32_t *read_idx, const int32_t *write_idx,
-                  const int32_t *ntok)
+                  const int32_t *ntok, const int32_t *cu_seqlens, int total)
 {
     if (B < 0 || T < 1 || HV < 1 || K < 1 || V < 1)
         return -1;
+    if (cu_seqlens)
+        for (int b = 0; b < B; ++b)
+            if (cu_seqlens[b] < 0 || cu_seqlens[b + 1] < cu_seqlens[b] ||
+                cu_seqlens[b + 1] > total ||
+                cu_seqlens[b + 1] - cu_seqlens[b] > T)
+                return -1;
     const size_t tile = (size_t)V * (size_t)K;
     const size_t rsz = (size_t)(2 * K + V);
     double *S = (double *)malloc(tile * sizeof(double));
@@ -296,18 +328,19 @@ int oracle_replay(int B, int T, int HV, int K, int V, const double *factors,
         const int r = read_idx[b];
         const int w = write_idx ? write_idx[b] : r;
         const int n = ntok[b];
+        const int Tb = cu_seqlens ? cu_seqlens[b + 1] - cu_seqlens[b] : T;
+        const size_t tok0 = cu_seqlens ? (size_t)cu_seqlens[b] : (size_t)b * T;
         if (r >= pool_size || w >= pool_size) {
             free(S);
             return -1;
         }
-        if (r < 0 || n < 0 || n > T)
+        if (r < 0 || n < 0 || n > Tb)
             continue;
         for (int hv = 0; hv < HV; ++hv) {
             memcpy(S, pool_in + ((size_t)r * HV + hv) * tile,
                    tile * sizeof(double));
             for (int t = 0; t < n; ++t) {
-                const double *rec =
-                    factors + (((size_t)b * T + t) * HV + hv) * rsz;
+                const double *rec = factors + ((tok0 + t) * HV + hv) * rsz;
                 const double *a = rec, *kk = rec + K, *err = rec + 2 * K;
                 for (int i = 0; i < V; ++i)
                     for (int j = 0; j < K; ++j)

@@ -28,7 +28,7 @@ MUTATIONS = {
     "lightning_decay_index": ("pow(2.0, -8.0 * (double)(head + 1)",
                               "pow(2.0, -8.0 * (double)(head)"),
     "padded_output_not_zeroed": (
-        "out[(((size_t)b * T + t) * HV + hv) * V + i] = 0.0;", ";"),
+        "out[((tok0 + t) * HV + hv) * V + i] = 0.0;", ";"),
     "beta_sigmoid_missing": ("bb = 1.0 / (1.0 + exp(-bb));", "bb = bb;"),
     "output_reads_key": ("o += S[(size_t)i * K + j] * qv[j];",
                          "o += S[(size_t)i * K + j] * kv[j];"),
@@ -38,8 +38,8 @@ MUTATIONS = {
         ": exp(g[bt * (size_t)K + j])) * kv[j];"),
     "l2norm_skipped_for_k": ("l2_normalise(kv, K);", ";"),
     "paged_seed_off_by_one": (
-        "r = (na >= 1 && na <= T) ? slots[(size_t)b * slots_stride + na - 1]",
-        "r = (na >= 1 && na <= T) ? slots[(size_t)b * slots_stride + na % T]"),
+        "? slots[(size_t)b * slots_stride + na - 1]",
+        "? slots[(size_t)b * slots_stride + na % T]"),
     "replay_decay_after_update": (
         "S[(size_t)i * K + j] * a[j] + err[i] * kk[j];",
         "(S[(size_t)i * K + j] + err[i] * kk[j]) * a[j];"),
@@ -48,6 +48,17 @@ MUTATIONS = {
     "paged_write_wrong_token": (
         "const int ws = slots[(size_t)b * slots_stride + t];",
         "const int ws = slots[(size_t)b * slots_stride + T - 1 - t];"),
+    "varlen_token_base_ignored": (
+        "const size_t tok0 = cu_seqlens ? (size_t)cu_seqlens[b] : (size_t)b * T;",
+        "const size_t tok0 = (size_t)b * T;"),
+    "varlen_accepted_bound_is_T": ("(na >= 1 && na <= Tb)",
+                                   "(na >= 1 && na <= T)"),
+    "varlen_replay_dense_records": (
+        "const double *rec = factors + ((tok0 + t) * HV + hv) * rsz;",
+        "const double *rec = factors + (((size_t)b * T + t) * HV + hv) * rsz;"),
+    "varlen_empty_request_skips_write": (
+        "            if (w >= 0)\n                memcpy(pool_out + ((size_t)w * HV + hv) * tile, S,",
+        "            if (w >= 0 && Tb > 0)\n                memcpy(pool_out + ((size_t)w * HV + hv) * tile, S,"),
 }
 
 

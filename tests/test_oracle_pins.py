@@ -569,3 +569,155 @@ def test_replay_skips_and_bounds():
     np.testing.assert_array_equal(out[3], c["pool"][0])
     for s in (0, 1, 2, 4, 5):
         np.testing.assert_array_equal(out[s], c["pool"][s])
+
+
+# ---------------------------------------------------- variable-length batches
+
+
+def _pack(x, lengths, T):
+    """[B, T, ...] -> token-packed [sum(lengths), ...] (first lengths[b] of
+    each request)."""
+    return np.concatenate([x[b, :n] for b, n in enumerate(lengths)], axis=0)
+
+
+def _varlen_case(rng, variant, lengths, T, H=1, HV=2, K=5, V=4, pool_size=9):
+    B = len(lengths)
+    c = _random_case(rng, variant, B=B, T=T, H=H, HV=HV, K=K, V=V,
+                     pool_size=pool_size)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    packed = {n: _pack(c[n], lengths, T) for n in ("q", "k", "v")}
+    packed["g"] = c["g"] if variant == oracle.LIGHTNING else _pack(
+        c["g"], lengths, T)
+    packed["beta"] = None if c["beta"] is None else _pack(c["beta"], lengths, T)
+    return c, packed, cu
+
+
+@pytest.mark.parametrize("variant", [oracle.LIGHTNING, oracle.GDN, oracle.KDA])
+def test_varlen_equal_lengths_equals_dense(variant):
+    """Offsets 0, T, 2T, ... over the packed tokens are the dense batch."""
+    rng = np.random.default_rng(200 + variant)
+    T = 3
+    c, p, cu = _varlen_case(rng, variant, [T, T, T], T)
+    flags = 0 if variant == oracle.LIGHTNING else oracle.BETA_LOGIT
+    ridx, widx = [4, 0, 7], [1, 8, 2]
+    dense = oracle.decode(variant, c["q"], c["k"], c["v"], c["g"], c["beta"],
+                          c["pool"], ridx, widx, flags=flags, inter=True,
+                          factors=True)
+    var = oracle.decode(variant, p["q"], p["k"], p["v"], p["g"], p["beta"],
+                        c["pool"], ridx, widx, flags=flags, inter=True,
+                        factors=True, cu_seqlens=cu)
+    np.testing.assert_array_equal(var["out"], dense["out"].reshape(9, 2, 4))
+    np.testing.assert_array_equal(var["pool"], dense["pool"])
+    np.testing.assert_array_equal(var["inter"],
+                                  dense["inter"].reshape((9,) + dense["inter"].shape[2:]))
+    np.testing.assert_array_equal(var["factors"],
+                                  dense["factors"].reshape((9,) + dense["factors"].shape[2:]))
+
+
+@pytest.mark.parametrize("variant", [oracle.LIGHTNING, oracle.GDN, oracle.KDA])
+def test_varlen_equals_separate_requests(variant):
+    """A variable-length batch is its requests run one by one, each with its
+    own token count; a request of zero tokens copies its read state to its
+    write slot and produces no output."""
+    rng = np.random.default_rng(210 + variant)
+    lengths, T = [2, 0, 4, 1], 4
+    c, p, cu = _varlen_case(rng, variant, lengths, T, pool_size=10)
+    flags = 0 if variant == oracle.LIGHTNING else (
+        oracle.BETA_LOGIT | oracle.L2NORM_QK)
+    ridx, widx = [3, 6, 0, 9], [5, 1, 0, 2]
+    var = oracle.decode(variant, p["q"], p["k"], p["v"], p["g"], p["beta"],
+                        c["pool"], ridx, widx, flags=flags, inter=True,
+                        factors=True, cu_seqlens=cu, max_tokens=T)
+    assert var["out"].shape[0] == sum(lengths)
+    want_pool = c["pool"].copy()
+    for b, n in enumerate(lengths):
+        if n == 0:
+            want_pool[widx[b]] = c["pool"][ridx[b]]
+            continue
+        sl = slice(0, n)
+        g = c["g"] if variant == oracle.LIGHTNING else c["g"][b:b + 1, sl]
+        beta = None if c["beta"] is None else c["beta"][b:b + 1, sl]
+        one = oracle.decode(variant, c["q"][b:b + 1, sl], c["k"][b:b + 1, sl],
+                            c["v"][b:b + 1, sl], g, beta, c["pool"],
+                            [ridx[b]], [widx[b]], flags=flags, inter=True,
+                            factors=True)
+        rows = slice(cu[b], cu[b + 1])
+        np.testing.assert_array_equal(var["out"][rows], one["out"][0])
+        np.testing.assert_array_equal(var["inter"][rows], one["inter"][0])
+        np.testing.assert_array_equal(var["factors"][rows], one["factors"][0])
+        want_pool[widx[b]] = one["pool"][widx[b]]
+    np.testing.assert_array_equal(var["pool"], want_pool)
+
+
+def test_varlen_padding_and_paged_slots():
+    """Padding (negative read slot) zeroes only the request's own packed
+    outputs; with a slot table the accepted count is checked against the
+    request's own token count."""
+    rng = np.random.default_rng(220)
+    lengths, T = [3, 1, 2], 3
+    c, p, cu = _varlen_case(rng, oracle.GDN, lengths, T, pool_size=12)
+    res = oracle.decode(oracle.GDN, p["q"], p["k"], p["v"], p["g"], p["beta"],
+                        c["pool"], [2, -1, 5], None, cu_seqlens=cu)
+    assert not res["out"][3].any()
+    assert np.isfinite(res["out"]).all() and res["out"][[0, 1, 2, 4, 5]].any()
+    table = np.array([[0, 1, 2, -1], [3, 7, -1, -1], [4, 6, -1, -1]],
+                     dtype=np.int32)
+    # request 1 has one token, so an accepted count of 2 makes it padding
+    # (its table entry 1 is a valid slot, which it must not read)
+    acc = np.array([2, 2, 1], dtype=np.int32)
+    paged = oracle.decode(oracle.GDN, p["q"], p["k"], p["v"], p["g"],
+                          p["beta"], c["pool"], None, token_slots=table,
+                          num_accepted=acc, cu_seqlens=cu, inter=True)
+    assert not paged["out"][3].any()
+    for b, n in enumerate(lengths):
+        if b == 1:
+            continue
+        rows = slice(cu[b], cu[b + 1])
+        one = oracle.decode(oracle.GDN, c["q"][b:b + 1, :n],
+                            c["k"][b:b + 1, :n], c["v"][b:b + 1, :n],
+                            c["g"][b:b + 1, :n], c["beta"][b:b + 1, :n],
+                            c["pool"], None, token_slots=table[b:b + 1],
+                            num_accepted=acc[b:b + 1], inter=True)
+        np.testing.assert_array_equal(paged["out"][rows], one["out"][0])
+        np.testing.assert_array_equal(paged["inter"][rows], one["inter"][0])
+        for t in range(n):
+            s = table[b, t]
+            np.testing.assert_array_equal(paged["pool"][s], one["pool"][s])
+    np.testing.assert_array_equal(paged["pool"][3], c["pool"][3])
+    np.testing.assert_array_equal(paged["pool"][7], c["pool"][7])
+
+
+def test_varlen_replay_equals_per_request_cache():
+    rng = np.random.default_rng(230)
+    lengths, T = [3, 0, 2], 3
+    c, p, cu = _varlen_case(rng, oracle.KDA, lengths, T, pool_size=8)
+    ridx = [1, 4, 6]
+    res = oracle.decode(oracle.KDA, p["q"], p["k"], p["v"], p["g"], p["beta"],
+                        c["pool"], ridx, [-1, -1, -1], inter=True,
+                        factors=True, cu_seqlens=cu)
+    ntok = [2, 0, 2]
+    out = oracle.replay(res["factors"], c["pool"], ridx, [0, 2, 3], ntok,
+                        cu_seqlens=cu)
+    np.testing.assert_allclose(out[0], res["inter"][cu[0] + 1], rtol=0,
+                               atol=1e-13)
+    np.testing.assert_array_equal(out[2], c["pool"][4])
+    np.testing.assert_allclose(out[3], res["inter"][cu[2] + 1], rtol=0,
+                               atol=1e-13)
+    # a count beyond the request's own tokens skips it
+    out = oracle.replay(res["factors"], c["pool"], ridx, [0, 2, 3], [1, 1, 3],
+                        cu_seqlens=cu)
+    np.testing.assert_array_equal(out[2], c["pool"][2])
+    np.testing.assert_array_equal(out[3], c["pool"][3])
+
+
+@pytest.mark.parametrize("cu", [[0, 2, 1, 3], [1, 2, 3, 5], [0, 4, 4, 5],
+                                [-1, 0, 2, 3]])
+def test_varlen_rejects_bad_offsets(cu):
+    """Offsets must be non-decreasing, inside [0, total], and no request may
+    hold more than T tokens."""
+    rng = np.random.default_rng(240)
+    c, p, _ = _varlen_case(rng, oracle.GDN, [1, 1, 2], 2, pool_size=6)
+    with pytest.raises(ValueError):
+        oracle.decode(oracle.GDN, p["q"][:4], p["k"][:4], p["v"][:4],
+                      p["g"][:4], p["beta"][:4], c["pool"], [0, 1, 2],
+                      cu_seqlens=np.array(cu, dtype=np.int32), max_tokens=3)
