@@ -86,11 +86,13 @@ def make_copies(wl, R, dev):
             for name in ("q", "k", "v"):
                 t = getattr(d, name)
                 t.copy_(torch.randn(t.shape, generator=gen, device=dev))
+        # (B, T), or the packed token count of a variable-length batch
+        lead = tuple(wl.q.shape[:-2])
         inter = None
         if wl.inter:
-            inter = torch.empty((wl.B, wl.T, wl.HV, wl.V, wl.K),
+            inter = torch.empty(lead + (wl.HV, wl.V, wl.K),
                                 dtype=wl.backing.dtype, device=dev)
-        out = torch.empty((wl.B, wl.T, wl.HV, wl.V), dtype=wl.out_dtype,
+        out = torch.empty(lead + (wl.HV, wl.V), dtype=wl.out_dtype,
                           device=dev)
         if wl.replay_tokens is not None:
             d.records = torch.empty((wl.B, wl.T, wl.HV, wl.record_floats),
@@ -111,10 +113,11 @@ def make_call(wl, d, inter, out, stream):
     if wl.variant != "lightning":
         flags = ((bnd.LA_F_L2NORM_QK if wl.l2norm else 0)
                  | (bnd.LA_F_BETA_LOGIT if wl.beta_logit else 0))
+    vl = dict(cu_seqlens=d.cu_seqlens, max_tokens=wl.T)
     if d.token_slots is not None:
         args = bnd.build_args(wl.variant, d.q, d.k, d.v, d.g, d.beta,
                               d.pool(), None, None, out, inter, flags,
-                              d.token_slots, d.num_accepted)
+                              d.token_slots, d.num_accepted, **vl)
     elif d.replay_tokens is not None:
         # verify: no writeback, one update record per token
         args = bnd.build_args(wl.variant, d.q, d.k, d.v, d.g, d.beta,
@@ -125,7 +128,7 @@ def make_call(wl, d, inter, out, stream):
     else:
         args = bnd.build_args(wl.variant, d.q, d.k, d.v, d.g, d.beta,
                               d.pool(), d.read_idx, d.write_idx, out, inter,
-                              flags)
+                              flags, **vl)
     entry = getattr(bnd.lib(), {"lightning": "la_decode",
                                 "gdn": "gdn_decode_mtp",
                                 "kda": "kda_decode_mtp"}[wl.variant])
@@ -190,19 +193,25 @@ def cpu_baseline(wl, seconds):
     flags = ((oracle.L2NORM_QK if wl.l2norm else 0)
              | (oracle.BETA_LOGIT if wl.beta_logit else 0))
 
+    counts = wl.counts()
+
     def run(nb):
         sel = slice(0, nb)
-        g = wl.g if wl.variant == "lightning" else wl.g[sel]
-        beta = None if wl.beta is None else wl.beta[sel]
+        extra = {}
+        tsel = sel  # per-token rows of the first nb requests
+        if wl.cu_seqlens is not None:
+            tsel = slice(0, sum(counts[:nb]))
+            extra = dict(cu_seqlens=wl.cu_seqlens[: nb + 1], max_tokens=wl.T)
+        g = wl.g if wl.variant == "lightning" else wl.g[tsel]
+        beta = None if wl.beta is None else wl.beta[tsel]
         widx = None if wl.write_idx is None else wl.write_idx[sel]
         t0 = time.perf_counter()
-        paged = {}
         if wl.token_slots is not None:
-            paged = dict(token_slots=wl.token_slots[sel],
+            extra.update(token_slots=wl.token_slots[sel],
                          num_accepted=wl.num_accepted[sel])
-        oracle.decode(variant, wl.q[sel], wl.k[sel], wl.v[sel], g, beta,
+        oracle.decode(variant, wl.q[tsel], wl.k[tsel], wl.v[tsel], g, beta,
                       wl.pool(), wl.read_idx[sel], widx, flags=flags,
-                      inter=wl.inter, **paged)
+                      inter=wl.inter, **extra)
         return time.perf_counter() - t0
 
     nb = wl.B
@@ -213,12 +222,12 @@ def cpu_baseline(wl, seconds):
     while spent < seconds:
         spent += run(nb)
         calls += 1
-        tokens += nb * wl.T
+        tokens += sum(counts[:nb])
     return {"value": tokens / spent, "unit": "tokens/s", "cores": 1,
             "kind": "oracle",
-            "sample": "%d calls of the fp64 oracle on %d of %d requests x %d "
-                      "token(s) of %s (pool conversion included), %.1f s"
-                      % (calls, nb, wl.B, wl.T, wl.name, spent)}
+            "sample": "%d calls of the fp64 oracle on %d of %d requests "
+                      "(%d tokens) of %s (pool conversion included), %.1f s"
+                      % (calls, nb, wl.B, sum(counts[:nb]), wl.name, spent)}
 
 
 def main():
@@ -277,7 +286,7 @@ def main():
 
     copy_gbps = None if args.no_copy_probe else copy_probe(dev, stream)
 
-    tokens = wl.B * wl.T
+    tokens = wl.tokens  # B T, or the packed tokens of a varlen batch
     achieved = per_call / (avg_launch_ms * 1e-3) / 1e9
     state_gbps = wl.state_bytes() / (avg_launch_ms * 1e-3) / 1e9
     traffic = read_traffic(wl.name)
@@ -303,6 +312,8 @@ def main():
                    "inter_cache": wl.inter,
                    "paged_slots": wl.token_slots is not None,
                    "spec_records_replay": wl.replay_tokens is not None,
+                   "varlen_tokens": (wl.tokens if wl.cu_seqlens is not None
+                                     else None),
                    "rotation": R},
         "roofline": {"bound": "hbm", "achieved": achieved,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",

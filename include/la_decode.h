@@ -20,7 +20,8 @@
  *   4. If w >= 0: pool[w, hv] = S, in place.
  *   With a per-token slot table (see la_decode_args), the seed slot is the
  *   last accepted token's entry and step 4 becomes a write after every
- *   token to that token's entry.
+ *   token to that token's entry. With cu_seqlens (a variable-length batch)
+ *   request b runs its own T_b tokens of token-packed inputs.
  *
  * Sources (page titles and sections):
  *  - "fix: wire h0_indices into Lightning Attention decode for state-pool
@@ -173,6 +174,26 @@ typedef struct la_decode_args {
      * from the seed state; 2K + V floats per token instead of V K. Written
      * for active requests only. */
     float *factors;
+
+    /* Variable-length batch (aiter KDA page, summary: the decode kernel takes
+     * varlen batches; the token-packed layout below is this library's
+     * reading), or NULL: cu_seqlens[B + 1] int32 offsets, contiguous.
+     * Request b owns tokens cu_seqlens[b] .. cu_seqlens[b+1] - 1 of
+     * token-packed per-token arrays and runs T_b = cu_seqlens[b+1] -
+     * cu_seqlens[b] tokens; T is an upper bound on every T_b. q, k, v, g,
+     * beta and out are then indexed by the flat token number through their
+     * t strides (their b strides are ignored); inter is
+     * [total_tokens, HV, V, K] and factors [total_tokens, HV, 2K + V], both
+     * contiguous. A request with T_b = 0 copies its read state to its write
+     * slot. With a slot table, num_accepted must lie in [1, T_b] (otherwise
+     * the request is padding). Device precondition (la_check_cu_seqlens
+     * checks it): 0 <= cu_seqlens[b] <= cu_seqlens[b+1] <= total_tokens and
+     * T_b <= T. A request that breaks it is skipped entirely: no output is
+     * written and neither the pool nor the cache is accessed. */
+    const int32_t *cu_seqlens;
+    int32_t total_tokens; /* rows of the token-packed arrays (cu_seqlens
+                             given), >= 0; ignored otherwise              */
+    int32_t reserved;     /* must be 0                                    */
 } la_decode_args;
 
 /* Arguments of la_replay. */
@@ -190,7 +211,13 @@ typedef struct la_replay_args {
     const int32_t *read_idx;    /* [B] seed slots; negative: skip request   */
     const int32_t *write_idx;   /* [B] or NULL (= read_idx); negative: skip */
     const int32_t *num_tokens;  /* [B] records to apply; a value outside
-                                   [0, T] skips the request                 */
+                                   [0, T] (with cu_seqlens: [0, T_b]) skips
+                                   the request                              */
+    const int32_t *cu_seqlens;  /* NULL, or [B + 1] offsets as in
+                                   la_decode_args: factors is then
+                                   [total_tokens, HV, 2K + V]               */
+    int32_t total_tokens;       /* with cu_seqlens, >= 0                    */
+    int32_t reserved;           /* must be 0                                */
 } la_replay_args;
 
 /* Lightning decode (cuLA page): S <- lambda_h S + v k^T, o = S q.
@@ -240,11 +267,20 @@ la_status la_check_token_slots(int32_t B, int32_t T, int32_t pool_size,
                                const int32_t *num_accepted,
                                int32_t *dev_result, void *stream);
 
+/* Debug validator of the variable-length offsets (same conventions as
+ * la_check_indices). Bits written to *dev_result:
+ *   1 = an offset outside [0, total_tokens],
+ *   2 = a request with a negative token count or more than T tokens.
+ * Requests flagged here are skipped by the decode and replay calls. */
+la_status la_check_cu_seqlens(int32_t B, int32_t T, int32_t total_tokens,
+                              const int32_t *cu_seqlens, int32_t *dev_result,
+                              void *stream);
+
 /* Static description of a status code; never NULL. */
 const char *la_status_string(la_status status);
 
 /* Library version as major * 100 + minor (2.00: state_dtype and paged
- * per-token slots in la_decode_args). */
+ * per-token slots in la_decode_args; 2.10: variable-length batches). */
 int32_t la_version(void);
 
 #ifdef __cplusplus

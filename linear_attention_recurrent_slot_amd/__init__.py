@@ -3,13 +3,14 @@
 Hand-written gfx950 HIP kernels behind a C ABI (include/la_decode.h), with a
 thin ctypes binding. Entry points: la_decode (Lightning), gdn_decode_mtp
 (gated delta rule), kda_decode_mtp (Kimi delta attention), replay (rebuild
-states from per-token update records), and the index validators
-check_indices and check_token_slots.
+states from per-token update records), and the validators check_indices,
+check_token_slots and check_cu_seqlens.
 """
-from ._binding import (DecodeArgs, LaDecodeError, ReplayArgs, check_indices,
-                       check_token_slots, gdn_decode_mtp, kda_decode_mtp,
-                       la_decode, lib, replay)
+from ._binding import (DecodeArgs, LaDecodeError, ReplayArgs,
+                       check_cu_seqlens, check_indices, check_token_slots,
+                       gdn_decode_mtp, kda_decode_mtp, la_decode, lib, replay)
 
-__all__ = ["DecodeArgs", "LaDecodeError", "ReplayArgs", "check_indices",
+__all__ = ["DecodeArgs", "LaDecodeError", "ReplayArgs", "check_cu_seqlens",
+           "check_indices",
            "check_token_slots", "gdn_decode_mtp", "kda_decode_mtp",
            "la_decode", "lib", "replay"]

@@ -59,6 +59,8 @@ class DecodeArgs(ctypes.Structure):
         ("token_slots_stride", ctypes.c_int64),
         ("num_accepted", ctypes.c_void_p),
         ("factors", ctypes.c_void_p),
+        ("cu_seqlens", ctypes.c_void_p),
+        ("total_tokens", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
 
@@ -71,6 +73,8 @@ class ReplayArgs(ctypes.Structure):
         ("factors", ctypes.c_void_p), ("pool", ctypes.c_void_p),
         ("sp", PoolStrides), ("read_idx", ctypes.c_void_p),
         ("write_idx", ctypes.c_void_p), ("num_tokens", ctypes.c_void_p),
+        ("cu_seqlens", ctypes.c_void_p),
+        ("total_tokens", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
 
@@ -108,6 +112,10 @@ def lib() -> ctypes.CDLL:
         L.la_check_token_slots.argtypes = [
             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
             ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.la_check_cu_seqlens.restype = ctypes.c_int
+        L.la_check_cu_seqlens.argtypes = [
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p]
         L.la_status_string.restype = ctypes.c_char_p
         L.la_status_string.argtypes = [ctypes.c_int]
         L.la_version.restype = ctypes.c_int32
@@ -141,13 +149,20 @@ def _dtype_code(t: torch.Tensor, what: str) -> int:
     raise TypeError("%s must be float32 or bfloat16, got %s" % (what, t.dtype))
 
 
-def _act(t: torch.Tensor, ndim: int, what: str):
-    if t.dim() != ndim:
-        raise ValueError("%s must have %d dims, got %s" % (what, ndim,
+def _act(t: torch.Tensor, ndim: int, what: str, packed: bool = False):
+    """Pointer and (b, t, h) strides of a per-token tensor: [B, T, ...], or
+    token-packed [total, ...] (packed=True: one dimension fewer, no b
+    stride)."""
+    nd = ndim - 1 if packed else ndim
+    if t.dim() != nd:
+        raise ValueError("%s must have %d dims, got %s" % (what, nd,
                                                            tuple(t.shape)))
-    if ndim == 4 and t.stride(3) != 1:
+    if ndim == 4 and t.stride(nd - 1) != 1:
         raise ValueError("%s: innermost stride must be 1" % what)
     s = t.stride()
+    if packed:
+        return ctypes.c_void_p(t.data_ptr()), ActStrides(
+            0, s[0], s[1] if nd > 1 else 0)
     return ctypes.c_void_p(t.data_ptr()), ActStrides(s[0], s[1], s[2])
 
 
@@ -181,13 +196,43 @@ def _factors(f, shape, dev):
     return ctypes.c_void_p(f.data_ptr())
 
 
+def _cu(cu_seqlens, max_tokens, dev):
+    """(B, T, total pointer args) of a varlen batch."""
+    if (cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1
+            or cu_seqlens.stride(0) != 1 or cu_seqlens.shape[0] < 1):
+        raise ValueError("cu_seqlens must be a contiguous 1-D int32 [B + 1] "
+                         "tensor")
+    if cu_seqlens.device != dev:
+        raise ValueError("cu_seqlens is on %s, pool on %s"
+                         % (cu_seqlens.device, dev))
+    B = cu_seqlens.shape[0] - 1
+    if max_tokens is None:  # reads the offsets back: a device sync
+        max_tokens = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) \
+            if B > 0 else 1
+    return B, max(1, int(max_tokens))
+
+
 def build_args(variant: str, q, k, v, g, beta, pool, read_idx, write_idx,
                out, inter, flags: int, token_slots=None,
-               num_accepted=None, factors=None) -> DecodeArgs:
-    if q.dim() != 4 or v.dim() != 4:
-        raise ValueError("q must be [B,T,H,K] and v [B,T,HV,V]")
-    B, T, H, K = q.shape
-    HV, V = v.shape[2], v.shape[3]
+               num_accepted=None, factors=None, cu_seqlens=None,
+               max_tokens=None) -> DecodeArgs:
+    vl = cu_seqlens is not None
+    if vl:
+        # token-packed: q, k [total, H, K], v [total, HV, V], ...
+        if q.dim() != 3 or v.dim() != 3:
+            raise ValueError("with cu_seqlens q must be [total,H,K] and v "
+                             "[total,HV,V]")
+        total, H, K = q.shape
+        HV, V = v.shape[1], v.shape[2]
+        B, T = _cu(cu_seqlens, max_tokens, pool.device)
+        lead = (total,)
+    else:
+        if q.dim() != 4 or v.dim() != 4:
+            raise ValueError("q must be [B,T,H,K] and v [B,T,HV,V]")
+        B, T, H, K = q.shape
+        HV, V = v.shape[2], v.shape[3]
+        total = 0
+        lead = (B, T)
     if (pool.dim() != 4 or pool.dtype not in (torch.float32, torch.bfloat16)
             or pool.stride(3) != 1):
         raise ValueError("pool must be a float32 or bfloat16 "
@@ -195,8 +240,8 @@ def build_args(variant: str, q, k, v, g, beta, pool, read_idx, write_idx,
                          "stride")
     # The library sees raw pointers: every extent it will index is checked
     # here against the tensors that back it.
-    want = {"k": (k, (B, T, H, K)), "v": (v, (B, T, HV, V)),
-            "out": (out, (B, T, HV, V))}
+    want = {"k": (k, lead + (H, K)), "v": (v, lead + (HV, V)),
+            "out": (out, lead + (HV, V))}
     if read_idx is not None:
         want["read_idx"] = (read_idx, (B,))
     if num_accepted is not None:
@@ -207,12 +252,12 @@ def build_args(variant: str, q, k, v, g, beta, pool, read_idx, write_idx,
     if write_idx is not None:
         want["write_idx"] = (write_idx, (B,))
     if beta is not None:
-        want["beta"] = (beta, (B, T, HV))
+        want["beta"] = (beta, lead + (HV,))
     if g is not None:
-        want["g"] = (g, {"lightning": (HV,), "gdn": (B, T, HV),
-                         "kda": (B, T, HV, K)}[variant])
+        want["g"] = (g, {"lightning": (HV,), "gdn": lead + (HV,),
+                         "kda": lead + (HV, K)}[variant])
     if inter is not None:
-        want["inter"] = (inter, (B, T, HV, V, K))
+        want["inter"] = (inter, lead + (HV, V, K))
     dev = pool.device
     if dev.type != "cuda":
         raise ValueError("tensors must live on a HIP device")
@@ -232,9 +277,9 @@ def build_args(variant: str, q, k, v, g, beta, pool, read_idx, write_idx,
         raise TypeError("q, k and v must share one dtype")
     a.out_dtype = _dtype_code(out, "out")
     a.state_dtype = _dtype_code(pool, "pool")
-    a.q, a.sq = _act(q, 4, "q")
-    a.k, a.sk = _act(k, 4, "k")
-    a.v, a.sv = _act(v, 4, "v")
+    a.q, a.sq = _act(q, 4, "q", vl)
+    a.k, a.sk = _act(k, 4, "k", vl)
+    a.v, a.sv = _act(v, 4, "v", vl)
     if g is not None:
         if g.dtype != torch.float32:
             raise TypeError("g must be float32")
@@ -243,52 +288,52 @@ def build_args(variant: str, q, k, v, g, beta, pool, read_idx, write_idx,
                 raise ValueError("lambda must be a contiguous [HV] tensor")
             a.g = ctypes.c_void_p(g.data_ptr())
         elif variant == "gdn":
-            if g.dim() != 3:
-                raise ValueError("gdn g must be [B, T, HV]")
-            a.g = ctypes.c_void_p(g.data_ptr())
-            a.sg = ActStrides(*g.stride())
+            a.g, a.sg = _act(g, 3, "gdn g", vl)
         else:
-            a.g, a.sg = _act(g, 4, "g")
+            a.g, a.sg = _act(g, 4, "g", vl)
     if beta is not None:
-        if beta.dtype != torch.float32 or beta.dim() != 3:
-            raise ValueError("beta must be float32 [B, T, HV]")
-        a.beta = ctypes.c_void_p(beta.data_ptr())
-        a.sbeta = ActStrides(*beta.stride())
+        if beta.dtype != torch.float32:
+            raise ValueError("beta must be float32")
+        a.beta, a.sbeta = _act(beta, 3, "beta", vl)
     a.pool = ctypes.c_void_p(pool.data_ptr())
     a.sp = PoolStrides(*pool.stride()[:3])
     a.read_idx = _idx(read_idx)
     a.write_idx = _idx(write_idx)
     if inter is not None:
         if (inter.dtype != pool.dtype or not inter.is_contiguous()
-                or tuple(inter.shape) != (B, T, HV, V, K)):
-            raise ValueError("inter must be a contiguous [B,T,HV,V,K] tensor "
-                             "of the pool's dtype")
+                or tuple(inter.shape) != lead + (HV, V, K)):
+            raise ValueError("inter must be a contiguous %s tensor of the "
+                             "pool's dtype" % (lead + (HV, V, K),))
         a.inter = ctypes.c_void_p(inter.data_ptr())
-    a.out, a.so = _act(out, 4, "out")
+    a.out, a.so = _act(out, 4, "out", vl)
     if token_slots is not None:
         if token_slots.device != dev:
             raise ValueError("token_slots is on %s, pool on %s"
                              % (token_slots.device, dev))
         a.token_slots, a.token_slots_stride = _slot_table(token_slots, B, T)
     a.num_accepted = _idx(num_accepted)
-    a.factors = _factors(factors, (B, T, HV, 2 * K + V), dev)
+    a.factors = _factors(factors, lead + (HV, 2 * K + V), dev)
+    if vl:
+        a.cu_seqlens = ctypes.c_void_p(cu_seqlens.data_ptr())
+        a.total_tokens = total
     return a
 
 
 def _run(variant, entry, q, k, v, g, beta, pool, read_idx, write_idx, out,
          inter, flags, out_dtype, stream, token_slots=None,
-         num_accepted=None, factors=None):
-    B, T = q.shape[0], q.shape[1]
-    HV, V, K = v.shape[2], v.shape[3], q.shape[3]
+         num_accepted=None, factors=None, cu_seqlens=None, max_tokens=None):
+    lead = tuple(q.shape[:-2])  # (B, T), or (total,) with cu_seqlens
+    HV, V, K = v.shape[-2], v.shape[-1], q.shape[-1]
     if out is None:
-        out = torch.empty((B, T, HV, V), dtype=out_dtype, device=q.device)
+        out = torch.empty(lead + (HV, V), dtype=out_dtype, device=q.device)
     if inter is True:
-        inter = torch.empty((B, T, HV, V, K), dtype=pool.dtype,
+        inter = torch.empty(lead + (HV, V, K), dtype=pool.dtype,
                             device=q.device)
     elif inter is False:
         inter = None
     args = build_args(variant, q, k, v, g, beta, pool, read_idx, write_idx,
-                      out, inter, flags, token_slots, num_accepted, factors)
+                      out, inter, flags, token_slots, num_accepted, factors,
+                      cu_seqlens, max_tokens)
     st = call(entry, args, stream)
     if st != LA_OK:
         raise LaDecodeError(st, entry)
@@ -299,42 +344,48 @@ def _run(variant, entry, q, k, v, g, beta, pool, read_idx, write_idx, out,
 # for paged speculative decoding, token_slots ([B, >=T] int32 table) and
 # num_accepted ([B] int32) with read_idx=None. `factors` is an optional
 # caller-allocated float32 [B, T, HV, 2K + V] tensor that receives the
-# per-token update records (see replay()).
+# per-token update records (see replay()). With cu_seqlens (int32 [B + 1]
+# offsets) the batch is variable-length: every per-token tensor is
+# token-packed ([total, ...] in place of [B, T, ...]) and max_tokens bounds
+# the tokens of one request (None: read back from the offsets, a sync).
 
 def la_decode(q, k, v, pool, read_idx=None, write_idx=None, *, lam=None,
               out=None, inter=None, out_dtype=torch.float32, stream=None,
-              token_slots=None, num_accepted=None, factors=None):
+              token_slots=None, num_accepted=None, factors=None,
+              cu_seqlens=None, max_tokens=None):
     """Lightning decode. lam: optional float32 [HV] decay factors (default:
     exp(-2^(-8(h+1)/HV)) per value head). Returns (out, inter)."""
     return _run("lightning", "la_decode", q, k, v, lam, None, pool, read_idx,
                 write_idx, out, inter, 0, out_dtype, stream, token_slots,
-                num_accepted, factors)
+                num_accepted, factors, cu_seqlens, max_tokens)
 
 
 def gdn_decode_mtp(q, k, v, g, beta, pool, read_idx=None, write_idx=None, *,
                    out=None, inter=None, l2norm_qk=False, beta_logit=False,
                    out_dtype=torch.float32, stream=None, token_slots=None,
-                   num_accepted=None, factors=None):
+                   num_accepted=None, factors=None, cu_seqlens=None,
+                   max_tokens=None):
     """Gated delta rule decode over T tokens. g: [B,T,HV] log-decay;
     beta: [B,T,HV] (logits if beta_logit). Returns (out, inter)."""
     flags = (LA_F_L2NORM_QK if l2norm_qk else 0) | \
         (LA_F_BETA_LOGIT if beta_logit else 0)
     return _run("gdn", "gdn_decode_mtp", q, k, v, g, beta, pool, read_idx,
                 write_idx, out, inter, flags, out_dtype, stream, token_slots,
-                num_accepted, factors)
+                num_accepted, factors, cu_seqlens, max_tokens)
 
 
 def kda_decode_mtp(q, k, v, g, beta, pool, read_idx=None, write_idx=None, *,
                    out=None, inter=None, l2norm_qk=False, beta_logit=False,
                    out_dtype=torch.float32, stream=None, token_slots=None,
-                   num_accepted=None, factors=None):
+                   num_accepted=None, factors=None, cu_seqlens=None,
+                   max_tokens=None):
     """KDA decode over T tokens. g: [B,T,HV,K] per-key-channel log-decay.
     Returns (out, inter)."""
     flags = (LA_F_L2NORM_QK if l2norm_qk else 0) | \
         (LA_F_BETA_LOGIT if beta_logit else 0)
     return _run("kda", "kda_decode_mtp", q, k, v, g, beta, pool, read_idx,
                 write_idx, out, inter, flags, out_dtype, stream, token_slots,
-                num_accepted, factors)
+                num_accepted, factors, cu_seqlens, max_tokens)
 
 
 def check_indices(read_idx, write_idx, pool_size, result=None, stream=None):
@@ -372,11 +423,40 @@ def check_token_slots(token_slots, num_accepted, pool_size, T, result=None,
     return result
 
 
+def check_cu_seqlens(cu_seqlens, max_tokens, total_tokens, result=None,
+                     stream=None):
+    """Launch the varlen offset validator; returns the device int32 result
+    (bits: 1 an offset outside [0, total_tokens], 2 a request with a negative
+    count or more than max_tokens tokens)."""
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be 1-D int32")
+    if result is None:
+        result = torch.empty((1,), dtype=torch.int32,
+                             device=cu_seqlens.device)
+    st = lib().la_check_cu_seqlens(cu_seqlens.shape[0] - 1, max_tokens,
+                                   total_tokens, _idx(cu_seqlens),
+                                   ctypes.c_void_p(result.data_ptr()),
+                                   _stream_handle(stream))
+    if st != LA_OK:
+        raise LaDecodeError(st, "la_check_cu_seqlens")
+    return result
+
+
 def build_replay_args(factors, pool, read_idx, write_idx,
-                      num_tokens) -> ReplayArgs:
-    if factors.dim() != 4:
-        raise ValueError("factors must be [B, T, HV, 2K + V]")
-    B, T, HV, R = factors.shape
+                      num_tokens, cu_seqlens=None,
+                      max_tokens=None) -> ReplayArgs:
+    if cu_seqlens is not None:
+        if factors.dim() != 3:
+            raise ValueError("with cu_seqlens factors must be "
+                             "[total, HV, 2K + V]")
+        total, HV, R = factors.shape
+        B, T = _cu(cu_seqlens, max_tokens, pool.device)
+        lead = (total,)
+    else:
+        if factors.dim() != 4:
+            raise ValueError("factors must be [B, T, HV, 2K + V]")
+        B, T, HV, R = factors.shape
+        lead = (B, T)
     if (pool.dim() != 4 or pool.dtype not in (torch.float32, torch.bfloat16)
             or pool.stride(3) != 1):
         raise ValueError("pool must be a float32 or bfloat16 "
@@ -395,21 +475,26 @@ def build_replay_args(factors, pool, read_idx, write_idx,
     a.B, a.T, a.HV, a.K, a.V = B, T, HV, K, V
     a.pool_size = pool.shape[0]
     a.state_dtype = _dtype_code(pool, "pool")
-    a.factors = _factors(factors, (B, T, HV, R), dev)
+    a.factors = _factors(factors, lead + (HV, R), dev)
     a.pool = ctypes.c_void_p(pool.data_ptr())
     a.sp = PoolStrides(*pool.stride()[:3])
     a.read_idx = _idx(read_idx)
     a.write_idx = _idx(write_idx)
     a.num_tokens = _idx(num_tokens)
+    if cu_seqlens is not None:
+        a.cu_seqlens = ctypes.c_void_p(cu_seqlens.data_ptr())
+        a.total_tokens = lead[0]
     return a
 
 
-def replay(factors, pool, read_idx, write_idx, num_tokens, stream=None):
+def replay(factors, pool, read_idx, write_idx, num_tokens, stream=None, *,
+           cu_seqlens=None, max_tokens=None):
     """Rebuild states from per-token update records (written by a decode call
     with factors=...): request b starts from pool[read_idx[b]], applies its
     first num_tokens[b] records and stores the result in write_idx[b]
     (None: the read slot; negative: skip)."""
-    args = build_replay_args(factors, pool, read_idx, write_idx, num_tokens)
+    args = build_replay_args(factors, pool, read_idx, write_idx, num_tokens,
+                             cu_seqlens, max_tokens)
     st = lib().la_replay(ctypes.byref(args), _stream_handle(stream))
     if st != LA_OK:
         raise LaDecodeError(st, "la_replay")

@@ -87,6 +87,8 @@ struct Params {
     int64_t ts_stride;
     const int32_t *naccept;
     float *factors;  // [B, T, HV, 2K + V] per-token records, or null
+    const int32_t *cu;  // [B + 1] token offsets of a varlen batch, or null
+    int32_t total;      // rows of the token-packed arrays (with cu)
 };
 
 // ---------------------------------------------------------------- helpers
@@ -408,13 +410,36 @@ __device__ __forceinline__ void prologue_finish(const Params &p, int hv,
     }
 }
 
-// Start of the update record of token t of (request b, value head hv).
+// Start of the update record of flat token `tok` (b T + t, or the packed
+// token number of a varlen batch) and value head hv.
 template <int K, int V>
-__device__ __forceinline__ float *factor_record(const Params &p, int b, int t,
+__device__ __forceinline__ float *factor_record(const Params &p, int64_t tok,
                                                 int hv)
 {
-    return p.factors + ((static_cast<int64_t>(b) * p.T + t) * p.HV + hv) *
-                           static_cast<int64_t>(2 * K + V);
+    return p.factors +
+           (tok * p.HV + hv) * static_cast<int64_t>(2 * K + V);
+}
+
+// Token range of request b: its count, the offset added to t in the
+// per-token arrays and the flat number of its token 0 (b T in a dense batch).
+// False when varlen offsets break the precondition (the request is skipped).
+__device__ __forceinline__ bool request_tokens(const int32_t *cu, int32_t total,
+                                               int b, int T, int &Tb,
+                                               int &tok0, int64_t &flat0)
+{
+    Tb = T;
+    tok0 = 0;
+    flat0 = static_cast<int64_t>(b) * T;
+    if (!cu)
+        return true;
+    const int c0 = __builtin_amdgcn_readfirstlane(cu[b]);
+    const int c1 = __builtin_amdgcn_readfirstlane(cu[b + 1]);
+    if (c0 < 0 || c1 < c0 || c1 > total || c1 - c0 > T)
+        return false;
+    Tb = c1 - c0;
+    tok0 = c0;
+    flat0 = c0;
+    return true;
 }
 
 #if LA_WAVES_PER_EU > 0
@@ -450,13 +475,17 @@ decode_kernel(const Params p)
     const int c8 = lane & 7;
     const int rs = lane >> 3;
     const int T = p.T;
+    int Tb, tok0;
+    int64_t flat0;
+    if (!request_tokens(p.cu, p.total, b, T, Tb, tok0, flat0))
+        return;
 
     int r, w;
     if (p.tslots) {
         // paged slots: seed = entry of the last accepted token; the state is
         // written after every token instead of once at the end
         const int na = __builtin_amdgcn_readfirstlane(p.naccept[b]);
-        r = (na >= 1 && na <= T)
+        r = (na >= 1 && na <= Tb)
                 ? __builtin_amdgcn_readfirstlane(p.tslots[b * p.ts_stride + na - 1])
                 : -1;
         w = -1;
@@ -469,11 +498,11 @@ decode_kernel(const Params p)
     // rows exactly once): row R wave + 8 c8 + rs.
     const int orow = wave * kRowsPerWave + (c8 & (RPL - 1)) * 8 + rs;
     const bool olane = c8 < RPL;
-    const int64_t obase = b * p.so_b + hv * p.so_h + orow;
+    const int64_t obase = b * p.so_b + tok0 * p.so_t + hv * p.so_h + orow;
 
     if (r < 0) {  // padded request: zero outputs, touch nothing else
         if (olane)
-            for (int t = 0; t < T; ++t)
+            for (int t = 0; t < Tb; ++t)
                 store_out<BF16OUT>(p.out, obase + t * p.so_t, 0.f);
         return;
     }
@@ -500,16 +529,17 @@ decode_kernel(const Params p)
                 S[i], src, lane_off, (wave * kRowsPerWave + i * 8) * row_bytes);
     }
 
-    for (int t0 = 0; t0 < T; t0 += kTokChunk) {
-        const int nt = min(kTokChunk, T - t0);
+    for (int t0 = 0; t0 < Tb; t0 += kTokChunk) {
+        const int nt = min(kTokChunk, Tb - t0);
         if (t0 > 0)
             lds_barrier();  // every wave is done with the previous chunk
         for (int tt = wave; tt < nt; tt += NW) {
             TokRaw<K, V> rw;
-            prologue_load<VAR, K, V, BF16IN>(p, b, hv, t0 + tt, lane, rw);
+            prologue_load<VAR, K, V, BF16IN>(p, b, hv, tok0 + t0 + tt, lane,
+                                             rw);
             prologue_finish<VAR, K, V>(
                 p, hv, lane, rw, lds + tt * L::size,
-                REC ? factor_record<K, V>(p, b, t0 + tt, hv) : nullptr);
+                REC ? factor_record<K, V>(p, flat0 + t0 + tt, hv) : nullptr);
         }
         lds_barrier();
 
@@ -603,7 +633,7 @@ decode_kernel(const Params p)
                 store_out<BF16OUT>(p.out, obase + t * p.so_t, mine);
             if constexpr (REC) {
                 // lane (c8 = i, rs) stores err of its row R w + 8 i + rs
-                float *ferr = factor_record<K, V>(p, b, t, hv) + 2 * K +
+                float *ferr = factor_record<K, V>(p, flat0 + t, hv) + 2 * K +
                               wave * kRowsPerWave + rs;
 #pragma unroll
                 for (int i = 0; i < RPL; ++i)
@@ -630,7 +660,7 @@ decode_kernel(const Params p)
                 // contiguous [B, T, HV, V, K] cache: rows are K floats apart
                 const BufRsrc dst = make_rsrc(
                     static_cast<char *>(p.inter) +
-                        ((static_cast<int64_t>(b) * T + t) * p.HV + hv) *
+                        ((flat0 + t) * p.HV + hv) *
                             static_cast<int64_t>(V * K * ES),
                     V * K * ES);
                 const uint32_t ioff = rs * (K * ES) + c8 * 16u;
@@ -816,6 +846,8 @@ struct ReplayParams {
     const int32_t *ridx;
     const int32_t *widx;
     const int32_t *ntok;
+    const int32_t *cu;  // varlen token offsets, or null
+    int32_t total;
 };
 
 // Rebuild the state of (request, value head) from its update records:
@@ -844,7 +876,11 @@ replay_kernel(const ReplayParams p)
     const int r = __builtin_amdgcn_readfirstlane(p.ridx[b]);
     const int w = __builtin_amdgcn_readfirstlane(p.widx ? p.widx[b] : r);
     const int n = __builtin_amdgcn_readfirstlane(p.ntok[b]);
-    if (r < 0 || n < 0 || n > p.T)
+    int Tb, tok0;
+    int64_t flat0;
+    if (!request_tokens(p.cu, p.total, b, p.T, Tb, tok0, flat0))
+        return;
+    if (r < 0 || n < 0 || n > Tb)
         return;
 
     const uint32_t row_bytes = static_cast<uint32_t>(p.sp_row) * ES;
@@ -861,7 +897,7 @@ replay_kernel(const ReplayParams p)
             S[i], src, lane_off, (wave * kRowsPerWave + i * 8) * row_bytes);
 
     const f4 *grec = reinterpret_cast<const f4 *>(
-        p.factors + (static_cast<int64_t>(b) * p.T * p.HV + hv) * RS);
+        p.factors + (flat0 * p.HV + hv) * RS);
     const int64_t tstride4 = static_cast<int64_t>(p.HV) * RS / 4;
     for (int t0 = 0; t0 < n; t0 += kTokChunk) {
         const int nt = min(kTokChunk, n - t0);
@@ -989,6 +1025,31 @@ check_token_slots_kernel(int32_t B, int32_t T, int32_t pool_size,
                         f |= 4;
             }
         }
+    }
+    if (f)
+        atomicOr(&flags, f);
+    __syncthreads();
+    if (threadIdx.x == 0)
+        *result = flags;
+}
+
+// Validator of varlen offsets (one workgroup): bit 1 = an offset outside
+// [0, total], bit 2 = a request with a negative count or more than T tokens.
+__global__ void __launch_bounds__(1024)
+check_cu_seqlens_kernel(int32_t B, int32_t T, int32_t total,
+                        const int32_t *cu, int32_t *result)
+{
+    __shared__ int32_t flags;
+    if (threadIdx.x == 0)
+        flags = 0;
+    __syncthreads();
+    int32_t f = 0;
+    for (int i = threadIdx.x; i < B; i += blockDim.x) {
+        const int32_t c0 = cu[i], c1 = cu[i + 1];
+        if (c0 < 0 || c0 > total || c1 < 0 || c1 > total)
+            f |= 1;
+        if (c1 < c0 || c1 - c0 > T)
+            f |= 2;
     }
     if (f)
         atomicOr(&flags, f);
@@ -1134,6 +1195,10 @@ la_status validate(const la_decode_args *a, int var)
         (a->out_dtype != LA_F32 && a->out_dtype != LA_BF16) ||
         (a->state_dtype != LA_F32 && a->state_dtype != LA_BF16))
         return LA_ERR_DTYPE;
+    if (a->reserved != 0)
+        return LA_ERR_ARG;
+    if (a->cu_seqlens && a->total_tokens < 0)
+        return LA_ERR_SHAPE;
     if (var == VAR_LA) {
         if (a->flags != 0 || a->beta != nullptr)
             return LA_ERR_ARG;
@@ -1186,8 +1251,13 @@ la_status validate(const la_decode_args *a, int var)
     const int64_t es = a->state_dtype == LA_BF16 ? 2 : 4;
     if ((static_cast<int64_t>(a->V - 1) * a->sp.row + a->K) * es > INT32_MAX)
         return LA_ERR_STRIDE;
-    // outputs must not overlap each other
-    {
+    // outputs must not overlap each other ([total, HV, V] when varlen)
+    if (a->cu_seqlens) {
+        const int64_t st[2] = {a->so.h, a->so.t};
+        const int64_t ex[2] = {a->HV, a->total_tokens};
+        if (!no_overlap(2, st, ex, a->V))
+            return LA_ERR_STRIDE;
+    } else {
         const int64_t st[3] = {a->so.h, a->so.t, a->so.b};
         const int64_t ex[3] = {a->HV, a->T, a->B};
         if (!no_overlap(3, st, ex, a->V))
@@ -1212,6 +1282,8 @@ la_status validate(const la_decode_args *a, int var)
     if (a->inter && !aligned(a->inter, 16))
         return LA_ERR_ALIGN;
     if (a->factors && !aligned(a->factors, 16))
+        return LA_ERR_ALIGN;
+    if (!aligned(a->cu_seqlens, 4))
         return LA_ERR_ALIGN;
     return LA_OK;
 }
@@ -1263,13 +1335,20 @@ la_status launch(const la_decode_args *a, void *stream, int var)
     p.ts_stride = a->token_slots_stride;
     p.naccept = a->num_accepted;
     p.factors = a->factors;
+    p.cu = a->cu_seqlens;
+    p.total = a->cu_seqlens ? a->total_tokens : 0;
+    if (a->cu_seqlens) {
+        // token-packed arrays: the flat token number goes through the t
+        // strides, so the per-request strides drop out
+        p.sq_b = p.sk_b = p.sv_b = p.sg_b = p.sb_b = p.so_b = 0;
+    }
 
     const bool bi = a->qkv_dtype == LA_BF16, bo = a->out_dtype == LA_BF16;
     const bool bs = a->state_dtype == LA_BF16;
     const bool rec = a->factors != nullptr;
     // one token on a bf16 pool with no per-token writes: packed tile
     const bool packed = bs && a->T == 1 && !a->inter && !a->token_slots &&
-                        !rec;
+                        !rec && !a->cu_seqlens;
     KernelFn fn;
     if (packed)
         fn = var == VAR_LA    ? pick_packed<VAR_LA>(a->K, a->V, bi, bo)
@@ -1336,12 +1415,18 @@ la_status la_replay(const la_replay_args *a, void *stream)
         return LA_ERR_UNSUPPORTED;
     if (a->state_dtype != LA_F32 && a->state_dtype != LA_BF16)
         return LA_ERR_DTYPE;
+    if (a->reserved != 0)
+        return LA_ERR_ARG;
+    if (a->cu_seqlens && a->total_tokens < 0)
+        return LA_ERR_SHAPE;
     if (static_cast<int64_t>(a->B) * a->HV > INT32_MAX)
         return LA_ERR_SHAPE;
     if (a->B == 0)
         return LA_OK;
     if (!a->factors || !a->pool || !a->read_idx || !a->num_tokens)
         return LA_ERR_NULL;
+    if (!aligned(a->cu_seqlens, 4))
+        return LA_ERR_ALIGN;
     if (a->sp.slot < 0 || a->sp.head < 0 || a->sp.row < 0)
         return LA_ERR_STRIDE;
     {
@@ -1374,6 +1459,8 @@ la_status la_replay(const la_replay_args *a, void *stream)
     p.ridx = a->read_idx;
     p.widx = a->write_idx;
     p.ntok = a->num_tokens;
+    p.cu = a->cu_seqlens;
+    p.total = a->cu_seqlens ? a->total_tokens : 0;
     const bool bs = a->state_dtype == LA_BF16;
     typedef void (*ReplayFn)(const ReplayParams);
     ReplayFn fn;
@@ -1437,6 +1524,23 @@ la_status la_check_token_slots(int32_t B, int32_t T, int32_t pool_size,
     return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
 }
 
+la_status la_check_cu_seqlens(int32_t B, int32_t T, int32_t total_tokens,
+                              const int32_t *cu_seqlens, int32_t *dev_result,
+                              void *stream)
+{
+    if (B < 0 || T < 1 || total_tokens < 0)
+        return LA_ERR_SHAPE;
+    if (!dev_result || !cu_seqlens)
+        return LA_ERR_NULL;
+    if (!aligned(dev_result, 4) || !aligned(cu_seqlens, 4))
+        return LA_ERR_ALIGN;
+    void *kargs[] = {&B, &T, &total_tokens, &cu_seqlens, &dev_result};
+    const hipError_t e = hipLaunchKernel(
+        reinterpret_cast<const void *>(check_cu_seqlens_kernel), dim3(1),
+        dim3(1024), kargs, 0, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
+}
+
 const char *la_status_string(la_status s)
 {
     switch (s) {
@@ -1462,6 +1566,6 @@ const char *la_status_string(la_status s)
     return "unknown status";
 }
 
-int32_t la_version(void) { return 200; }
+int32_t la_version(void) { return 210; }
 
 }  // extern "C"

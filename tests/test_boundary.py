@@ -37,8 +37,8 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("la_decode", "gdn_decode_mtp", "kda_decode_mtp", "la_replay",
-              "la_check_indices", "la_check_token_slots", "la_status_string",
-              "la_version"):
+              "la_check_indices", "la_check_token_slots",
+              "la_check_cu_seqlens", "la_status_string", "la_version"):
         assert n in names
 
 
@@ -196,6 +196,17 @@ REJECT = [
                                     token_slots_stride=2), "lightning", 4),
     ("num_accepted_without_table", _mut(num_accepted=FAKE + 0x700100),
      "gdn", 6),
+    # variable-length batches
+    ("reserved_nonzero", _mut(reserved=1), "gdn", 6),
+    ("varlen_negative_total", _mut(cu_seqlens=FAKE + 0x900000,
+                                   total_tokens=-1), "kda", 2),
+    ("varlen_misaligned_offsets", _mut(cu_seqlens=FAKE + 0x900002,
+                                       total_tokens=8), "lightning", 4),
+    # packed outputs [total, HV, V]: rows of consecutive tokens overlap
+    ("varlen_out_tokens_overlap", _mut(cu_seqlens=FAKE + 0x900000,
+                                       total_tokens=8,
+                                       so=bnd.ActStrides(0, 128, 128)),
+     "gdn", 3),
 ]
 
 
@@ -226,6 +237,31 @@ def test_check_indices_host_rejections(lib):
     assert L.la_check_indices(4, 4, FAKE, None, None, None) == 1
     assert L.la_check_indices(4, 4, None, None, FAKE, None) == 1
     assert L.la_check_indices(4, 4, FAKE, None, FAKE + 2, None) == 4
+
+
+def test_check_cu_seqlens_host_rejections(lib):
+    L = lib
+    assert L.la_check_cu_seqlens(-1, 2, 4, FAKE, FAKE, None) == 2
+    assert L.la_check_cu_seqlens(4, 0, 4, FAKE, FAKE, None) == 2
+    assert L.la_check_cu_seqlens(4, 2, -1, FAKE, FAKE, None) == 2
+    assert L.la_check_cu_seqlens(4, 2, 4, None, FAKE, None) == 1
+    assert L.la_check_cu_seqlens(4, 2, 4, FAKE, None, None) == 1
+    assert L.la_check_cu_seqlens(4, 2, 4, FAKE + 2, FAKE, None) == 4
+
+
+def test_varlen_packed_outputs_accept_flat_token_strides(lib):
+    """With cu_seqlens the b strides are ignored and outputs are
+    [total, HV, V]: a packed output layout passes the overlap check. The
+    offsets pointer is misaligned on purpose so that validation stops at the
+    last host check (LA_ERR_ALIGN) and nothing is launched."""
+    a = _valid_args("gdn")
+    a.cu_seqlens = FAKE + 0x900002
+    a.total_tokens = 8
+    a.so = bnd.ActStrides(0, 4 * 128, 128)
+    a.sq = bnd.ActStrides(0, 2 * 128, 128)
+    assert _status("gdn", a) == 4
+    a.so = bnd.ActStrides(0, 128, 128)  # token rows overlap: rejected first
+    assert _status("gdn", a) == 3
 
 
 def test_check_token_slots_host_rejections(lib):
@@ -309,6 +345,11 @@ REPLAY_REJECT = [
     ("factors_misaligned", _mut(factors=FAKE + 0x800008), 4),
     ("pool_misaligned", _mut(pool=FAKE + 0x1000008), 4),
     ("num_tokens_misaligned", _mut(num_tokens=FAKE + 0x500202), 4),
+    ("reserved_nonzero", _mut(reserved=3), 6),
+    ("varlen_negative_total", _mut(cu_seqlens=FAKE + 0x900000,
+                                   total_tokens=-2), 2),
+    ("varlen_misaligned_offsets", _mut(cu_seqlens=FAKE + 0x900001,
+                                       total_tokens=4), 4),
 ]
 
 

@@ -221,7 +221,8 @@ SAMPLE = {"gdn_small_k64": None, "lightning_b33_h64": None,
           "kda_b256_t1": range(0, 256, 9), "kda_b256_t8": range(0, 256, 17)}
 
 
-@pytest.mark.parametrize("name", [n for n in W.NAMED if "paged" not in n])
+@pytest.mark.parametrize("name", [n for n in W.NAMED
+                                  if "paged" not in n and "varlen" not in n])
 def test_named_workload_parity(name):
     wl = W.named(name)
     run_and_check(wl, SAMPLE[name])
@@ -957,3 +958,310 @@ def test_named_spec_step_parity():
     keep = torch.ones(wl.pool_size, dtype=torch.bool)
     keep[torch.tensor(written)] = False
     assert torch.equal(_bits(got)[keep], _bits(wl.pool())[keep])
+
+
+# ----------------------------------------------------- variable-length batches
+
+
+def gpu_run_varlen(wl, factors=False):
+    """Run a token-packed workload (wl.cu_seqlens set). Outputs, cache and
+    records are pre-filled with NaN."""
+    lad = _lad()
+    d = wl.to(DEV)
+    pool = d.backing[:: wl.stride_mult]
+    total = wl.q.shape[0]
+    assert int(lad.check_cu_seqlens(d.cu_seqlens, wl.T, total).item()) == 0
+    paged = wl.token_slots is not None
+    if not paged:
+        assert int(lad.check_indices(d.read_idx, d.write_idx,
+                                     wl.pool_size).item()) == 0
+    out = torch.full((total, wl.HV, wl.V), float("nan"), dtype=wl.out_dtype,
+                     device=DEV)
+    inter = (torch.full((total, wl.HV, wl.V, wl.K), float("nan"),
+                        dtype=wl.backing.dtype, device=DEV)
+             if wl.inter else None)
+    fac = (torch.full((total, wl.HV, 2 * wl.K + wl.V), float("nan"),
+                      dtype=torch.float32, device=DEV) if factors else None)
+    kw = dict(out=out, inter=inter, factors=fac, cu_seqlens=d.cu_seqlens,
+              max_tokens=wl.T, token_slots=d.token_slots,
+              num_accepted=d.num_accepted, out_dtype=wl.out_dtype)
+    ridx = None if paged else d.read_idx
+    widx = None if paged else d.write_idx
+    if wl.variant == W.LIGHTNING:
+        lad.la_decode(d.q, d.k, d.v, pool, ridx, widx, lam=d.g, **kw)
+    else:
+        fn = lad.gdn_decode_mtp if wl.variant == W.GDN else lad.kda_decode_mtp
+        fn(d.q, d.k, d.v, d.g, d.beta, pool, ridx, widx,
+           l2norm_qk=wl.l2norm, beta_logit=wl.beta_logit, **kw)
+    torch.cuda.synchronize()
+    return {"out": out.cpu(), "backing": d.backing.cpu(),
+            "inter": None if inter is None else inter.cpu(),
+            "factors": None if fac is None else fac.cpu()}
+
+
+def oracle_run_varlen(wl, reqs=None, factors=False):
+    """The oracle on the requests `reqs` of a token-packed workload, as a
+    variable-length sub-batch over the whole pool."""
+    reqs = list(range(wl.B)) if reqs is None else list(reqs)
+    cu = wl.cu_seqlens.tolist()
+    rows = [r for b in reqs for r in range(cu[b], cu[b + 1])]
+    counts = [cu[b + 1] - cu[b] for b in reqs]
+    cu_sub = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    sel = torch.tensor(rows, dtype=torch.long)
+    bsel = torch.tensor(reqs, dtype=torch.long)
+    g = wl.g if wl.variant == W.LIGHTNING else wl.g[sel]
+    beta = None if wl.beta is None else wl.beta[sel]
+    kw = {}
+    if wl.token_slots is not None:
+        kw = dict(token_slots=wl.token_slots[bsel],
+                  num_accepted=wl.num_accepted[bsel])
+        ridx, widx = None, None
+    else:
+        ridx = wl.read_idx[bsel]
+        widx = None if wl.write_idx is None else wl.write_idx[bsel]
+    res = oracle.decode(VARIANT_CODE[wl.variant], wl.q[sel], wl.k[sel],
+                        wl.v[sel], g, beta, wl.pool(), ridx, widx,
+                        flags=_flags(wl), inter=wl.inter, factors=factors,
+                        cu_seqlens=cu_sub, max_tokens=wl.T, **kw)
+    res["reqs"], res["cu_sub"] = reqs, cu_sub
+    return res
+
+
+def _varlen_active(wl, b):
+    """Whether request b of a varlen workload runs (is not padding)."""
+    n = wl.counts()[b]
+    if wl.token_slots is not None:
+        na = int(wl.num_accepted[b])
+        return 1 <= na <= n and int(wl.token_slots[b, na - 1]) >= 0
+    return int(wl.read_idx[b]) >= 0
+
+
+def check_varlen(wl, got, before, reqs=None):
+    ref = oracle_run_varlen(wl, reqs)
+    kind, tol_out, tol_state = _tol(wl)
+    cu = wl.cu_seqlens.tolist()
+    m = wl.stride_mult
+    errs = {"out": 0.0, "state": 0.0, "inter": 0.0}
+    assert not torch.isnan(got["out"].float()).any() or reqs is not None
+    written = set()
+    for i, b in enumerate(ref["reqs"]):
+        g0, g1 = cu[b], cu[b + 1]
+        r0, r1 = ref["cu_sub"][i], ref["cu_sub"][i + 1]
+        if g1 == g0:
+            continue  # no tokens: only its state write is checked (below)
+        errs["out"] = max(errs["out"], _err(kind, got["out"][g0:g1].float(),
+                                            ref["out"][r0:r1]))
+        if not _varlen_active(wl, b):
+            assert not got["out"][g0:g1].float().any(), "padding outputs 0"
+            if wl.inter:
+                assert torch.isnan(got["inter"][g0:g1].float()).all(), \
+                    "padded request must not touch the cache"
+            continue
+        if wl.inter:
+            errs["inter"] = max(errs["inter"], _state_err(
+                wl, kind, tol_state, got["inter"][g0:g1].float().numpy(),
+                ref["inter"][r0:r1]))
+    # every slot of the pool: the oracle ran on the whole pool
+    if reqs is None:
+        errs["state"] = _state_err(wl, kind, tol_state,
+                                   got["backing"][::m].float().numpy(),
+                                   ref["pool"])
+    else:
+        widx = (wl.write_idx if wl.write_idx is not None
+                else wl.read_idx).tolist()
+        ridx = wl.read_idx.tolist()
+        for b in ref["reqs"]:
+            if ridx[b] >= 0 and widx[b] >= 0:
+                written.add(widx[b])
+                errs["state"] = max(errs["state"], _state_err(
+                    wl, kind, tol_state,
+                    got["backing"][m * widx[b]].float().numpy(),
+                    ref["pool"][widx[b]]))
+    bf = wl.backing.dtype == torch.bfloat16
+    assert errs["out"] <= tol_out, errs
+    assert errs["state"] <= (0.0 if bf else tol_state), errs
+    assert errs["inter"] <= (0.0 if bf else tol_state), errs
+    if m > 1:  # the gaps between logical slots are never written
+        keep = torch.ones(got["backing"].shape[0], dtype=torch.bool)
+        keep[::m] = False
+        assert torch.equal(_bits(got["backing"][keep]), _bits(before[keep]))
+    print("  %s errors %s" % (wl.name, {k: "%.2e" % v
+                                        for k, v in errs.items()}),
+          flush=True)
+    return ref
+
+
+@pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN, W.KDA])
+@pytest.mark.parametrize("K,V", [(128, 128), (64, 128), (128, 64)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16],
+                         ids=["f32", "bf16"])
+def test_varlen_parity(variant, K, V, dtype):
+    """Variable-length batch with a zero-token request, a padded request,
+    separate write slots (some skipped), strided pool and token cache."""
+    seed = (4000 + 100 * [W.LIGHTNING, W.GDN, W.KDA].index(variant)
+            + 10 * [(128, 128), (64, 128), (128, 64)].index((K, V))
+            + (5 if dtype == torch.bfloat16 else 0))
+    wl = W.make("varlen", variant, B=7, T=5, H=2, HV=4, K=K, V=V,
+                pool_size=20, seed=seed, act_dtype=dtype, pool_std=0.1,
+                stride_mult=2, separate_write=True, write_skip=0.3,
+                inter=True, varlen_min=0)
+    ridx = wl.read_idx.clone()
+    ridx[3] = -1  # padded
+    wl.read_idx = ridx
+    before = wl.backing.clone()
+    got = gpu_run_varlen(wl)
+    check_varlen(wl, got, before)
+
+
+@pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN, W.KDA])
+def test_varlen_zero_and_full_length_requests(variant):
+    """Explicit lengths 0, T, 1: a zero-token request copies its read state
+    to its write slot; outputs of the others match the oracle."""
+    wl = W.make("varlen0", variant, B=3, T=4, H=1, HV=2, K=128, V=128,
+                pool_size=8, seed=4300 + len(variant), separate_write=True,
+                inter=True)
+    lengths = [0, 4, 1]
+    cu = torch.tensor([0, 0, 4, 5], dtype=torch.int32)
+
+    def pack(x):
+        return torch.cat([x[b, :n] for b, n in enumerate(lengths)], 0)
+    wl.q, wl.k, wl.v = pack(wl.q), pack(wl.k), pack(wl.v)
+    if variant != W.LIGHTNING:
+        wl.g, wl.beta = pack(wl.g), pack(wl.beta)
+    wl.cu_seqlens = cu
+    before = wl.backing.clone()
+    got = gpu_run_varlen(wl)
+    check_varlen(wl, got, before)
+    r0, w0 = int(wl.read_idx[0]), int(wl.write_idx[0])
+    assert torch.equal(_bits(got["backing"][w0]), _bits(before[r0]))
+
+
+@pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN, W.KDA])
+def test_varlen_equal_lengths_bit_identical_to_dense(variant):
+    """Offsets 0, T, 2T, ... over token-packed inputs give the dense call's
+    bits (same kernels, same arithmetic)."""
+    wl = W.make("vdense", variant, B=5, T=3, H=2, HV=4, K=128, V=128,
+                pool_size=12, seed=4400 + len(variant), separate_write=True,
+                inter=True)
+    dense = gpu_run(wl)
+    B, T = wl.B, wl.T
+    vl = dataclasses.replace(
+        wl, q=wl.q.reshape((B * T,) + wl.q.shape[2:]),
+        k=wl.k.reshape((B * T,) + wl.k.shape[2:]),
+        v=wl.v.reshape((B * T,) + wl.v.shape[2:]),
+        g=wl.g if variant == W.LIGHTNING else wl.g.reshape(
+            (B * T,) + wl.g.shape[2:]),
+        beta=None if wl.beta is None else wl.beta.reshape(B * T, wl.HV),
+        cu_seqlens=torch.arange(0, B * T + 1, T, dtype=torch.int32))
+    got = gpu_run_varlen(vl)
+    assert torch.equal(_bits(got["out"].reshape(dense["out"].shape)),
+                       _bits(dense["out"]))
+    assert torch.equal(_bits(got["backing"]), _bits(dense["backing"]))
+    assert torch.equal(_bits(got["inter"].reshape(dense["inter"].shape)),
+                       _bits(dense["inter"]))
+
+
+@pytest.mark.parametrize("variant", [W.GDN, W.KDA])
+def test_varlen_paged_slots(variant):
+    """Paged per-token slots over a variable-length batch: the accepted
+    count is checked against each request's own token count."""
+    wl = W.make("vpaged", variant, B=4, T=3, H=2, HV=2, K=128, V=128,
+                pool_size=16, seed=4500 + len(variant), paged=True,
+                inter=True, varlen_min=1)
+    counts = wl.counts()
+    acc = wl.num_accepted.clone()
+    for b, n in enumerate(counts):
+        acc[b] = min(int(acc[b]), n)
+    acc[1] = counts[1] + 1  # beyond its own tokens: padding
+    wl.num_accepted = acc
+    before = wl.backing.clone()
+    got = gpu_run_varlen(wl)
+    check_varlen(wl, got, before)
+    cu = wl.cu_seqlens.tolist()
+    assert not got["out"][cu[1]:cu[2]].any()
+
+
+@pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN, W.KDA])
+def test_varlen_records_replay_equal_cache_bitwise(variant):
+    """Records written by a varlen decode, replayed for n_b <= T_b tokens,
+    rebuild the token cache's state bit for bit (fp32 pool)."""
+    lad = _lad()
+    wl = W.make("vrec", variant, B=6, T=4, H=2, HV=2, K=128, V=128,
+                pool_size=14, seed=4600 + len(variant), separate_write=True,
+                inter=True, varlen_min=0)
+    got = gpu_run_varlen(wl, factors=True)
+    counts = wl.counts()
+    ntok = torch.tensor([min(c, 2) for c in counts], dtype=torch.int32)
+    d = wl.to(DEV)  # a fresh copy of the pool as it was before the decode
+    pool = d.backing[:: wl.stride_mult]
+    lad.replay(got["factors"].to(DEV), pool, d.read_idx, d.write_idx,
+               ntok.to(DEV), cu_seqlens=d.cu_seqlens, max_tokens=wl.T)
+    torch.cuda.synchronize()
+    after = d.backing.cpu()
+    cu = wl.cu_seqlens.tolist()
+    for b, n in enumerate(ntok.tolist()):
+        w = int(wl.write_idx[b])
+        if w < 0:
+            continue
+        want = (wl.backing[int(wl.read_idx[b])] if n == 0
+                else got["inter"][cu[b] + n - 1])
+        assert torch.equal(_bits(after[w]), _bits(want)), b
+    ref = oracle_run_varlen(wl, factors=True)
+    fac = got["factors"].double().numpy()
+    assert np.isfinite(fac).all()
+    kind, tol_out, _ = _tol(wl)
+    assert _err(kind, fac, ref["factors"]) <= 10 * tol_out
+
+
+@pytest.mark.parametrize("cu,T,total,expect", [
+    ([0, 2, 3, 6], 3, 6, 0),
+    ([0, 2, 3, 7], 4, 6, 1),
+    ([0, 4, 5, 6], 3, 6, 2),
+    ([0, 3, 2, 6], 3, 6, 2),
+    ([-1, 2, 3, 6], 3, 6, 1),
+    ([0, 0, 0, 0], 1, 0, 0),
+])
+def test_check_cu_seqlens(cu, T, total, expect):
+    lad = _lad()
+    t = torch.tensor(cu, dtype=torch.int32, device=DEV)
+    assert int(lad.check_cu_seqlens(t, T, total).item()) == expect
+
+
+def test_varlen_bad_offsets_skip_the_request():
+    """A request whose offsets break the precondition is skipped entirely:
+    its pool slots stay untouched and the other requests are unaffected."""
+    lad = _lad()
+    wl = W.make("vbad", W.GDN, B=3, T=2, H=1, HV=2, K=128, V=128,
+                pool_size=8, seed=4700, separate_write=True, varlen_min=2)
+    # request 2 claims tokens 4..6 of a 5-token buffer: past the end
+    wl.q, wl.k, wl.v = wl.q[:5], wl.k[:5], wl.v[:5]
+    wl.g, wl.beta = wl.g[:5], wl.beta[:5]
+    cu_bad = torch.tensor([0, 2, 4, 6], dtype=torch.int32)
+    d = wl.to(DEV)
+    assert int(lad.check_cu_seqlens(cu_bad.to(DEV), 2, 5).item()) == 1
+    pool = d.backing[:: wl.stride_mult]
+    out = torch.full((5, wl.HV, wl.V), float("nan"), device=DEV)
+    lad.gdn_decode_mtp(d.q, d.k, d.v, d.g, d.beta, pool, d.read_idx,
+                       d.write_idx, out=out, cu_seqlens=cu_bad.to(DEV),
+                       max_tokens=2, l2norm_qk=True, beta_logit=True)
+    torch.cuda.synchronize()
+    after = d.backing.cpu()
+    w2 = int(wl.write_idx[2])
+    assert torch.equal(after[w2], wl.backing[w2])
+    assert torch.isnan(out[4].cpu()).all()  # the skipped request's row
+    good = dataclasses.replace(wl, B=2, read_idx=wl.read_idx[:2],
+                               write_idx=wl.write_idx[:2], q=wl.q[:4],
+                               k=wl.k[:4], v=wl.v[:4], g=wl.g[:4],
+                               beta=wl.beta[:4],
+                               cu_seqlens=torch.tensor([0, 2, 4],
+                                                       dtype=torch.int32))
+    ref = oracle_run_varlen(good)
+    _, tol_out, _ = _tol(wl)
+    assert _err("abs", out[:4].cpu().float(), ref["out"]) <= tol_out
+
+
+def test_named_varlen_workload_parity():
+    wl = W.named("gdn_varlen_b64_t4")
+    before = wl.backing.clone()
+    got = gpu_run_varlen(wl)
+    check_varlen(wl, got, before, reqs=range(0, 64, 5))

@@ -58,10 +58,20 @@ class Workload:
     # writes no state and records every token; then the first
     # replay_tokens[b] records are replayed into write slot b
     replay_tokens: Optional[torch.Tensor] = None
+    # variable-length batch: int32 [B + 1] token offsets; q, k, v, g, beta
+    # are then token-packed ([total, ...]) and T is the longest request
+    cu_seqlens: Optional[torch.Tensor] = None
 
     @property
     def record_floats(self) -> int:
         return 2 * self.K + self.V
+
+    def counts(self) -> list:
+        """Tokens of each request."""
+        if self.cu_seqlens is None:
+            return [self.T] * self.B
+        cu = self.cu_seqlens.tolist()
+        return [cu[i + 1] - cu[i] for i in range(self.B)]
 
     def pool(self, backing: Optional[torch.Tensor] = None) -> torch.Tensor:
         """The logical pool [pool_size, HV, V, K]: every stride_mult-th slot
@@ -71,7 +81,7 @@ class Workload:
 
     @property
     def tokens(self) -> int:
-        return self.B * self.T
+        return sum(self.counts())
 
     def to(self, device) -> "Workload":
         """A copy with every tensor moved to ``device``."""
@@ -95,16 +105,18 @@ class Workload:
                            if r >= 0 and w >= 0 and 0 <= c <= self.T)
             # decode reads every active tile; replay reads and writes again
             return (active + 2 * replayed) * self.HV * tile
+        counts = self.counts()
         if self.token_slots is not None:
-            reads = writes = 0
-            for row, na in zip(self.token_slots.tolist(),
-                               self.num_accepted.tolist()):
-                if 1 <= na <= self.T and row[na - 1] >= 0:
+            reads = writes = cached = 0
+            for row, na, n in zip(self.token_slots.tolist(),
+                                  self.num_accepted.tolist(), counts):
+                if 1 <= na <= n and row[na - 1] >= 0:
                     reads += 1
-                    writes += sum(1 for s in row[: self.T] if s >= 0)
+                    writes += sum(1 for s in row[:n] if s >= 0)
+                    cached += n
             total = (reads + writes) * self.HV * tile
             if self.inter:
-                total += reads * self.T * self.HV * tile
+                total += cached * self.HV * tile
             return total
         ridx = self.read_idx.tolist()
         widx = self.write_idx.tolist() if self.write_idx is not None else ridx
@@ -112,7 +124,8 @@ class Workload:
         writes = sum(1 for r, w in zip(ridx, widx) if r >= 0 and w >= 0)
         total = (reads + writes) * self.HV * tile
         if self.inter:
-            total += reads * self.T * self.HV * tile
+            total += sum(n for r, n in zip(ridx, counts) if r >= 0) * \
+                self.HV * tile
         return total
 
     def io_bytes(self) -> int:
@@ -120,21 +133,24 @@ class Workload:
         beta, indices and outputs."""
         act = self.q.element_size()
         B, T, H, HV, K, V = self.B, self.T, self.H, self.HV, self.K, self.V
-        n = 2 * B * T * H * K * act + B * T * HV * V * act
+        N = self.tokens  # B T, or the packed token count
+        n = 2 * N * H * K * act + N * HV * V * act
         if self.variant == GDN:
-            n += B * T * HV * 4
+            n += N * HV * 4
         elif self.variant == KDA:
-            n += B * T * HV * K * 4
+            n += N * HV * K * 4
         elif self.g is not None:
             n += HV * 4
         if self.beta is not None:
-            n += B * T * HV * 4
+            n += N * HV * 4
         if self.token_slots is not None:
             n += B * T * 4 + B * 4
         else:
             n += B * 4 * (2 if self.write_idx is not None else 1)
+        if self.cu_seqlens is not None:
+            n += (B + 1) * 4
         out_size = torch.empty((), dtype=self.out_dtype).element_size()
-        n += B * T * HV * V * out_size
+        n += N * HV * V * out_size
         if self.replay_tokens is not None:
             rec = self.record_floats * 4 * HV
             n += B * T * rec  # records written by the decode
@@ -148,12 +164,33 @@ def _randperm(n, gen):
     return torch.randperm(n, generator=gen)
 
 
+def _packed(wl, gen, varlen_min):
+    """Turn the dense draws of ``wl`` into a variable-length batch."""
+    if varlen_min is None:
+        return wl
+    lengths = torch.randint(varlen_min, wl.T + 1, (wl.B,), generator=gen,
+                            dtype=torch.int32)
+    cu = torch.zeros((wl.B + 1,), dtype=torch.int32)
+    cu[1:] = torch.cumsum(lengths, 0)
+
+    def pack(x):
+        return torch.cat([x[b, :n] for b, n in enumerate(lengths.tolist())],
+                         0).contiguous()
+
+    wl.q, wl.k, wl.v = pack(wl.q), pack(wl.k), pack(wl.v)
+    if wl.variant != LIGHTNING:
+        wl.g, wl.beta = pack(wl.g), pack(wl.beta)
+    wl.cu_seqlens = cu
+    return wl
+
+
 def make(name, variant, B, T, H, HV, K, V, pool_size, *, seed,
          act_dtype=torch.bfloat16, pool_std=0.05, g_low=-1.0, g_high=0.0,
          l2norm=True, beta_logit=True, stride_mult=1, read_idx=None,
          write_idx=None, separate_write=False, write_skip=0.0,
          inter=False, lightning_decay=None, out_dtype=torch.float32,
-         paged=False, state_dtype=torch.float32, spec_replay=False):
+         paged=False, state_dtype=torch.float32, spec_replay=False,
+         varlen_min=None):
     """Draw one workload.
 
     paged: draw a [B, T] per-token slot table of distinct slots and accepted
@@ -161,6 +198,10 @@ def make(name, variant, B, T, H, HV, K, V, pool_size, *, seed,
     then hold the seed slots and -1 (informational only).
     spec_replay: a verify step with update records followed by a replay of
     replay_tokens[b] ~U{1..T} records into the (separate) write slots.
+
+    varlen_min: draw a variable-length batch, request b holding T_b ~
+    U{varlen_min..T} tokens (drawn last); the per-token tensors are then
+    token-packed and ``cu_seqlens`` holds the offsets.
 
     read_idx: explicit list, or None for ``randperm(pool_size)[:B]``.
     write_idx: explicit list, or None: equal to read_idx unless
@@ -189,15 +230,16 @@ def make(name, variant, B, T, H, HV, K, V, pool_size, *, seed,
         accepted = torch.randint(1, T + 1, (B,), generator=gen,
                                  dtype=torch.int32)
         seeds = table[torch.arange(B), accepted.long() - 1]
-        return Workload(name=name, variant=variant, B=B, T=T, H=H, HV=HV,
-                        K=K, V=V, pool_size=pool_size,
-                        l2norm=l2norm if variant != LIGHTNING else False,
-                        beta_logit=beta_logit if variant != LIGHTNING else False,
-                        q=q, k=k, v=v, g=g, beta=beta, backing=backing,
-                        stride_mult=stride_mult, read_idx=seeds.contiguous(),
-                        write_idx=torch.full((B,), -1, dtype=torch.int32),
-                        inter=inter, out_dtype=out_dtype, token_slots=table,
-                        num_accepted=accepted)
+        return _packed(Workload(
+            name=name, variant=variant, B=B, T=T, H=H, HV=HV, K=K, V=V,
+            pool_size=pool_size,
+            l2norm=l2norm if variant != LIGHTNING else False,
+            beta_logit=beta_logit if variant != LIGHTNING else False,
+            q=q, k=k, v=v, g=g, beta=beta, backing=backing,
+            stride_mult=stride_mult, read_idx=seeds.contiguous(),
+            write_idx=torch.full((B,), -1, dtype=torch.int32),
+            inter=inter, out_dtype=out_dtype, token_slots=table,
+            num_accepted=accepted), gen, varlen_min)
     if read_idx is None:
         if B > pool_size:
             raise ValueError("need pool_size >= B for distinct slots")
@@ -224,14 +266,15 @@ def make(name, variant, B, T, H, HV, K, V, pool_size, *, seed,
             raise ValueError("spec_replay needs separate write slots")
         replay_tokens = torch.randint(1, T + 1, (B,), generator=gen,
                                       dtype=torch.int32)
-    return Workload(name=name, variant=variant, B=B, T=T, H=H, HV=HV, K=K,
-                    V=V, pool_size=pool_size,
-                    l2norm=l2norm if variant != LIGHTNING else False,
-                    beta_logit=beta_logit if variant != LIGHTNING else False,
-                    q=q, k=k, v=v, g=g, beta=beta, backing=backing,
-                    stride_mult=stride_mult, read_idx=ridx, write_idx=widx,
-                    inter=inter, out_dtype=out_dtype,
-                    replay_tokens=replay_tokens)
+    return _packed(Workload(
+        name=name, variant=variant, B=B, T=T, H=H, HV=HV, K=K, V=V,
+        pool_size=pool_size,
+        l2norm=l2norm if variant != LIGHTNING else False,
+        beta_logit=beta_logit if variant != LIGHTNING else False,
+        q=q, k=k, v=v, g=g, beta=beta, backing=backing,
+        stride_mult=stride_mult, read_idx=ridx, write_idx=widx,
+        inter=inter, out_dtype=out_dtype,
+        replay_tokens=replay_tokens), gen, varlen_min)
 
 
 # The named workloads. Each is the shape, distribution and index structure of
@@ -310,6 +353,16 @@ def gdn_gva_b64_bf16_state(seed=3):
                 state_dtype=torch.bfloat16)
 
 
+def gdn_varlen_b64_t4(seed=8):
+    """GDN multi-token verify over a variable-length batch: B=64 requests
+    with T_b ~ U{1..4} tokens each (token-packed q/k/v/g/beta), H=16, HV=32,
+    K=V=128, pool of 128 with random distinct slots, every token's state
+    cached to a token-packed [total, HV, V, K] buffer."""
+    return make("gdn_varlen_b64_t4", GDN, B=64, T=4, H=16, HV=32, K=128,
+                V=128, pool_size=128, seed=seed, g_low=-0.5, g_high=0.0,
+                inter=True, varlen_min=1)
+
+
 NAMED = {
     "gdn_small_k64": gdn_small_k64,
     "lightning_b33_h64": lightning_b33_h64,
@@ -320,6 +373,7 @@ NAMED = {
     "gdn_paged_b64_t4": gdn_paged_b64_t4,
     "gdn_gva_b64_bf16_state": gdn_gva_b64_bf16_state,
     "kda_spec_b64_t4": kda_spec_b64_t4,
+    "gdn_varlen_b64_t4": gdn_varlen_b64_t4,
 }
 
 
