@@ -16,11 +16,13 @@ import subprocess
 
 import numpy as np
 
-__all__ = ["LIGHTNING", "GDN", "KDA", "L2NORM_QK", "BETA_LOGIT", "build",
+__all__ = ["LIGHTNING", "GDN", "KDA", "L2NORM_QK", "BETA_LOGIT", "GATE",
+           "GATE_LOWER_BOUND", "build",
            "decode", "replay", "lib_path"]
 
 LIGHTNING, GDN, KDA = 0, 1, 2
 L2NORM_QK, BETA_LOGIT = 1, 2
+GATE, GATE_LOWER_BOUND = 4, 8
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
@@ -59,7 +61,8 @@ def _load():
         lib.oracle_decode.argtypes = (
             [ctypes.c_int] * 8 + [dp] * 5 + [ctypes.c_int, dp, dp, ip, ip,
                                              dp, dp, ip, ctypes.c_int, ip,
-                                             dp, ip, ctypes.c_int])
+                                             dp, ip, ctypes.c_int, dp, dp,
+                                             ctypes.c_double])
         lib.oracle_replay.restype = ctypes.c_int
         lib.oracle_replay.argtypes = (
             [ctypes.c_int] * 5 + [dp, ctypes.c_int, dp, dp, ip, ip, ip, ip,
@@ -93,7 +96,8 @@ def _ptr(a, ctype):
 
 def decode(variant, q, k, v, g, beta, pool, read_idx, write_idx=None,
            flags=0, inter=False, token_slots=None, num_accepted=None,
-           factors=False, cu_seqlens=None, max_tokens=None):
+           factors=False, cu_seqlens=None, max_tokens=None, A_log=None,
+           dt_bias=None, lower_bound=None):
     """Run the fp64 recurrence.
 
     q, k: [B,T,H,K]; v: [B,T,HV,V]; g: Lightning [HV] decay factors or None,
@@ -105,6 +109,8 @@ def decode(variant, q, k, v, g, beta, pool, read_idx, write_idx=None,
     cu_seqlens: optional [B+1] offsets of a variable-length batch; then every
     per-token array is token-packed ([total, ...] in place of [B, T, ...]) and
     T is max_tokens (default: the longest request).
+    A_log [HV], dt_bias ([HV] GDN, [HV,K] KDA), lower_bound: the in-kernel
+    gate chain (g then holds the raw gate); see oracle.c for the reading.
 
     Returns a dict with ``out`` [B,T,HV,V], ``pool`` (the pool after the
     call, float64) and ``inter`` ([B,T,HV,V,K] or None).
@@ -157,6 +163,15 @@ def decode(variant, q, k, v, g, beta, pool, read_idx, write_idx=None,
         stride = slots.shape[1]
         ridx = np.full((B,), -1, dtype=np.int32)
         widx = None
+    a_log, dt = _f64(A_log), _f64(dt_bias)
+    if a_log is not None or dt is not None:
+        flags |= GATE
+        if a_log is None or dt is None or a_log.shape != (HV,) or \
+                dt.shape != ((HV,) if variant == GDN else (HV, K)):
+            raise ValueError("gate chain needs A_log [HV] and dt_bias "
+                             "[HV] (GDN) / [HV, K] (KDA)")
+    if lower_bound is not None:
+        flags |= GATE_LOWER_BOUND
     pool_out = pool_in.copy()
     # NaN until the oracle writes it: a position it skips cannot pass as 0
     out = np.full(lead + (HV, V), np.nan, dtype=np.float64)
@@ -171,7 +186,8 @@ def decode(variant, q, k, v, g, beta, pool, read_idx, write_idx=None,
         _ptr(pool_in, dp), _ptr(pool_out, dp), _ptr(ridx, ctypes.c_int32),
         _ptr(widx, ctypes.c_int32), _ptr(out, dp), _ptr(inter_a, dp),
         _ptr(slots, ctypes.c_int32), stride, _ptr(acc, ctypes.c_int32),
-        _ptr(fac, dp), _ptr(cu, ctypes.c_int32), total)
+        _ptr(fac, dp), _ptr(cu, ctypes.c_int32), total, _ptr(a_log, dp),
+        _ptr(dt, dp), float(lower_bound if lower_bound is not None else 0.0))
     if rc != 0:
         raise ValueError("oracle_decode rejected its arguments (rc=%d)" % rc)
     return {"out": out, "pool": pool_out, "inter": inter_a, "factors": fac}

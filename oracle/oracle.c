@@ -75,6 +75,17 @@
  * bound on T_b. A request with T_b = 0 runs no token: its state is written to
  * its write slot unchanged. With a slot table, the accepted count must lie in
  * [1, T_b].
+ *
+ * In-kernel gate chain (aiter KDA page, advisory review: the wrapper takes
+ * A_log, dt_bias with HV*K entries and lower_bound, and gate inputs given
+ * without use_gate_in_kernel must be refused). The pages name the inputs
+ * but not the formula; this oracle takes the plainest reading, the gated
+ * log-decay of the delta-rule models, and marks it "parity unpinned" against
+ * the pages. With the gate flag, g holds the raw gate x and the log-decay is
+ *     g' = -exp(A_log[hv]) * softplus(x + dt_bias)              (default)
+ *     g' = lower_bound * sigmoid(exp(A_log[hv]) * (x + dt_bias)) (bounded)
+ * with dt_bias[hv] (GDN, one per value head) or dt_bias[hv][k] (KDA, one per
+ * key channel); the decay is exp(g') as before.
  */
 #include <math.h>
 #include <stddef.h>
@@ -88,6 +99,8 @@
 
 #define ORACLE_L2NORM_QK 1
 #define ORACLE_BETA_LOGIT 2
+#define ORACLE_GATE 4             /* g is the raw gate of the gate chain */
+#define ORACLE_GATE_LOWER_BOUND 8 /* bounded (sigmoid) form of the chain */
 
 #define ORACLE_L2NORM_EPS 1e-6
 
@@ -100,6 +113,16 @@ static void l2_normalise(double *x, int n)
     double inv = 1.0 / sqrt(ss + ORACLE_L2NORM_EPS);
     for (int i = 0; i < n; ++i)
         x[i] *= inv;
+}
+
+/* The gate chain's log-decay for raw gate x (see the header comment). */
+static double gate_chain(double x, double a_log, double dt, int bounded,
+                         double lower_bound)
+{
+    const double z = x + dt;
+    if (bounded)
+        return lower_bound / (1.0 + exp(-exp(a_log) * z));
+    return -exp(a_log) * log1p(exp(z));
 }
 
 /* The standard Lightning Attention per-head decay. */
@@ -129,6 +152,8 @@ static double lightning_decay(int head, int num_heads)
  *   cu_seqlens  NULL, or [B + 1] non-decreasing offsets in [0, total] with
  *             cu_seqlens[b+1] - cu_seqlens[b] <= T; then every [B][T] pair
  *             of dimensions above is one [total] token dimension
+ *   A_log     [HV], dt_bias [HV] (GDN) or [HV][K] (KDA), lower_bound: the
+ *             gate chain, used when flags has ORACLE_GATE
  */
 int oracle_decode(int variant, int B, int T, int H, int HV, int K, int V,
                   int flags, const double *q, const double *k, const double *v,
@@ -137,9 +162,16 @@ int oracle_decode(int variant, int B, int T, int H, int HV, int K, int V,
                   const int32_t *read_idx, const int32_t *write_idx,
                   double *out, double *inter, const int32_t *slots,
                   int slots_stride, const int32_t *accepted, double *factors,
-                  const int32_t *cu_seqlens, int total)
+                  const int32_t *cu_seqlens, int total, const double *A_log,
+                  const double *dt_bias, double lower_bound)
 {
     if (B < 0 || T < 1 || H < 1 || HV < 1 || K < 1 || V < 1 || HV % H != 0)
+        return -1;
+    const int gate = (flags & ORACLE_GATE) != 0;
+    const int bounded = (flags & ORACLE_GATE_LOWER_BOUND) != 0;
+    if (gate && (variant == ORACLE_LIGHTNING || !A_log || !dt_bias))
+        return -1;
+    if (bounded && !gate)
         return -1;
     if (cu_seqlens)
         for (int b = 0; b < B; ++b)
@@ -157,10 +189,12 @@ int oracle_decode(int variant, int B, int T, int H, int HV, int K, int V,
     double *S = (double *)malloc(tile * sizeof(double));
     double *qv = (double *)malloc((size_t)K * sizeof(double));
     double *kv = (double *)malloc((size_t)K * sizeof(double));
-    if (!S || !qv || !kv) {
+    double *kdec = (double *)malloc((size_t)K * sizeof(double));
+    if (!S || !qv || !kv || !kdec) {
         free(S);
         free(qv);
         free(kv);
+        free(kdec);
         return -2;
     }
     const int group = HV / H;
@@ -181,6 +215,7 @@ int oracle_decode(int variant, int B, int T, int H, int HV, int K, int V,
                     free(S);
                     free(qv);
                     free(kv);
+                    free(kdec);
                     return -1;
                 }
         } else {
@@ -191,6 +226,7 @@ int oracle_decode(int variant, int B, int T, int H, int HV, int K, int V,
             free(S);
             free(qv);
             free(kv);
+            free(kdec);
             return -1;
         }
         for (int hv = 0; hv < HV; ++hv) {
@@ -240,7 +276,10 @@ int oracle_decode(int variant, int B, int T, int H, int HV, int K, int V,
                         bb = 1.0 / (1.0 + exp(-bb));
                     /* decay: S <- alpha S (GDN) or S <- S diag(exp g) (KDA) */
                     if (variant == ORACLE_GDN) {
-                        const double alpha = exp(g[bt]);
+                        const double alpha =
+                            exp(gate ? gate_chain(g[bt], A_log[hv], dt_bias[hv],
+                                                  bounded, lower_bound)
+                                     : g[bt]);
                         for (size_t e = 0; e < tile; ++e)
                             S[e] *= alpha;
                         if (rec)
@@ -248,12 +287,19 @@ int oracle_decode(int variant, int B, int T, int H, int HV, int K, int V,
                                 rec[j] = alpha;
                     } else {
                         const double *gk = g + bt * (size_t)K;
+                        /* the channel decays of this token */
+                        double *ek = kdec;
+                        for (int j = 0; j < K; ++j)
+                            ek[j] = exp(gate ? gate_chain(gk[j], A_log[hv],
+                                                          dt_bias[(size_t)hv * K + j],
+                                                          bounded, lower_bound)
+                                             : gk[j]);
                         for (int i = 0; i < V; ++i)
                             for (int j = 0; j < K; ++j)
-                                S[(size_t)i * K + j] *= exp(gk[j]);
+                                S[(size_t)i * K + j] *= ek[j];
                         if (rec)
                             for (int j = 0; j < K; ++j)
-                                rec[j] = exp(gk[j]);
+                                rec[j] = ek[j];
                     }
                     /* delta rule: S <- S + beta (v - S k) k^T, one row at a
                      * time (row i's read-out uses only row i) */
@@ -292,6 +338,7 @@ int oracle_decode(int variant, int B, int T, int H, int HV, int K, int V,
     free(S);
     free(qv);
     free(kv);
+    free(kdec);
     return 0;
 }
 

@@ -20,8 +20,8 @@ MUTATIONS = {
         "lam * S[(size_t)i * K + j] + vv[i] * kv[j];",
         "lam * S[(size_t)i * K + j] + vv[j % V] * kv[i % K];"),
     "gva_head_map": ("const int h = hv / group;", "const int h = hv % H;"),
-    "kda_decay_on_rows": ("S[(size_t)i * K + j] *= exp(gk[j]);",
-                          "S[(size_t)i * K + j] *= exp(gk[i % K]);"),
+    "kda_decay_on_rows": ("S[(size_t)i * K + j] *= ek[j];",
+                          "S[(size_t)i * K + j] *= ek[i % K];"),
     "write_to_read_slot": (
         "memcpy(pool_out + ((size_t)w * HV + hv) * tile, S,",
         "memcpy(pool_out + ((size_t)r * HV + hv) * tile, S,"),
@@ -56,6 +56,15 @@ MUTATIONS = {
     "varlen_replay_dense_records": (
         "const double *rec = factors + ((tok0 + t) * HV + hv) * rsz;",
         "const double *rec = factors + (((size_t)b * T + t) * HV + hv) * rsz;"),
+    "gate_softplus_sign": ("return -exp(a_log) * log1p(exp(z));",
+                           "return exp(a_log) * log1p(exp(z));"),
+    "gate_softplus_missing_a_log": ("return -exp(a_log) * log1p(exp(z));",
+                                    "return -log1p(exp(z));"),
+    "gate_sigmoid_scale_outside": (
+        "return lower_bound / (1.0 + exp(-exp(a_log) * z));",
+        "return lower_bound * exp(a_log) / (1.0 + exp(-z));"),
+    "gate_kda_dt_bias_transposed": ("dt_bias[(size_t)hv * K + j],",
+                                    "dt_bias[(size_t)j * HV + hv],"),
     "varlen_empty_request_skips_write": (
         "            if (w >= 0)\n                memcpy(pool_out + ((size_t)w * HV + hv) * tile, S,",
         "            if (w >= 0 && Tb > 0)\n                memcpy(pool_out + ((size_t)w * HV + hv) * tile, S,"),

@@ -721,3 +721,114 @@ def test_varlen_rejects_bad_offsets(cu):
         oracle.decode(oracle.GDN, p["q"][:4], p["k"][:4], p["v"][:4],
                       p["g"][:4], p["beta"][:4], c["pool"], [0, 1, 2],
                       cu_seqlens=np.array(cu, dtype=np.int32), max_tokens=3)
+
+
+# ------------------------------------------- in-kernel gate chain (a reading)
+# The pages name the chain's inputs but not its formula (parity unpinned
+# against the pages). These pins fix the implementation of the reading the
+# oracle states: closed forms of softplus and sigmoid at 0, the limits, and
+# the per-head / per-channel indexing of A_log and dt_bias.
+
+
+def _gate_case(variant, seed, HV=3, K=4):
+    rng = np.random.default_rng(seed)
+    c = _random_case(rng, variant, B=2, T=2, H=1, HV=HV, K=K, V=3,
+                     pool_size=4)
+    dt = rng.normal(size=(HV,) if variant == oracle.GDN else (HV, K))
+    return c, dt
+
+
+def _run_gate(variant, c, g, **kw):
+    return oracle.decode(variant, c["q"], c["k"], c["v"], g, c["beta"],
+                         c["pool"], [0, 2], [1, 3], inter=True,
+                         factors=True, **kw)
+
+
+def _decays(res, K):
+    return res["factors"][..., :K]
+
+
+@pytest.mark.parametrize("variant", [oracle.GDN, oracle.KDA])
+def test_gate_chain_softplus_at_zero_halves(variant):
+    """x + dt_bias = 0 with A_log = 0: g' = -softplus(0) = -ln 2, every decay
+    is exactly 1/2, and the call equals the ungated one with g = ln(1/2)."""
+    c, dt = _gate_case(variant, 300 + variant)
+    HV = dt.shape[0]
+    raw = -np.broadcast_to(dt[None, None] if variant == oracle.GDN
+                           else dt[None, None], c["g"].shape).copy()
+    gated = _run_gate(variant, c, raw, A_log=np.zeros(HV), dt_bias=dt)
+    np.testing.assert_allclose(_decays(gated, 4), 0.5, rtol=1e-15)
+    plain = _run_gate(variant, c, np.full(c["g"].shape, math.log(0.5)))
+    assert _rel(gated["out"], plain["out"]) < 1e-13
+    assert _rel(gated["pool"], plain["pool"]) < 1e-13
+
+
+@pytest.mark.parametrize("variant", [oracle.GDN, oracle.KDA])
+def test_gate_chain_scale_is_exp_a_log(variant):
+    """A_log = ln 3 at x + dt = 0: g' = -3 ln 2, decay 1/8 in every head."""
+    c, dt = _gate_case(variant, 310 + variant)
+    raw = -np.broadcast_to(dt[None, None], c["g"].shape).copy()
+    res = _run_gate(variant, c, raw, A_log=np.full(dt.shape[0], math.log(3)),
+                    dt_bias=dt)
+    np.testing.assert_allclose(_decays(res, 4), 0.125, rtol=1e-14)
+
+
+@pytest.mark.parametrize("variant", [oracle.GDN, oracle.KDA])
+def test_gate_chain_lower_bound_form(variant):
+    """Bounded form: at x + dt = 0 the decay is exp(lb / 2) whatever A_log;
+    far above 0 it tends to exp(lb), far below to 1; always inside
+    (exp(lb), 1)."""
+    c, dt = _gate_case(variant, 320 + variant)
+    HV = dt.shape[0]
+    a_log = np.random.default_rng(7).normal(size=HV)
+    raw = -np.broadcast_to(dt[None, None], c["g"].shape).copy()
+    lb = -5.0
+    mid = _run_gate(variant, c, raw, A_log=a_log, dt_bias=dt, lower_bound=lb)
+    np.testing.assert_allclose(_decays(mid, 4), math.exp(lb / 2), rtol=1e-14)
+    hi = _run_gate(variant, c, raw + 60.0, A_log=np.zeros(HV), dt_bias=dt,
+                   lower_bound=lb)
+    np.testing.assert_allclose(_decays(hi, 4), math.exp(lb), rtol=1e-12)
+    lo = _run_gate(variant, c, raw - 60.0, A_log=np.zeros(HV), dt_bias=dt,
+                   lower_bound=lb)
+    np.testing.assert_allclose(_decays(lo, 4), 1.0, rtol=1e-12)
+    rnd = _run_gate(variant, c, np.random.default_rng(8).normal(
+        size=c["g"].shape) * 3, A_log=a_log, dt_bias=dt, lower_bound=lb)
+    d = _decays(rnd, 4)
+    assert (d > math.exp(lb)).all() and (d < 1.0).all()
+
+
+def test_gate_chain_kda_channel_indexing():
+    """dt_bias is per (value head, key channel): raw gates equal to -dt_bias
+    of their own head and channel give decay 1/2 everywhere; the transposed
+    pattern does not."""
+    HV, K = 3, 4
+    c, dt = _gate_case(oracle.KDA, 330, HV=HV, K=K)
+    raw = -np.broadcast_to(dt[None, None], c["g"].shape).copy()
+    res = _run_gate(oracle.KDA, c, raw, A_log=np.zeros(HV), dt_bias=dt)
+    np.testing.assert_allclose(_decays(res, K), 0.5, rtol=1e-15)
+    wrong = -np.broadcast_to(dt.T.reshape(HV, K)[None, None], c["g"].shape)
+    res = _run_gate(oracle.KDA, c, wrong.copy(), A_log=np.zeros(HV),
+                    dt_bias=dt)
+    assert np.abs(_decays(res, K) - 0.5).max() > 1e-3
+
+
+def test_gate_chain_gdn_head_indexing_and_monotone():
+    """GDN: one dt_bias per value head; a larger raw gate decays more."""
+    c, dt = _gate_case(oracle.GDN, 340)
+    HV = dt.shape[0]
+    raw = -np.broadcast_to(dt[None, None], c["g"].shape).copy()
+    base = _decays(_run_gate(oracle.GDN, c, raw, A_log=np.zeros(HV),
+                             dt_bias=dt), 4)
+    np.testing.assert_allclose(base, 0.5, rtol=1e-15)
+    more = _decays(_run_gate(oracle.GDN, c, raw + 0.5, A_log=np.zeros(HV),
+                             dt_bias=dt), 4)
+    assert (more < base).all()
+
+
+def test_gate_chain_refused_where_it_has_no_meaning():
+    c, dt = _gate_case(oracle.GDN, 350)
+    with pytest.raises(ValueError):  # lower bound without the chain
+        _run_gate(oracle.GDN, c, c["g"], lower_bound=-5.0)
+    with pytest.raises(ValueError):  # dt_bias of the wrong shape
+        _run_gate(oracle.GDN, c, c["g"], A_log=np.zeros(3),
+                  dt_bias=np.zeros((3, 4)))
