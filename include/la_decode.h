@@ -82,7 +82,8 @@ typedef enum la_status {
     LA_ERR_DTYPE = 5,       /* unknown dtype code                            */
     LA_ERR_ARG = 6,         /* argument inconsistent with the entry point
                                (e.g. beta or flags given to la_decode, an
-                               unknown flag bit)                             */
+                               unknown flag bit, gate inputs without the
+                               gate flag, a nonzero reserved field)         */
     LA_ERR_UNSUPPORTED = 7, /* K or V not in {64, 128}                        */
     LA_ERR_LAUNCH = 8       /* the HIP runtime refused the launch            */
 } la_status;
@@ -95,6 +96,8 @@ typedef enum la_dtype {
 /* flags (GDN and KDA only; la_decode requires flags == 0) */
 #define LA_F_L2NORM_QK 0x1u  /* q, k <- x / sqrt(sum x^2 + 1e-6) per head */
 #define LA_F_BETA_LOGIT 0x2u /* beta holds logits; beta <- 1/(1+exp(-x))  */
+#define LA_F_GATE 0x4u       /* g holds the raw gate of the gate chain    */
+#define LA_F_GATE_LOWER_BOUND 0x8u /* bounded form of the gate chain     */
 
 /* Element strides of an activation tensor [B, T, heads, (inner)]. */
 typedef struct la_act_strides {
@@ -194,6 +197,25 @@ typedef struct la_decode_args {
     int32_t total_tokens; /* rows of the token-packed arrays (cu_seqlens
                              given), >= 0; ignored otherwise              */
     int32_t reserved;     /* must be 0                                    */
+
+    /* In-kernel gate chain (aiter KDA page, advisory review: the wrapper
+     * takes A_log, dt_bias with HV*K entries, lower_bound and
+     * use_gate_in_kernel, and gate inputs given without the switch must be
+     * refused; the pages do not state the formula, this is the library's
+     * reading). With LA_F_GATE (GDN, KDA), g holds the raw gate x and the
+     * log-decay becomes
+     *     -exp(A_log[hv]) * softplus(x + dt_bias)
+     * or, with LA_F_GATE_LOWER_BOUND,
+     *     lower_bound * sigmoid(exp(A_log[hv]) * (x + dt_bias)),
+     * where dt_bias is dt_bias[hv] (GDN) or dt_bias[hv][k] (KDA); the decay
+     * is exp of it, as without the chain. A_log [HV] and dt_bias ([HV] or
+     * [HV, K]) are fp32, contiguous, and required with LA_F_GATE (else
+     * LA_ERR_NULL); either given without LA_F_GATE, or
+     * LA_F_GATE_LOWER_BOUND without LA_F_GATE, is LA_ERR_ARG. */
+    const float *A_log;
+    const float *dt_bias;
+    float lower_bound;    /* with LA_F_GATE_LOWER_BOUND: finite, < 0      */
+    int32_t reserved2;    /* must be 0                                    */
 } la_decode_args;
 
 /* Arguments of la_replay. */
@@ -280,7 +302,8 @@ la_status la_check_cu_seqlens(int32_t B, int32_t T, int32_t total_tokens,
 const char *la_status_string(la_status status);
 
 /* Library version as major * 100 + minor (2.00: state_dtype and paged
- * per-token slots in la_decode_args; 2.10: variable-length batches). */
+ * per-token slots in la_decode_args; 2.10: variable-length batches; 2.20:
+ * the in-kernel gate chain). */
 int32_t la_version(void);
 
 #ifdef __cplusplus

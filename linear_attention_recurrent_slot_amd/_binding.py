@@ -24,6 +24,7 @@ STATUS_NAMES = {0: "LA_OK", 1: "LA_ERR_NULL", 2: "LA_ERR_SHAPE",
 LA_F32, LA_BF16 = 0, 1
 # flags
 LA_F_L2NORM_QK, LA_F_BETA_LOGIT = 0x1, 0x2
+LA_F_GATE, LA_F_GATE_LOWER_BOUND = 0x4, 0x8
 
 ENTRY_POINTS = ("la_decode", "gdn_decode_mtp", "kda_decode_mtp")
 
@@ -61,6 +62,8 @@ class DecodeArgs(ctypes.Structure):
         ("factors", ctypes.c_void_p),
         ("cu_seqlens", ctypes.c_void_p),
         ("total_tokens", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
+        ("lower_bound", ctypes.c_float), ("reserved2", ctypes.c_int32),
     ]
 
 
@@ -212,10 +215,34 @@ def _cu(cu_seqlens, max_tokens, dev):
     return B, max(1, int(max_tokens))
 
 
+def _gate_inputs(a, variant, A_log, dt_bias, lower_bound, HV, K, dev):
+    """Fill the gate-chain fields; returns the extra flag bits."""
+    if A_log is None and dt_bias is None and lower_bound is None:
+        return 0
+    if variant == "lightning":
+        raise ValueError("the gate chain applies to gdn and kda only")
+    if A_log is None or dt_bias is None:
+        raise ValueError("the gate chain needs both A_log and dt_bias")
+    want = (HV,) if variant == "gdn" else (HV, K)
+    for name, t, shape in (("A_log", A_log, (HV,)),
+                           ("dt_bias", dt_bias, want)):
+        if (t.dtype != torch.float32 or not t.is_contiguous()
+                or tuple(t.shape) != shape or t.device != dev):
+            raise ValueError("%s must be a contiguous float32 %s tensor on %s"
+                             % (name, shape, dev))
+    a.A_log = ctypes.c_void_p(A_log.data_ptr())
+    a.dt_bias = ctypes.c_void_p(dt_bias.data_ptr())
+    if lower_bound is None:
+        return LA_F_GATE
+    a.lower_bound = float(lower_bound)
+    return LA_F_GATE | LA_F_GATE_LOWER_BOUND
+
+
 def build_args(variant: str, q, k, v, g, beta, pool, read_idx, write_idx,
                out, inter, flags: int, token_slots=None,
                num_accepted=None, factors=None, cu_seqlens=None,
-               max_tokens=None) -> DecodeArgs:
+               max_tokens=None, A_log=None, dt_bias=None,
+               lower_bound=None) -> DecodeArgs:
     vl = cu_seqlens is not None
     if vl:
         # token-packed: q, k [total, H, K], v [total, HV, V], ...
@@ -316,12 +343,15 @@ def build_args(variant: str, q, k, v, g, beta, pool, read_idx, write_idx,
     if vl:
         a.cu_seqlens = ctypes.c_void_p(cu_seqlens.data_ptr())
         a.total_tokens = total
+    a.flags = flags | _gate_inputs(a, variant, A_log, dt_bias, lower_bound,
+                                   HV, K, dev)
     return a
 
 
 def _run(variant, entry, q, k, v, g, beta, pool, read_idx, write_idx, out,
          inter, flags, out_dtype, stream, token_slots=None,
-         num_accepted=None, factors=None, cu_seqlens=None, max_tokens=None):
+         num_accepted=None, factors=None, cu_seqlens=None, max_tokens=None,
+         A_log=None, dt_bias=None, lower_bound=None):
     lead = tuple(q.shape[:-2])  # (B, T), or (total,) with cu_seqlens
     HV, V, K = v.shape[-2], v.shape[-1], q.shape[-1]
     if out is None:
@@ -333,7 +363,7 @@ def _run(variant, entry, q, k, v, g, beta, pool, read_idx, write_idx, out,
         inter = None
     args = build_args(variant, q, k, v, g, beta, pool, read_idx, write_idx,
                       out, inter, flags, token_slots, num_accepted, factors,
-                      cu_seqlens, max_tokens)
+                      cu_seqlens, max_tokens, A_log, dt_bias, lower_bound)
     st = call(entry, args, stream)
     if st != LA_OK:
         raise LaDecodeError(st, entry)
@@ -348,6 +378,9 @@ def _run(variant, entry, q, k, v, g, beta, pool, read_idx, write_idx, out,
 # offsets) the batch is variable-length: every per-token tensor is
 # token-packed ([total, ...] in place of [B, T, ...]) and max_tokens bounds
 # the tokens of one request (None: read back from the offsets, a sync).
+# gdn_decode_mtp / kda_decode_mtp: A_log ([HV]) and dt_bias ([HV] for GDN,
+# [HV, K] for KDA), float32, switch the in-kernel gate chain on (g is then
+# the raw gate); lower_bound selects its bounded form.
 
 def la_decode(q, k, v, pool, read_idx=None, write_idx=None, *, lam=None,
               out=None, inter=None, out_dtype=torch.float32, stream=None,
@@ -364,28 +397,33 @@ def gdn_decode_mtp(q, k, v, g, beta, pool, read_idx=None, write_idx=None, *,
                    out=None, inter=None, l2norm_qk=False, beta_logit=False,
                    out_dtype=torch.float32, stream=None, token_slots=None,
                    num_accepted=None, factors=None, cu_seqlens=None,
-                   max_tokens=None):
-    """Gated delta rule decode over T tokens. g: [B,T,HV] log-decay;
-    beta: [B,T,HV] (logits if beta_logit). Returns (out, inter)."""
+                   max_tokens=None, A_log=None, dt_bias=None,
+                   lower_bound=None):
+    """Gated delta rule decode over T tokens. g: [B,T,HV] log-decay (the
+    raw gate with A_log/dt_bias); beta: [B,T,HV] (logits if beta_logit).
+    Returns (out, inter)."""
     flags = (LA_F_L2NORM_QK if l2norm_qk else 0) | \
         (LA_F_BETA_LOGIT if beta_logit else 0)
     return _run("gdn", "gdn_decode_mtp", q, k, v, g, beta, pool, read_idx,
                 write_idx, out, inter, flags, out_dtype, stream, token_slots,
-                num_accepted, factors, cu_seqlens, max_tokens)
+                num_accepted, factors, cu_seqlens, max_tokens, A_log,
+                dt_bias, lower_bound)
 
 
 def kda_decode_mtp(q, k, v, g, beta, pool, read_idx=None, write_idx=None, *,
                    out=None, inter=None, l2norm_qk=False, beta_logit=False,
                    out_dtype=torch.float32, stream=None, token_slots=None,
                    num_accepted=None, factors=None, cu_seqlens=None,
-                   max_tokens=None):
-    """KDA decode over T tokens. g: [B,T,HV,K] per-key-channel log-decay.
-    Returns (out, inter)."""
+                   max_tokens=None, A_log=None, dt_bias=None,
+                   lower_bound=None):
+    """KDA decode over T tokens. g: [B,T,HV,K] per-key-channel log-decay
+    (the raw gate with A_log/dt_bias). Returns (out, inter)."""
     flags = (LA_F_L2NORM_QK if l2norm_qk else 0) | \
         (LA_F_BETA_LOGIT if beta_logit else 0)
     return _run("kda", "kda_decode_mtp", q, k, v, g, beta, pool, read_idx,
                 write_idx, out, inter, flags, out_dtype, stream, token_slots,
-                num_accepted, factors, cu_seqlens, max_tokens)
+                num_accepted, factors, cu_seqlens, max_tokens, A_log,
+                dt_bias, lower_bound)
 
 
 def check_indices(read_idx, write_idx, pool_size, result=None, stream=None):

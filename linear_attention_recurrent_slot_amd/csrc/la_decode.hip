@@ -62,33 +62,40 @@ static_assert(kRowsPerWave == 16 || kRowsPerWave == 32, "16 or 32 rows");
 constexpr int kTokChunk = 8;
 constexpr float kL2Eps = 1e-6f;
 
+// Activation strides are 32-bit: the host checks that every element offset
+// of q, k, v, g, beta and out fits in 31 bits (the pool keeps 64-bit
+// strides), which keeps the kernels' scalar registers within budget.
 struct Params {
     int32_t B, T, HV, group;  // group = HV / H
     uint32_t flags;
     int32_t stream_loads;  // 1: nontemporal state loads, 0: cached loads
     const void *q;
-    int64_t sq_b, sq_t, sq_h;
+    int32_t sq_b, sq_t, sq_h;
     const void *k;
-    int64_t sk_b, sk_t, sk_h;
+    int32_t sk_b, sk_t, sk_h;
     const void *v;
-    int64_t sv_b, sv_t, sv_h;
+    int32_t sv_b, sv_t, sv_h;
     const float *g;
-    int64_t sg_b, sg_t, sg_h;
+    int32_t sg_b, sg_t, sg_h;
     const float *beta;
-    int64_t sb_b, sb_t, sb_h;
+    int32_t sb_b, sb_t, sb_h;
     void *pool;  // fp32 or bf16 elements (state dtype)
     int64_t sp_slot, sp_head, sp_row;
     const int32_t *ridx;
     const int32_t *widx;
     void *inter;  // state dtype
     void *out;
-    int64_t so_b, so_t, so_h;
+    int32_t so_b, so_t, so_h;
     const int32_t *tslots;  // paged per-token slot table, or null
     int64_t ts_stride;
     const int32_t *naccept;
     float *factors;  // [B, T, HV, 2K + V] per-token records, or null
     const int32_t *cu;  // [B + 1] token offsets of a varlen batch, or null
     int32_t total;      // rows of the token-packed arrays (with cu)
+    int32_t gate;       // gate chain: 0 off, 1 softplus form, 2 bounded form
+    const float *A_log;    // [HV]
+    const float *dt_bias;  // [HV] (GDN) or [HV, K] (KDA)
+    float lower_bound;
 };
 
 // ---------------------------------------------------------------- helpers
@@ -310,6 +317,22 @@ struct TokRaw {
     float g, beta;
 };
 
+// Log-decay of the gate chain for z = raw gate + dt_bias:
+// -exp(A_log) softplus(z), or lower_bound sigmoid(exp(A_log) z) in the
+// bounded form. Hardware exp, log and reciprocal (about 1 ulp each):
+// softplus(z) = log(1 + e^z) loses only terms below 2^-24 of the decay, and
+// z > 20 takes softplus = z.
+__device__ __forceinline__ float gate_chain(const Params &p, float z,
+                                            float a_log)
+{
+    const float a = __expf(a_log);
+    if (p.gate == 2)
+        return p.lower_bound *
+               __builtin_amdgcn_rcpf(1.f + __expf(-a * z));
+    const float sp = z > 20.f ? z : __logf(1.f + __expf(z));
+    return -a * sp;
+}
+
 // First half of the prologue of token t: global loads only, so they can be
 // issued ahead of the state tile and arrive first.
 template <int VAR, int K, int V, bool BF16IN>
@@ -320,16 +343,19 @@ __device__ __forceinline__ void prologue_load(const Params &p, int b, int hv,
     constexpr int EPL = K / 64;  // key elements per lane
     constexpr int VPL = V / 64;  // value elements per lane
     const int h = hv / p.group;
-    const int64_t qo = b * p.sq_b + t * p.sq_t + h * p.sq_h;
-    const int64_t ko = b * p.sk_b + t * p.sk_t + h * p.sk_h;
-    const int64_t vo = b * p.sv_b + t * p.sv_t + hv * p.sv_h;
-    const int64_t go = b * p.sg_b + t * p.sg_t + hv * p.sg_h;
+    const int32_t qo = b * p.sq_b + t * p.sq_t + h * p.sq_h;
+    const int32_t ko = b * p.sk_b + t * p.sk_t + h * p.sk_h;
+    const int32_t vo = b * p.sv_b + t * p.sv_t + hv * p.sv_h;
+    const int32_t go = b * p.sg_b + t * p.sg_t + hv * p.sg_h;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         raw.q[i] = load_act<BF16IN>(p.q, qo + lane * EPL + i);
         raw.k[i] = load_act<BF16IN>(p.k, ko + lane * EPL + i);
-        if constexpr (VAR == VAR_KDA)
-            raw.e[i] = p.g[go + lane * EPL + i];
+        if constexpr (VAR == VAR_KDA) {
+            // with the gate chain: z = raw gate + dt_bias of the channel
+            raw.e[i] = p.g[go + lane * EPL + i] +
+                       (p.gate ? p.dt_bias[hv * K + lane * EPL + i] : 0.f);
+        }
     }
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
@@ -338,7 +364,9 @@ __device__ __forceinline__ void prologue_load(const Params &p, int b, int hv,
         raw.g = p.g ? p.g[hv] : 0.f;
         raw.beta = 1.f;
     } else {
-        raw.g = (VAR == VAR_GDN) ? p.g[go] : 0.f;
+        raw.g = (VAR == VAR_GDN)
+                    ? p.g[go] + (p.gate ? p.dt_bias[hv] : 0.f)
+                    : 0.f;
         raw.beta = p.beta[b * p.sb_b + t * p.sb_t + hv * p.sb_h];
     }
 }
@@ -376,8 +404,10 @@ __device__ __forceinline__ void prologue_finish(const Params &p, int hv,
         decay = p.g ? raw.g
                     : __expf(-exp2f(-8.f * static_cast<float>(hv + 1) /
                                     static_cast<float>(p.HV)));
+    else if constexpr (VAR == VAR_GDN)
+        decay = __expf(p.gate ? gate_chain(p, raw.g, p.A_log[hv]) : raw.g);
     else
-        decay = (VAR == VAR_GDN) ? __expf(raw.g) : 1.f;
+        decay = 1.f;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int j = lane * EPL + i;
@@ -386,7 +416,8 @@ __device__ __forceinline__ void prologue_finish(const Params &p, int hv,
         rec[L::qOff + j] = raw.q[i] * rq;
         float a = decay;
         if constexpr (VAR == VAR_KDA) {
-            a = __expf(raw.e[i]);
+            a = __expf(p.gate ? gate_chain(p, raw.e[i], p.A_log[hv])
+                              : raw.e[i]);
             rec[L::eOff + j] = a;
         }
         if (frec) {
@@ -498,7 +529,7 @@ decode_kernel(const Params p)
     // rows exactly once): row R wave + 8 c8 + rs.
     const int orow = wave * kRowsPerWave + (c8 & (RPL - 1)) * 8 + rs;
     const bool olane = c8 < RPL;
-    const int64_t obase = b * p.so_b + tok0 * p.so_t + hv * p.so_h + orow;
+    const int32_t obase = b * p.so_b + tok0 * p.so_t + hv * p.so_h + orow;
 
     if (r < 0) {  // padded request: zero outputs, touch nothing else
         if (olane)
@@ -711,7 +742,7 @@ __global__ void __launch_bounds__(V) decode_packed_kernel(const Params p)
     const int r = __builtin_amdgcn_readfirstlane(p.ridx[b]);
     const int w = __builtin_amdgcn_readfirstlane(p.widx ? p.widx[b] : r);
     // every lane writes one output row: R wave + 8 c8 + rs
-    const int64_t oidx = b * p.so_b + hv * p.so_h + wave * R + c8 * 8 + rs;
+    const int32_t oidx = b * p.so_b + hv * p.so_h + wave * R + c8 * 8 + rs;
     if (r < 0) {
         store_out<BF16OUT>(p.out, oidx, 0.f);
         return;
@@ -1154,6 +1185,28 @@ bool strides_nonneg(const la_act_strides &s)
     return s.b >= 0 && s.t >= 0 && s.h >= 0;
 }
 
+// Whether every element offset of an activation tensor [nb, nt, nh, inner]
+// (strides s, innermost stride 1) fits in 31 bits.
+bool fits31(const la_act_strides &s, int64_t nb, int64_t nt, int64_t nh,
+            int64_t inner)
+{
+    if (nb < 1 || nt < 1 || nh < 1)
+        return true;  // nothing is indexed
+    const int64_t st[3] = {s.b, s.t, s.h};
+    const int64_t ex[3] = {nb - 1, nt - 1, nh - 1};
+    int64_t off = inner - 1;
+    for (int i = 0; i < 3; ++i) {
+        if (ex[i] == 0)
+            continue;
+        if (st[i] > INT32_MAX || ex[i] > INT32_MAX)
+            return false;
+        off += st[i] * ex[i];  // each term < 2^62, at most three of them
+        if (off > INT32_MAX)
+            return false;
+    }
+    return off <= INT32_MAX;
+}
+
 // True when the n blocks (extent[i] copies at stride[i]) of `inner`
 // contiguous elements never overlap: sorted by stride, each stride must
 // clear everything nested inside it.
@@ -1195,16 +1248,27 @@ la_status validate(const la_decode_args *a, int var)
         (a->out_dtype != LA_F32 && a->out_dtype != LA_BF16) ||
         (a->state_dtype != LA_F32 && a->state_dtype != LA_BF16))
         return LA_ERR_DTYPE;
-    if (a->reserved != 0)
+    if (a->reserved != 0 || a->reserved2 != 0)
         return LA_ERR_ARG;
     if (a->cu_seqlens && a->total_tokens < 0)
         return LA_ERR_SHAPE;
     if (var == VAR_LA) {
-        if (a->flags != 0 || a->beta != nullptr)
+        if (a->flags != 0 || a->beta != nullptr || a->A_log || a->dt_bias)
             return LA_ERR_ARG;
     } else {
-        if (a->flags & ~(LA_F_L2NORM_QK | LA_F_BETA_LOGIT))
+        if (a->flags & ~(LA_F_L2NORM_QK | LA_F_BETA_LOGIT | LA_F_GATE |
+                         LA_F_GATE_LOWER_BOUND))
             return LA_ERR_ARG;
+        const bool gate = (a->flags & LA_F_GATE) != 0;
+        // gate inputs without the switch are refused, not ignored
+        if (!gate && (a->A_log || a->dt_bias ||
+                      (a->flags & LA_F_GATE_LOWER_BOUND)))
+            return LA_ERR_ARG;
+        if ((a->flags & LA_F_GATE_LOWER_BOUND) &&
+            !(a->lower_bound < 0.f && a->lower_bound > -3.0e38f))
+            return LA_ERR_ARG;
+        if (gate && a->B > 0 && (!a->A_log || !a->dt_bias))
+            return LA_ERR_NULL;
     }
     if (static_cast<int64_t>(a->B) * a->HV > INT32_MAX)
         return LA_ERR_SHAPE;
@@ -1237,6 +1301,21 @@ la_status validate(const la_decode_args *a, int var)
         return LA_ERR_STRIDE;
     if (var != VAR_LA && (!strides_nonneg(a->sg) || !strides_nonneg(a->sbeta)))
         return LA_ERR_STRIDE;
+    {
+        // 32-bit activation offsets (per-request b strides unused when
+        // the batch is token-packed)
+        const int64_t nb = a->cu_seqlens ? 1 : a->B;
+        const int64_t nt = a->cu_seqlens ? a->total_tokens : a->T;
+        if (!fits31(a->sq, nb, nt, a->H, a->K) ||
+            !fits31(a->sk, nb, nt, a->H, a->K) ||
+            !fits31(a->sv, nb, nt, a->HV, a->V) ||
+            !fits31(a->so, nb, nt, a->HV, a->V))
+            return LA_ERR_STRIDE;
+        if (var != VAR_LA &&
+            (!fits31(a->sg, nb, nt, a->HV, var == VAR_KDA ? a->K : 1) ||
+             !fits31(a->sbeta, nb, nt, a->HV, 1)))
+            return LA_ERR_STRIDE;
+    }
     if (a->sp.slot < 0 || a->sp.head < 0 || a->sp.row < 0)
         return LA_ERR_STRIDE;
 
@@ -1283,7 +1362,8 @@ la_status validate(const la_decode_args *a, int var)
         return LA_ERR_ALIGN;
     if (a->factors && !aligned(a->factors, 16))
         return LA_ERR_ALIGN;
-    if (!aligned(a->cu_seqlens, 4))
+    if (!aligned(a->cu_seqlens, 4) || !aligned(a->A_log, 4) ||
+        !aligned(a->dt_bias, 4))
         return LA_ERR_ALIGN;
     return LA_OK;
 }
@@ -1337,6 +1417,12 @@ la_status launch(const la_decode_args *a, void *stream, int var)
     p.factors = a->factors;
     p.cu = a->cu_seqlens;
     p.total = a->cu_seqlens ? a->total_tokens : 0;
+    p.gate = !(a->flags & LA_F_GATE)            ? 0
+             : (a->flags & LA_F_GATE_LOWER_BOUND) ? 2
+                                                 : 1;
+    p.A_log = a->A_log;
+    p.dt_bias = a->dt_bias;
+    p.lower_bound = a->lower_bound;
     if (a->cu_seqlens) {
         // token-packed arrays: the flat token number goes through the t
         // strides, so the per-request strides drop out
@@ -1566,6 +1652,6 @@ const char *la_status_string(la_status s)
     return "unknown status";
 }
 
-int32_t la_version(void) { return 210; }
+int32_t la_version(void) { return 220; }
 
 }  // extern "C"

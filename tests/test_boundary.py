@@ -150,7 +150,7 @@ REJECT = [
     ("out_dtype_code", _mut(out_dtype=3), "lightning", 5),
     ("beta_for_lightning", _mut(beta=FAKE), "lightning", 6),
     ("flags_for_lightning", _mut(flags=1), "lightning", 6),
-    ("unknown_flag_bit", _mut(flags=4), "gdn", 6),
+    ("unknown_flag_bit", _mut(flags=16), "gdn", 6),
     ("negative_q_stride", _mut(sq=bnd.ActStrides(-1, 0, 0)), "gdn", 3),
     ("negative_pool_stride", _mut(sp=bnd.PoolStrides(-4, 0, 128)), "gdn", 3),
     ("pool_rows_overlap", _mut(sp=bnd.PoolStrides(4 * 128 * 128 * 4,
@@ -202,6 +202,19 @@ REJECT = [
                                    total_tokens=-1), "kda", 2),
     ("varlen_misaligned_offsets", _mut(cu_seqlens=FAKE + 0x900002,
                                        total_tokens=8), "lightning", 4),
+    # gate chain: inputs without the switch are refused, not ignored
+    ("gate_inputs_without_flag", _mut(A_log=FAKE + 0xa00000), "kda", 6),
+    ("dt_bias_without_flag", _mut(dt_bias=FAKE + 0xa00100), "gdn", 6),
+    ("gate_flag_without_inputs", _mut(flags=3 | 4), "kda", 1),
+    ("lower_bound_without_gate", _mut(flags=3 | 8), "gdn", 6),
+    ("lower_bound_not_negative", _mut(flags=3 | 4 | 8, A_log=FAKE + 0xa00000,
+                                      dt_bias=FAKE + 0xa00100,
+                                      lower_bound=0.5), "kda", 6),
+    ("gate_for_lightning", _mut(A_log=FAKE + 0xa00000,
+                                dt_bias=FAKE + 0xa00100), "lightning", 6),
+    ("gate_misaligned", _mut(flags=3 | 4, A_log=FAKE + 0xa00002,
+                             dt_bias=FAKE + 0xa00100), "gdn", 4),
+    ("reserved2_nonzero", _mut(reserved2=1), "gdn", 6),
     # packed outputs [total, HV, V]: rows of consecutive tokens overlap
     ("varlen_out_tokens_overlap", _mut(cu_seqlens=FAKE + 0x900000,
                                        total_tokens=8,

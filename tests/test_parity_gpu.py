@@ -1265,3 +1265,97 @@ def test_named_varlen_workload_parity():
     before = wl.backing.clone()
     got = gpu_run_varlen(wl)
     check_varlen(wl, got, before, reqs=range(0, 64, 5))
+
+
+# ------------------------------------------------ in-kernel gate chain
+
+
+def _gate_inputs(variant, HV, K, seed):
+    gen = torch.Generator().manual_seed(seed)
+    a_log = torch.log(1 + 15 * torch.rand(HV, generator=gen))  # A in [1, 16]
+    dt = torch.randn((HV,) if variant == W.GDN else (HV, K), generator=gen)
+    return a_log.float(), dt.float()
+
+
+def _gate_run(wl, a_log, dt, lower_bound):
+    """GPU and oracle runs of a gated workload (wl.g holds raw gates)."""
+    lad = _lad()
+    d = wl.to(DEV)
+    pool = d.backing[:: wl.stride_mult]
+    fn = lad.gdn_decode_mtp if wl.variant == W.GDN else lad.kda_decode_mtp
+    fac = torch.full((wl.B, wl.T, wl.HV, 2 * wl.K + wl.V), float("nan"),
+                     device=DEV)
+    out, inter = fn(d.q, d.k, d.v, d.g, d.beta, pool, d.read_idx,
+                    d.write_idx, inter=wl.inter, l2norm_qk=wl.l2norm,
+                    beta_logit=wl.beta_logit, factors=fac,
+                    A_log=a_log.to(DEV), dt_bias=dt.to(DEV),
+                    lower_bound=lower_bound)
+    torch.cuda.synchronize()
+    ref = oracle.decode(VARIANT_CODE[wl.variant], wl.q, wl.k, wl.v, wl.g,
+                        wl.beta, wl.pool(), wl.read_idx, wl.write_idx,
+                        flags=_flags(wl), inter=wl.inter, factors=True,
+                        A_log=a_log, dt_bias=dt, lower_bound=lower_bound)
+    return {"out": out.cpu(), "backing": d.backing.cpu(),
+            "inter": None if inter is None else inter.cpu(),
+            "factors": fac.cpu()}, ref
+
+
+@pytest.mark.parametrize("variant", [W.GDN, W.KDA])
+@pytest.mark.parametrize("lower_bound", [None, -5.0], ids=["softplus", "lb"])
+@pytest.mark.parametrize("T,state", [(3, torch.float32), (1, torch.float32),
+                                     (1, torch.bfloat16)],
+                         ids=["t3", "t1", "t1_bf16_state"])
+def test_gate_chain_parity(variant, lower_bound, T, state):
+    """The in-kernel gate chain (this library's reading of the pages' A_log
+    / dt_bias / lower_bound inputs) against the oracle's, with the raw gate
+    ~ N(0, 2^2), A in [1, 16], dt_bias ~ N(0, 1); one bf16-state case runs
+    the packed one-token kernel."""
+    seed = 5000 + 10 * [W.GDN, W.KDA].index(variant) + T + (
+        5 if lower_bound is None else 0) + (100 if state != torch.float32
+                                           else 0)
+    wl = W.make("gate", variant, B=5, T=T, H=2, HV=4, K=128, V=128,
+                pool_size=12, seed=seed, separate_write=True,
+                write_skip=0.2, inter=state == torch.float32,
+                state_dtype=state)
+    wl.g = 2 * torch.randn(wl.g.shape, generator=torch.Generator()
+                           .manual_seed(seed + 1))
+    a_log, dt = _gate_inputs(variant, wl.HV, wl.K, seed + 2)
+    got, ref = _gate_run(wl, a_log, dt, lower_bound)
+    kind, tol_out, tol_state = _tol(wl)
+    assert _err(kind, got["out"].float(), ref["out"]) <= tol_out
+    m = wl.stride_mult
+    widx = wl.write_idx.tolist()
+    for b, w in enumerate(widx):
+        if w >= 0:
+            err = _state_err(wl, kind, tol_state,
+                             got["backing"][m * w].float().numpy(),
+                             ref["pool"][w])
+            assert err <= (0.0 if state != torch.float32 else tol_state), b
+    if wl.inter:
+        assert _err(kind, got["inter"].float(), ref["inter"]) <= tol_state
+    # the decays themselves (record field a): fp32 exp/log vs fp64. A few
+    # ulp of error in the log-decay g' become |g'| times that, relative, in
+    # exp(g'); decays below fp32 range (exp(-128) at A = 16) flush to 0,
+    # hence the floor
+    a_gpu = got["factors"][..., :wl.K].double().numpy()
+    a_ref = ref["factors"][..., :wl.K]
+    bound = 1e-6 * (1 + np.abs(np.log(a_ref))) * a_ref + 1e-12
+    assert np.all(np.abs(a_gpu - a_ref) <= bound)
+
+
+@pytest.mark.parametrize("variant", [W.GDN, W.KDA])
+def test_gate_chain_closed_form_on_gpu(variant):
+    """x + dt_bias = 0 with A_log = 0: every decay is 1/2 (softplus(0) =
+    ln 2); in the bounded form exp(lb / 2) for any A_log."""
+    wl = W.make("gatecf", variant, B=3, T=2, H=1, HV=2, K=128, V=128,
+                pool_size=6, seed=5100 + len(variant))
+    a_log, dt = _gate_inputs(variant, wl.HV, wl.K, 5101)
+    raw = -dt.expand(wl.g.shape) if variant == W.KDA else \
+        -dt.view(1, 1, -1).expand(wl.g.shape)
+    wl.g = raw.contiguous()
+    got, _ = _gate_run(wl, torch.zeros_like(a_log), dt, None)
+    np.testing.assert_allclose(got["factors"][..., :wl.K].numpy(), 0.5,
+                               rtol=2e-6)
+    got, _ = _gate_run(wl, a_log, dt, -3.0)
+    np.testing.assert_allclose(got["factors"][..., :wl.K].numpy(),
+                               np.exp(-1.5), rtol=2e-6)
