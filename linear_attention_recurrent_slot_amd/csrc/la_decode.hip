@@ -663,13 +663,13 @@ decode_kernel(const Params p)
             if (olane)
                 store_out<BF16OUT>(p.out, obase + t * p.so_t, mine);
             if constexpr (REC) {
-                // lane (c8 = i, rs) stores err of its row R w + 8 i + rs
-                float *ferr = factor_record<K, V>(p, flat0 + t, hv) + 2 * K +
-                              wave * kRowsPerWave + rs;
+                // err of row orow, by the lane that writes its output
+                float cm = c[0];
 #pragma unroll
-                for (int i = 0; i < RPL; ++i)
-                    if (c8 == i)
-                        ferr[i * 8] = c[i];
+                for (int i = 1; i < RPL; ++i)
+                    cm = (c8 == i) ? c[i] : cm;
+                if (olane)
+                    factor_record<K, V>(p, flat0 + t, hv)[2 * K + orow] = cm;
             }
 
             if (p.tslots) {

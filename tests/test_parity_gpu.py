@@ -1359,3 +1359,52 @@ def test_gate_chain_closed_form_on_gpu(variant):
     got, _ = _gate_run(wl, a_log, dt, -3.0)
     np.testing.assert_allclose(got["factors"][..., :wl.K].numpy(),
                                np.exp(-1.5), rtol=2e-6)
+
+
+# --------------------------------------------- untouched-slot sentinels
+
+
+def _fill_sentinels(wl):
+    """Overwrite every backing slot that no active request reads or writes
+    (stride gaps included) with NaN bit patterns carrying payloads, so that
+    any stray read-modify-write (which would canonicalise or recompute them)
+    changes bits."""
+    m = wl.stride_mult
+    ridx = wl.read_idx.tolist()
+    widx = (wl.write_idx if wl.write_idx is not None else wl.read_idx).tolist()
+    used = {m * r for r in ridx if r >= 0}
+    used |= {m * w for r, w in zip(ridx, widx) if r >= 0 and w >= 0}
+    bits = _bits(wl.backing)  # int32 or int16 view, shares storage
+    if wl.backing.dtype == torch.float32:
+        pats = torch.tensor([0x7FA5A5A5, -0x003F4111, 0x7F800001,
+                             -0x00000001], dtype=torch.int32)
+    else:
+        pats = torch.tensor([0x7FA5, -0x007F, 0x7F81, -0x0001],
+                            dtype=torch.int16)
+    flat_n = bits[0].numel()
+    pattern = pats.repeat(flat_n // 4 + 1)[:flat_n].view(bits.shape[1:])
+    filled = []
+    for s in range(bits.shape[0]):
+        if s not in used:
+            bits[s] = pattern
+            filled.append(s)
+    return filled
+
+
+@pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN, W.KDA])
+@pytest.mark.parametrize("state", [torch.float32, torch.bfloat16],
+                         ids=["f32state", "bf16state"])
+@pytest.mark.parametrize("T", [1, 3])
+def test_untouched_slots_keep_nan_payload_sentinels(variant, state, T):
+    wl = W.make("sentinel", variant, B=5, T=T, H=2, HV=2, K=128, V=128,
+                pool_size=14, seed=5200 + 10 * T + len(variant)
+                + (7 if state == torch.bfloat16 else 0), stride_mult=2,
+                read_idx=[3, -1, 9, 0, 12], write_idx=[5, 7, -1, 0, 1],
+                inter=True, state_dtype=state)
+    filled = _fill_sentinels(wl)
+    assert len(filled) > wl.pool_size  # gaps and unused logical slots
+    snapshot = _bits(wl.backing).clone()
+    got = run_and_check(wl)  # parity, plus the bytewise check of every slot
+    after = _bits(got["backing"])
+    for s in filled:
+        assert torch.equal(after[s], snapshot[s]), s
