@@ -1408,3 +1408,46 @@ def test_untouched_slots_keep_nan_payload_sentinels(variant, state, T):
     after = _bits(got["backing"])
     for s in filled:
         assert torch.equal(after[s], snapshot[s]), s
+
+
+# ------------------------------------------------------- HIP graph capture
+
+
+@pytest.mark.parametrize("variant", [W.GDN, W.KDA])
+def test_hip_graph_capture_replays_match_eager(variant):
+    """A decode captured in a HIP graph and replayed four times (with eager
+    work and synchronisation between replays) reproduces the eager call bit
+    for bit: the call launches one kernel and allocates, clears and
+    synchronises nothing. Read and write slots are disjoint, so every replay
+    starts from the same states."""
+    lad = _lad()
+    wl = W.make("graph", variant, B=4, T=3, H=2, HV=4, K=128, V=128,
+                pool_size=12, seed=5300 + len(variant), separate_write=True,
+                inter=True)
+    d = wl.to(DEV)
+    pool = d.backing[:: wl.stride_mult]
+    fn = lad.gdn_decode_mtp if variant == W.GDN else lad.kda_decode_mtp
+    kw = dict(l2norm_qk=wl.l2norm, beta_logit=wl.beta_logit)
+    out = torch.empty((wl.B, wl.T, wl.HV, wl.V), device=DEV)
+    inter = torch.empty((wl.B, wl.T, wl.HV, wl.V, wl.K), device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up off the default stream
+        fn(d.q, d.k, d.v, d.g, d.beta, pool, d.read_idx, d.write_idx,
+           out=out, inter=inter, **kw)
+    torch.cuda.synchronize()
+    eager = (out.clone(), inter.clone(), d.backing.clone())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn(d.q, d.k, d.v, d.g, d.beta, pool, d.read_idx, d.write_idx,
+           out=out, inter=inter, **kw)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        inter.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(out), _bits(eager[0])), rep
+        assert torch.equal(_bits(inter), _bits(eager[1])), rep
+        assert torch.equal(_bits(d.backing), _bits(eager[2])), rep
