@@ -7,9 +7,13 @@ of synthetic input resident in HBM. Prints one JSON line.
 Timing: W untimed warm-up calls, then K timed calls bracketed by
 torch.cuda.synchronize(). Two HIP events on the stream the kernels are
 launched on bracket the K back-to-back launches; their elapsed time / K is
-the kernel's average launch duration used for the roofline. The calls rotate over R independent copies of the pool and
-inputs (R x bytes-per-call >= 1 GiB) so that the 256 MB Infinity Cache cannot
-serve the state: every call reads its tiles from HBM.
+the kernel's average launch duration used for the roofline. The calls
+rotate over R independent copies of the pool and inputs, R x bytes-per-call
+>= 4 GiB (16 times the 256 MB Infinity Cache; at most 512 copies, a limit only
+the launch-bound small workload reaches), so that no call finds its tiles in
+the cache: on MI355X a 1 GiB rotation still let cached loads reuse lines
+across calls (GDN B=128 with cached loads: 77 % of peak at 1 GiB, 63 % at
+3 GiB).
 """
 import argparse
 import hashlib
@@ -26,6 +30,8 @@ if ROOT not in sys.path:
 METRIC = ("decode tokens/sec and achieved HBM GB/s (% of peak), K=V=128 fp32 "
           "state")
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
+ROTATE_BYTES = 4 << 30  # bytes the rotated copies span (16 x the MALL)
+ROTATE_MAX = 512
 DEFAULT_WORKLOAD = "lightning_b33_h64"
 KERNEL_SRC = os.path.join(ROOT, "linear_attention_recurrent_slot_amd", "csrc",
                           "la_decode.hip")
@@ -39,7 +45,7 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--rotate", type=int, default=0,
-                    help="pool copies to rotate over (0: enough for 1 GiB)")
+                    help="pool copies to rotate over (0: enough for 4 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU time budget of the oracle baseline (0: skip)")
     ap.add_argument("--no-copy-probe", action="store_true")
@@ -247,7 +253,7 @@ def main():
     wl = workloads.named(args.workload)
     per_call = wl.state_bytes() + wl.io_bytes()
     pool_bytes = wl.backing.numel() * wl.backing.element_size()
-    R = args.rotate or max(1, math.ceil((1 << 30) / per_call))
+    R = args.rotate or min(ROTATE_MAX, max(2, math.ceil(ROTATE_BYTES / per_call)))
     print("[bench] workload %s: B=%d T=%d H=%d HV=%d K=%d V=%d pool=%d, "
           "%.1f MB per call, rotating %d copies (%.2f GB of pools)"
           % (wl.name, wl.B, wl.T, wl.H, wl.HV, wl.K, wl.V, wl.pool_size,

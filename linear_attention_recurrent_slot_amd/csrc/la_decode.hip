@@ -38,8 +38,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <map>
-#include <mutex>
 
 #include "la_decode.h"
 
@@ -51,14 +49,15 @@ enum Variant { VAR_LA = 0, VAR_GDN = 1, VAR_KDA = 2 };
 
 // Tunables (compile-time; the defaults are the measured best on MI355X).
 #ifndef LA_ROWS_PER_WAVE
-#define LA_ROWS_PER_WAVE 32  // state rows a wave keeps in VGPRs: 16 or 32
+#define LA_ROWS_PER_WAVE 32  // state rows a wave keeps in VGPRs: 8, 16 or 32
 #endif
 #ifndef LA_WAVES_PER_EU
 #define LA_WAVES_PER_EU 0  // >0: ask the register allocator for this occupancy
 #endif
 
 constexpr int kRowsPerWave = LA_ROWS_PER_WAVE;
-static_assert(kRowsPerWave == 16 || kRowsPerWave == 32, "16 or 32 rows");
+static_assert(kRowsPerWave == 8 || kRowsPerWave == 16 || kRowsPerWave == 32,
+              "8, 16 or 32 rows");
 constexpr int kTokChunk = 8;
 constexpr float kL2Eps = 1e-6f;
 
@@ -68,7 +67,6 @@ constexpr float kL2Eps = 1e-6f;
 struct Params {
     int32_t B, T, HV, group;  // group = HV / H
     uint32_t flags;
-    int32_t stream_loads;  // 1: nontemporal state loads, 0: cached loads
     const void *q;
     int32_t sq_b, sq_t, sq_h;
     const void *k;
@@ -160,6 +158,27 @@ __device__ __forceinline__ float sum8(float x)
     return x;
 }
 
+__device__ __forceinline__ float dpp_row_mirror(float x)
+{
+    return __int_as_float(
+        __builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, true));
+}
+
+// Sum over groups of L = 8, 16 or 32 consecutive lanes, bit-identical in all
+// L lanes (each step adds a lane pair's values in both lanes; the last step
+// swaps the two 16-lane rows of each 32-lane half with ds_swizzle, xor 16).
+template <int L>
+__device__ __forceinline__ float sum_lanes(float x)
+{
+    x = sum8(x);
+    if constexpr (L >= 16)
+        x += dpp_row_mirror(x);
+    if constexpr (L >= 32)
+        x += __int_as_float(
+            __builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+    return x;
+}
+
 // Sum over the whole wave (prologue only).
 __device__ __forceinline__ float wave_sum(float x)
 {
@@ -177,8 +196,10 @@ typedef __amdgpu_buffer_rsrc_t BufRsrc;
 typedef unsigned u4 __attribute__((ext_vector_type(4)));
 constexpr int kBufDword3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format
 // Cache-policy bits of the state tile's buffer accesses (gfx950: 2 = nt).
-constexpr int kStreamPolicy = 2;  // nontemporal: the tile is used once
-constexpr int kCachedPolicy = 0;
+// Every tile load and store streams: a tile is used once per call, and on
+// MI355X streaming loads measured as fast as or faster than cached loads for
+// every workload once the Infinity Cache cannot keep tiles between calls.
+constexpr int kStreamPolicy = 2;
 
 __device__ __forceinline__ BufRsrc make_rsrc(const void *base, uint32_t bytes)
 {
@@ -548,17 +569,10 @@ decode_kernel(const Params p)
     const BufRsrc src = make_rsrc(
         pool + (r * p.sp_slot + hv * p.sp_head) * ES, tile_bytes);
     f4 S[RPL][CPL];
-    if (p.stream_loads) {
 #pragma unroll
-        for (int i = 0; i < RPL; ++i)
-            IO::template load_row<kStreamPolicy>(
-                S[i], src, lane_off, (wave * kRowsPerWave + i * 8) * row_bytes);
-    } else {
-#pragma unroll
-        for (int i = 0; i < RPL; ++i)
-            IO::template load_row<kCachedPolicy>(
-                S[i], src, lane_off, (wave * kRowsPerWave + i * 8) * row_bytes);
-    }
+    for (int i = 0; i < RPL; ++i)
+        IO::template load_row<kStreamPolicy>(
+            S[i], src, lane_off, (wave * kRowsPerWave + i * 8) * row_bytes);
 
     for (int t0 = 0; t0 < Tb; t0 += kTokChunk) {
         const int nt = min(kTokChunk, Tb - t0);
@@ -758,23 +772,13 @@ __global__ void __launch_bounds__(V) decode_packed_kernel(const Params p)
     const BufRsrc src = make_rsrc(
         pool + (r * p.sp_slot + hv * p.sp_head) * ES, tile_bytes);
     u4 P[RPL][NCH];
-    if (p.stream_loads) {
 #pragma unroll
-        for (int i = 0; i < RPL; ++i)
+    for (int i = 0; i < RPL; ++i)
 #pragma unroll
-            for (int j = 0; j < NCH; ++j)
-                P[i][j] = __builtin_amdgcn_raw_buffer_load_b128(
-                    src, lane_off + j * 128u, (wave * R + i * 8) * row_bytes,
-                    kStreamPolicy);
-    } else {
-#pragma unroll
-        for (int i = 0; i < RPL; ++i)
-#pragma unroll
-            for (int j = 0; j < NCH; ++j)
-                P[i][j] = __builtin_amdgcn_raw_buffer_load_b128(
-                    src, lane_off + j * 128u, (wave * R + i * 8) * row_bytes,
-                    kCachedPolicy);
-    }
+        for (int j = 0; j < NCH; ++j)
+            P[i][j] = __builtin_amdgcn_raw_buffer_load_b128(
+                src, lane_off + j * 128u, (wave * R + i * 8) * row_bytes,
+                kStreamPolicy);
 
     if (wave == 0) {
         TokRaw<K, V> rw;
@@ -866,6 +870,147 @@ __global__ void __launch_bounds__(V) decode_packed_kernel(const Params p)
         }
     }
     store_out<BF16OUT>(p.out, oidx, mine);
+}
+
+// One token of Lightning or GDN on an fp32 pool with no per-token writes.
+// Each load instruction of a wave reads 1 KiB of contiguous tile bytes
+// (64 lanes x 16 B: two rows at K = 128, four at K = 64); on MI355X an
+// in-place tile update moved that way keeps HBM busier than rows split into
+// 128-byte pieces. A wave owns 8 rows, so a workgroup has V / 8 waves; lane
+// (cl = lane % (K/4), rl = lane / (K/4)) holds columns 4 cl .. 4 cl + 3 of
+// rows 8 wave + RPI j + rl, and a row's dot products are summed over its K/4
+// lanes (a different summation order from decode_kernel's, so the two agree
+// to fp32 rounding, not bit for bit). Every wave forms the token prologue it
+// needs itself (its columns of q and k, its rows of v, the scalars): no LDS
+// and no barrier, and those loads are issued before the tile's.
+template <int VAR, int K, int V, bool BF16IN, bool BF16OUT>
+__global__ void __launch_bounds__((V / 8) * 64) decode1_kernel(const Params p)
+{
+    static_assert(VAR != VAR_KDA, "KDA one-token calls use decode_kernel");
+    constexpr int LPR = K / 4;     // lanes per row
+    constexpr int RPI = 64 / LPR;  // rows per load instruction
+    constexpr int RPL = 8 / RPI;   // rows per lane
+
+    const int pair = blockIdx.x;
+    const int b = pair / p.HV;
+    const int hv = pair - b * p.HV;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int cl = lane % LPR;
+    const int rl = lane / LPR;
+
+    const int r = __builtin_amdgcn_readfirstlane(p.ridx[b]);
+    const int w = __builtin_amdgcn_readfirstlane(p.widx ? p.widx[b] : r);
+    // lane cl = j (< RPL) writes the output of its row j
+    const bool olane = cl < RPL;
+    const int orow = 8 * wave + RPI * (olane ? cl : 0) + rl;
+    const int32_t oidx = b * p.so_b + hv * p.so_h + orow;
+    if (r < 0) {
+        if (olane)
+            store_out<BF16OUT>(p.out, oidx, 0.f);
+        return;
+    }
+
+    // token inputs of this lane
+    const int h = hv / p.group;
+    const int32_t qo = b * p.sq_b + h * p.sq_h + 4 * cl;
+    const int32_t ko = b * p.sk_b + h * p.sk_h + 4 * cl;
+    const int32_t vo = b * p.sv_b + hv * p.sv_h + 8 * wave + rl;
+    const int32_t go = b * p.sg_b + hv * p.sg_h;
+    float qv[4], kv[4], vv[RPL];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        qv[i] = load_act<BF16IN>(p.q, qo + i);
+        kv[i] = load_act<BF16IN>(p.k, ko + i);
+    }
+#pragma unroll
+    for (int j = 0; j < RPL; ++j)
+        vv[j] = load_act<BF16IN>(p.v, vo + RPI * j);
+    float gs = 0.f, bs = 1.f;
+    if constexpr (VAR == VAR_GDN)
+        gs = p.g[go] + (p.gate ? p.dt_bias[hv] : 0.f);
+    if constexpr (VAR != VAR_LA)
+        bs = p.beta[b * p.sb_b + hv * p.sb_h];
+
+    // the tile rows of this lane
+    const uint32_t row_bytes = static_cast<uint32_t>(p.sp_row) * 4u;
+    const uint32_t tile_bytes = static_cast<uint32_t>(
+        (static_cast<int64_t>(V - 1) * p.sp_row + K) * 4);
+    const uint32_t lane_off = rl * row_bytes + cl * 16u;
+    char *const pool = static_cast<char *>(p.pool);
+    const BufRsrc src = make_rsrc(
+        pool + (r * p.sp_slot + hv * p.sp_head) * 4, tile_bytes);
+    f4 S[RPL];
+#pragma unroll
+    for (int j = 0; j < RPL; ++j)
+        S[j] = __builtin_bit_cast(
+            f4, __builtin_amdgcn_raw_buffer_load_b128(
+                    src, lane_off, (8 * wave + RPI * j) * row_bytes,
+                    kStreamPolicy));
+
+    // prologue: l2norm over K (the row's lanes hold all K columns), k.q,
+    // beta, decay
+    float ssq = 0.f, ssk = 0.f, qk = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        ssq = fmaf(qv[i], qv[i], ssq);
+        ssk = fmaf(kv[i], kv[i], ssk);
+        qk = fmaf(qv[i], kv[i], qk);
+    }
+    qk = sum_lanes<LPR>(qk);
+    float rq = 1.f, rk = 1.f;
+    if (p.flags & LA_F_L2NORM_QK) {
+        rq = __frsqrt_rn(sum_lanes<LPR>(ssq) + kL2Eps);
+        rk = __frsqrt_rn(sum_lanes<LPR>(ssk) + kL2Eps);
+    }
+    const float kq = qk * rq * rk;
+    f4 kk = {kv[0] * rk, kv[1] * rk, kv[2] * rk, kv[3] * rk};
+    const f4 qq = {qv[0] * rq, qv[1] * rq, qv[2] * rq, qv[3] * rq};
+    float decay;
+    if constexpr (VAR == VAR_LA)
+        decay = p.g ? p.g[hv]
+                    : __expf(-exp2f(-8.f * static_cast<float>(hv + 1) /
+                                    static_cast<float>(p.HV)));
+    else
+        decay = __expf(p.gate ? gate_chain(p, gs, p.A_log[hv]) : gs);
+    float beta = 1.f;
+    if constexpr (VAR != VAR_LA)
+        beta = (p.flags & LA_F_BETA_LOGIT) ? 1.f / (1.f + __expf(-bs)) : bs;
+
+    float mine = 0.f;
+#pragma unroll
+    for (int j = 0; j < RPL; ++j) {
+        S[j] *= decay;
+        float u = 0.f, wq = 0.f;
+        if constexpr (VAR != VAR_LA) {
+            u = fmaf(S[j].x, kk.x, u);
+            u = fmaf(S[j].y, kk.y, u);
+            u = fmaf(S[j].z, kk.z, u);
+            u = fmaf(S[j].w, kk.w, u);
+            u = sum_lanes<LPR>(u);
+        }
+        wq = fmaf(S[j].x, qq.x, wq);
+        wq = fmaf(S[j].y, qq.y, wq);
+        wq = fmaf(S[j].z, qq.z, wq);
+        wq = fmaf(S[j].w, qq.w, wq);
+        wq = sum_lanes<LPR>(wq);
+        const float c = (VAR == VAR_LA) ? vv[j] : beta * (vv[j] - u);
+        mine = (cl == j) ? fmaf(c, kq, wq) : mine;
+        S[j].x = fmaf(c, kk.x, S[j].x);
+        S[j].y = fmaf(c, kk.y, S[j].y);
+        S[j].z = fmaf(c, kk.z, S[j].z);
+        S[j].w = fmaf(c, kk.w, S[j].w);
+    }
+    if (olane)
+        store_out<BF16OUT>(p.out, oidx, mine);
+    if (w >= 0) {
+        const BufRsrc dst = make_rsrc(
+            pool + (w * p.sp_slot + hv * p.sp_head) * 4, tile_bytes);
+#pragma unroll
+        for (int j = 0; j < RPL; ++j)
+            store_b128(__builtin_bit_cast(u4, S[j]), dst, lane_off,
+                       (8 * wave + RPI * j) * row_bytes);
+    }
 }
 
 struct ReplayParams {
@@ -1133,6 +1278,26 @@ KernelFn pick_packed(int K, int V, bool bi, bool bo)
                     : pick_packed<VAR, 64, 64>(bi, bo);
 }
 
+template <int VAR, int K, int V>
+KernelFn pick_one(bool bi, bool bo)
+{
+    if (bi)
+        return bo ? decode1_kernel<VAR, K, V, true, true>
+                  : decode1_kernel<VAR, K, V, true, false>;
+    return bo ? decode1_kernel<VAR, K, V, false, true>
+              : decode1_kernel<VAR, K, V, false, false>;
+}
+
+template <int VAR>
+KernelFn pick_one(int K, int V, bool bi, bool bo)
+{
+    if (K == 128)
+        return V == 128 ? pick_one<VAR, 128, 128>(bi, bo)
+                        : pick_one<VAR, 128, 64>(bi, bo);
+    return V == 128 ? pick_one<VAR, 64, 128>(bi, bo)
+                    : pick_one<VAR, 64, 64>(bi, bo);
+}
+
 template <int VAR>
 KernelFn pick(int K, int V, bool bi, bool bo, bool bs, bool rec)
 {
@@ -1141,33 +1306,6 @@ KernelFn pick(int K, int V, bool bi, bool bo, bool bs, bool rec)
                         : pick_dtype<VAR, 128, 64>(bi, bo, bs, rec);
     return V == 128 ? pick_dtype<VAR, 64, 128>(bi, bo, bs, rec)
                     : pick_dtype<VAR, 64, 64>(bi, bo, bs, rec);
-}
-
-// Workgroups of `fn` that the current device holds at once (compute units
-// times workgroups per unit), looked up once per device and kernel; 0 when
-// the runtime cannot say.
-int64_t resident_blocks(KernelFn fn, int block, size_t lds)
-{
-    static std::mutex mu;
-    static std::map<std::pair<int, const void *>, int64_t> cache;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess)
-        return 0;
-    const auto key = std::make_pair(dev, reinterpret_cast<const void *>(fn));
-    std::lock_guard<std::mutex> lock(mu);
-    const auto it = cache.find(key);
-    if (it != cache.end())
-        return it->second;
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
-                              dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void *>(fn), block, lds) !=
-            hipSuccess)
-        return 0;
-    const int64_t n = static_cast<int64_t>(cus) * per_cu;
-    cache[key] = n;
-    return n;
 }
 
 int lds_floats_per_token(int var, int K, int V)
@@ -1435,11 +1573,22 @@ la_status launch(const la_decode_args *a, void *stream, int var)
     // one token on a bf16 pool with no per-token writes: packed tile
     const bool packed = bs && a->T == 1 && !a->inter && !a->token_slots &&
                         !rec && !a->cu_seqlens;
+    // One token of Lightning or GDN on an fp32 pool with no per-token
+    // writes, over at least 2048 tiles: the contiguous-row kernel. Measured
+    // on MI355X (4 GiB rotation): Lightning B=33 H=64 71.0 -> 74.3 % of
+    // peak, GDN B=64 HV=32 66.8 -> 68.7 %; at 512 tiles it was 9 % slower,
+    // and KDA (B=256, HV=24) 1 % slower, so those keep decode_kernel.
+    const bool one = var != VAR_KDA && !bs && a->T == 1 && !a->inter &&
+                     !a->token_slots && !rec && !a->cu_seqlens &&
+                     static_cast<int64_t>(a->B) * a->HV >= 2048;
     KernelFn fn;
     if (packed)
         fn = var == VAR_LA    ? pick_packed<VAR_LA>(a->K, a->V, bi, bo)
              : var == VAR_GDN ? pick_packed<VAR_GDN>(a->K, a->V, bi, bo)
                               : pick_packed<VAR_KDA>(a->K, a->V, bi, bo);
+    else if (one)
+        fn = var == VAR_LA ? pick_one<VAR_LA>(a->K, a->V, bi, bo)
+                           : pick_one<VAR_GDN>(a->K, a->V, bi, bo);
     else
         fn = var == VAR_LA    ? pick<VAR_LA>(a->K, a->V, bi, bo, bs, rec)
              : var == VAR_GDN ? pick<VAR_GDN>(a->K, a->V, bi, bo, bs, rec)
@@ -1448,23 +1597,12 @@ la_status launch(const la_decode_args *a, void *stream, int var)
     const size_t lds = static_cast<size_t>(chunk) *
                        lds_floats_per_token(var, a->K, a->V) * sizeof(float);
     const dim3 grid(static_cast<unsigned>(a->B) * a->HV);
-    // 64 rows per wave in the packed kernel, kRowsPerWave otherwise
-    const dim3 block(packed ? a->V : (a->V / kRowsPerWave) * 64);
+    // rows per wave: 64 in the packed kernel, 8 in the one-token fp32
+    // kernel, kRowsPerWave otherwise
+    const dim3 block(packed ? a->V
+                     : one  ? (a->V / 8) * 64
+                            : (a->V / kRowsPerWave) * 64);
 
-    // State-load cache policy, from measurements on MI355X: streaming
-    // (nontemporal) loads, except cached loads for calls that also write
-    // per-token states and for delta-rule calls of one or two tokens whose
-    // grid is more than 1.5 rounds of resident workgroups (small grids of
-    // those calls are faster streaming). The bf16 KDA one-token kernel
-    // measured faster streaming at every size.
-    bool nt = true;
-    if (a->inter || a->token_slots)
-        nt = false;
-    else if (var != VAR_LA && a->T <= 2 && !(packed && var == VAR_KDA)) {
-        const int64_t res = resident_blocks(fn, block.x, lds);
-        nt = res > 0 && 2 * static_cast<int64_t>(grid.x) <= 3 * res;
-    }
-    p.stream_loads = nt;
     void *kargs[] = {&p};
     const hipError_t e =
         hipLaunchKernel(reinterpret_cast<const void *>(fn), grid, block,

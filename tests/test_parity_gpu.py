@@ -1451,3 +1451,82 @@ def test_hip_graph_capture_replays_match_eager(variant):
         assert torch.equal(_bits(out), _bits(eager[0])), rep
         assert torch.equal(_bits(inter), _bits(eager[1])), rep
         assert torch.equal(_bits(d.backing), _bits(eager[2])), rep
+
+
+# ------------------------------- one-token fp32 kernel (grids >= 2048 tiles)
+
+
+@pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN])
+@pytest.mark.parametrize("K,V", SHAPES)
+@pytest.mark.parametrize("dtype,out", [(torch.float32, torch.float32),
+                                       (torch.bfloat16, torch.float32),
+                                       (torch.bfloat16, torch.bfloat16)],
+                         ids=["f32", "bf16", "bf16_out_bf16"])
+def test_one_token_kernel_parity(variant, K, V, dtype, out):
+    """Lightning/GDN, T = 1, fp32 pool, B * HV = 2048 tiles: the
+    contiguous-row one-token kernel. Padded requests, separate and skipped
+    writes on a strided pool; sampled requests against the oracle, every
+    untouched byte checked."""
+    seed = (6000 + 100 * [W.LIGHTNING, W.GDN].index(variant)
+            + 10 * SHAPES.index((K, V)) + (5 if dtype != torch.float32 else 0)
+            + (2 if out != torch.float32 else 0))
+    B, HV = 64, 32
+    ridx = list(range(0, 2 * B, 2))
+    widx = [s + 1 for s in ridx]
+    for b in (3, 17, 40):
+        ridx[b] = -1  # padded
+    for b in (5, 22, 63):
+        widx[b] = -1  # skipped write
+    wl = W.make("one", variant, B=B, T=1, H=16, HV=HV, K=K, V=V,
+                pool_size=2 * B, seed=seed, act_dtype=dtype, pool_std=0.1,
+                stride_mult=2 if K == V else 1, read_idx=ridx,
+                write_idx=widx, out_dtype=out)
+    run_and_check(wl, reqs=[0, 3, 5, 11, 17, 22, 40, 47, 63])
+
+
+def test_one_token_kernel_gate_chain():
+    """The gate chain (both forms) in the one-token GDN kernel."""
+    wl = W.make("onegate", W.GDN, B=64, T=1, H=16, HV=32, K=128, V=128,
+                pool_size=128, seed=6300, separate_write=True)
+    wl.g = 2 * torch.randn(wl.g.shape, generator=torch.Generator()
+                           .manual_seed(6301))
+    a_log, dt = _gate_inputs(W.GDN, wl.HV, wl.K, 6302)
+    for lb in (None, -5.0):
+        got, ref = _gate_run(wl, a_log, dt, lb)
+        kind, tol_out, tol_state = _tol(wl)
+        assert _err(kind, got["out"].float(), ref["out"]) <= tol_out
+        for b, w in enumerate(wl.write_idx.tolist()):
+            if w >= 0:
+                assert _err(kind, got["backing"][w].float(),
+                            ref["pool"][w]) <= tol_state, b
+
+
+@pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN])
+def test_one_token_kernel_token_split_within_rounding(variant):
+    """T single-token calls (one-token kernel) against one T-token call
+    (decode_kernel): equal to fp32 rounding; the kernels sum each dot
+    product in a different order, so not bit for bit."""
+    lad = _lad()
+    T = 3
+    wl = W.make("onesplit", variant, B=64, T=T, H=16, HV=32, K=128, V=128,
+                pool_size=64, seed=6400 + len(variant),
+                act_dtype=torch.float32)
+    whole = gpu_run(wl)
+    d = wl.to(DEV)
+    pool = d.backing
+    outs = []
+    for t in range(T):
+        sl = slice(t, t + 1)
+        if variant == W.LIGHTNING:
+            o, _ = lad.la_decode(d.q[:, sl], d.k[:, sl], d.v[:, sl], pool,
+                                 d.read_idx, lam=d.g)
+        else:
+            o, _ = lad.gdn_decode_mtp(d.q[:, sl], d.k[:, sl], d.v[:, sl],
+                                      d.g[:, sl], d.beta[:, sl], pool,
+                                      d.read_idx, l2norm_qk=wl.l2norm,
+                                      beta_logit=wl.beta_logit)
+        outs.append(o)
+    torch.cuda.synchronize()
+    split_out = torch.cat(outs, 1).cpu()
+    assert _err("rel", split_out, whole["out"]) <= 2e-6
+    assert _err("rel", pool.cpu(), whole["backing"]) <= 2e-6
