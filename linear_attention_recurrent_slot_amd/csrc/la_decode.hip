@@ -872,24 +872,28 @@ __global__ void __launch_bounds__(V) decode_packed_kernel(const Params p)
     store_out<BF16OUT>(p.out, oidx, mine);
 }
 
-// One token of Lightning or GDN on an fp32 pool with no per-token writes.
-// Each load instruction of a wave reads 1 KiB of contiguous tile bytes
-// (64 lanes x 16 B: two rows at K = 128, four at K = 64); on MI355X an
-// in-place tile update moved that way keeps HBM busier than rows split into
-// 128-byte pieces. A wave owns 8 rows, so a workgroup has V / 8 waves; lane
-// (cl = lane % (K/4), rl = lane / (K/4)) holds columns 4 cl .. 4 cl + 3 of
-// rows 8 wave + RPI j + rl, and a row's dot products are summed over its K/4
-// lanes (a different summation order from decode_kernel's, so the two agree
-// to fp32 rounding, not bit for bit). Every wave forms the token prologue it
-// needs itself (its columns of q and k, its rows of v, the scalars): no LDS
-// and no barrier, and those loads are issued before the tile's.
-template <int VAR, int K, int V, bool BF16IN, bool BF16OUT>
+// One token of Lightning or GDN with no per-token writes. Each load
+// instruction of a wave reads 1 KiB of contiguous tile bytes (64 lanes x
+// 16 B: 2 to 8 whole rows); on MI355X an in-place tile update moved that way
+// keeps HBM busier than rows split into 128-byte pieces. A wave owns 8 rows,
+// so a workgroup has V / 8 waves. Lane (cl = lane % LPR, rl = lane / LPR)
+// holds the 16-byte chunk cl of rows 8 wave + RPI j + rl (4 fp32 or 8 bf16
+// columns, widened to fp32 in registers), and a row's dot products are
+// summed over its LPR lanes: a different summation order from
+// decode_kernel's, so the two agree to fp32 rounding, not bit for bit. Every
+// wave forms the token prologue it needs itself (its columns of q and k, its
+// rows of v, the scalars): no LDS and no barrier, and those loads are issued
+// before the tile's. A bf16 state is rounded once, to nearest even, on store.
+template <int VAR, int K, int V, bool BF16IN, bool BF16OUT, bool BF16S>
 __global__ void __launch_bounds__((V / 8) * 64) decode1_kernel(const Params p)
 {
     static_assert(VAR != VAR_KDA, "KDA one-token calls use decode_kernel");
-    constexpr int LPR = K / 4;     // lanes per row
-    constexpr int RPI = 64 / LPR;  // rows per load instruction
-    constexpr int RPL = 8 / RPI;   // rows per lane
+    constexpr uint32_t ES = BF16S ? 2u : 4u;  // state bytes per element
+    constexpr int CPL = 16 / ES;    // columns per lane (one chunk per row)
+    constexpr int G = CPL / 4;      // 4-column groups per chunk
+    constexpr int LPR = K / CPL;    // lanes per row
+    constexpr int RPI = 64 / LPR;   // rows per load instruction
+    constexpr int RPL = 8 / RPI;    // rows per lane
 
     const int pair = blockIdx.x;
     const int b = pair / p.HV;
@@ -913,13 +917,13 @@ __global__ void __launch_bounds__((V / 8) * 64) decode1_kernel(const Params p)
 
     // token inputs of this lane
     const int h = hv / p.group;
-    const int32_t qo = b * p.sq_b + h * p.sq_h + 4 * cl;
-    const int32_t ko = b * p.sk_b + h * p.sk_h + 4 * cl;
+    const int32_t qo = b * p.sq_b + h * p.sq_h + CPL * cl;
+    const int32_t ko = b * p.sk_b + h * p.sk_h + CPL * cl;
     const int32_t vo = b * p.sv_b + hv * p.sv_h + 8 * wave + rl;
     const int32_t go = b * p.sg_b + hv * p.sg_h;
-    float qv[4], kv[4], vv[RPL];
+    float qv[CPL], kv[CPL], vv[RPL];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < CPL; ++i) {
         qv[i] = load_act<BF16IN>(p.q, qo + i);
         kv[i] = load_act<BF16IN>(p.k, ko + i);
     }
@@ -933,26 +937,37 @@ __global__ void __launch_bounds__((V / 8) * 64) decode1_kernel(const Params p)
         bs = p.beta[b * p.sb_b + hv * p.sb_h];
 
     // the tile rows of this lane
-    const uint32_t row_bytes = static_cast<uint32_t>(p.sp_row) * 4u;
+    const uint32_t row_bytes = static_cast<uint32_t>(p.sp_row) * ES;
     const uint32_t tile_bytes = static_cast<uint32_t>(
-        (static_cast<int64_t>(V - 1) * p.sp_row + K) * 4);
+        (static_cast<int64_t>(V - 1) * p.sp_row + K) * ES);
     const uint32_t lane_off = rl * row_bytes + cl * 16u;
     char *const pool = static_cast<char *>(p.pool);
     const BufRsrc src = make_rsrc(
-        pool + (r * p.sp_slot + hv * p.sp_head) * 4, tile_bytes);
-    f4 S[RPL];
+        pool + (r * p.sp_slot + hv * p.sp_head) * ES, tile_bytes);
+    f4 S[RPL][G];
 #pragma unroll
-    for (int j = 0; j < RPL; ++j)
-        S[j] = __builtin_bit_cast(
-            f4, __builtin_amdgcn_raw_buffer_load_b128(
-                    src, lane_off, (8 * wave + RPI * j) * row_bytes,
-                    kStreamPolicy));
+    for (int j = 0; j < RPL; ++j) {
+        const u4 x = __builtin_amdgcn_raw_buffer_load_b128(
+            src, lane_off, (8 * wave + RPI * j) * row_bytes, kStreamPolicy);
+        if constexpr (BF16S) {
+            S[j][0] = f4{__uint_as_float(x.x << 16),
+                         __uint_as_float(x.x & 0xffff0000u),
+                         __uint_as_float(x.y << 16),
+                         __uint_as_float(x.y & 0xffff0000u)};
+            S[j][1] = f4{__uint_as_float(x.z << 16),
+                         __uint_as_float(x.z & 0xffff0000u),
+                         __uint_as_float(x.w << 16),
+                         __uint_as_float(x.w & 0xffff0000u)};
+        } else {
+            S[j][0] = __builtin_bit_cast(f4, x);
+        }
+    }
 
     // prologue: l2norm over K (the row's lanes hold all K columns), k.q,
     // beta, decay
     float ssq = 0.f, ssk = 0.f, qk = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < CPL; ++i) {
         ssq = fmaf(qv[i], qv[i], ssq);
         ssk = fmaf(kv[i], kv[i], ssk);
         qk = fmaf(qv[i], kv[i], qk);
@@ -964,8 +979,14 @@ __global__ void __launch_bounds__((V / 8) * 64) decode1_kernel(const Params p)
         rk = __frsqrt_rn(sum_lanes<LPR>(ssk) + kL2Eps);
     }
     const float kq = qk * rq * rk;
-    f4 kk = {kv[0] * rk, kv[1] * rk, kv[2] * rk, kv[3] * rk};
-    const f4 qq = {qv[0] * rq, qv[1] * rq, qv[2] * rq, qv[3] * rq};
+    f4 kk[G], qq[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        kk[g] = f4{kv[4 * g] * rk, kv[4 * g + 1] * rk, kv[4 * g + 2] * rk,
+                   kv[4 * g + 3] * rk};
+        qq[g] = f4{qv[4 * g] * rq, qv[4 * g + 1] * rq, qv[4 * g + 2] * rq,
+                   qv[4 * g + 3] * rq};
+    }
     float decay;
     if constexpr (VAR == VAR_LA)
         decay = p.g ? p.g[hv]
@@ -980,36 +1001,52 @@ __global__ void __launch_bounds__((V / 8) * 64) decode1_kernel(const Params p)
     float mine = 0.f;
 #pragma unroll
     for (int j = 0; j < RPL; ++j) {
-        S[j] *= decay;
         float u = 0.f, wq = 0.f;
-        if constexpr (VAR != VAR_LA) {
-            u = fmaf(S[j].x, kk.x, u);
-            u = fmaf(S[j].y, kk.y, u);
-            u = fmaf(S[j].z, kk.z, u);
-            u = fmaf(S[j].w, kk.w, u);
-            u = sum_lanes<LPR>(u);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            S[j][g] *= decay;
+            if constexpr (VAR != VAR_LA) {
+                u = fmaf(S[j][g].x, kk[g].x, u);
+                u = fmaf(S[j][g].y, kk[g].y, u);
+                u = fmaf(S[j][g].z, kk[g].z, u);
+                u = fmaf(S[j][g].w, kk[g].w, u);
+            }
+            wq = fmaf(S[j][g].x, qq[g].x, wq);
+            wq = fmaf(S[j][g].y, qq[g].y, wq);
+            wq = fmaf(S[j][g].z, qq[g].z, wq);
+            wq = fmaf(S[j][g].w, qq[g].w, wq);
         }
-        wq = fmaf(S[j].x, qq.x, wq);
-        wq = fmaf(S[j].y, qq.y, wq);
-        wq = fmaf(S[j].z, qq.z, wq);
-        wq = fmaf(S[j].w, qq.w, wq);
+        if constexpr (VAR != VAR_LA)
+            u = sum_lanes<LPR>(u);
         wq = sum_lanes<LPR>(wq);
         const float c = (VAR == VAR_LA) ? vv[j] : beta * (vv[j] - u);
         mine = (cl == j) ? fmaf(c, kq, wq) : mine;
-        S[j].x = fmaf(c, kk.x, S[j].x);
-        S[j].y = fmaf(c, kk.y, S[j].y);
-        S[j].z = fmaf(c, kk.z, S[j].z);
-        S[j].w = fmaf(c, kk.w, S[j].w);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            S[j][g].x = fmaf(c, kk[g].x, S[j][g].x);
+            S[j][g].y = fmaf(c, kk[g].y, S[j][g].y);
+            S[j][g].z = fmaf(c, kk[g].z, S[j][g].z);
+            S[j][g].w = fmaf(c, kk[g].w, S[j][g].w);
+        }
     }
     if (olane)
         store_out<BF16OUT>(p.out, oidx, mine);
     if (w >= 0) {
         const BufRsrc dst = make_rsrc(
-            pool + (w * p.sp_slot + hv * p.sp_head) * 4, tile_bytes);
+            pool + (w * p.sp_slot + hv * p.sp_head) * ES, tile_bytes);
 #pragma unroll
-        for (int j = 0; j < RPL; ++j)
-            store_b128(__builtin_bit_cast(u4, S[j]), dst, lane_off,
-                       (8 * wave + RPI * j) * row_bytes);
+        for (int j = 0; j < RPL; ++j) {
+            u4 x;
+            if constexpr (BF16S) {
+                x.x = StateIO<true>::pack(S[j][0].x, S[j][0].y);
+                x.y = StateIO<true>::pack(S[j][0].z, S[j][0].w);
+                x.z = StateIO<true>::pack(S[j][1].x, S[j][1].y);
+                x.w = StateIO<true>::pack(S[j][1].z, S[j][1].w);
+            } else {
+                x = __builtin_bit_cast(u4, S[j][0]);
+            }
+            store_b128(x, dst, lane_off, (8 * wave + RPI * j) * row_bytes);
+        }
     }
 }
 
@@ -1278,24 +1315,31 @@ KernelFn pick_packed(int K, int V, bool bi, bool bo)
                     : pick_packed<VAR, 64, 64>(bi, bo);
 }
 
-template <int VAR, int K, int V>
+template <int VAR, int K, int V, bool BF16S>
 KernelFn pick_one(bool bi, bool bo)
 {
     if (bi)
-        return bo ? decode1_kernel<VAR, K, V, true, true>
-                  : decode1_kernel<VAR, K, V, true, false>;
-    return bo ? decode1_kernel<VAR, K, V, false, true>
-              : decode1_kernel<VAR, K, V, false, false>;
+        return bo ? decode1_kernel<VAR, K, V, true, true, BF16S>
+                  : decode1_kernel<VAR, K, V, true, false, BF16S>;
+    return bo ? decode1_kernel<VAR, K, V, false, true, BF16S>
+              : decode1_kernel<VAR, K, V, false, false, BF16S>;
+}
+
+template <int VAR, int K, int V>
+KernelFn pick_one(bool bi, bool bo, bool bs)
+{
+    return bs ? pick_one<VAR, K, V, true>(bi, bo)
+              : pick_one<VAR, K, V, false>(bi, bo);
 }
 
 template <int VAR>
-KernelFn pick_one(int K, int V, bool bi, bool bo)
+KernelFn pick_one(int K, int V, bool bi, bool bo, bool bs)
 {
     if (K == 128)
-        return V == 128 ? pick_one<VAR, 128, 128>(bi, bo)
-                        : pick_one<VAR, 128, 64>(bi, bo);
-    return V == 128 ? pick_one<VAR, 64, 128>(bi, bo)
-                    : pick_one<VAR, 64, 64>(bi, bo);
+        return V == 128 ? pick_one<VAR, 128, 128>(bi, bo, bs)
+                        : pick_one<VAR, 128, 64>(bi, bo, bs);
+    return V == 128 ? pick_one<VAR, 64, 128>(bi, bo, bs)
+                    : pick_one<VAR, 64, 64>(bi, bo, bs);
 }
 
 template <int VAR>
@@ -1570,25 +1614,28 @@ la_status launch(const la_decode_args *a, void *stream, int var)
     const bool bi = a->qkv_dtype == LA_BF16, bo = a->out_dtype == LA_BF16;
     const bool bs = a->state_dtype == LA_BF16;
     const bool rec = a->factors != nullptr;
-    // one token on a bf16 pool with no per-token writes: packed tile
-    const bool packed = bs && a->T == 1 && !a->inter && !a->token_slots &&
-                        !rec && !a->cu_seqlens;
-    // One token of Lightning or GDN on an fp32 pool with no per-token
-    // writes, over at least 2048 tiles: the contiguous-row kernel. Measured
-    // on MI355X (4 GiB rotation): Lightning B=33 H=64 71.0 -> 74.3 % of
-    // peak, GDN B=64 HV=32 66.8 -> 68.7 %; at 512 tiles it was 9 % slower,
-    // and KDA (B=256, HV=24) 1 % slower, so those keep decode_kernel.
-    const bool one = var != VAR_KDA && !bs && a->T == 1 && !a->inter &&
+    // One token of Lightning or GDN with no per-token writes, over at least
+    // 2048 tiles: the contiguous-row kernel (either state dtype). Measured on
+    // MI355X with a 4 GiB rotation, % of peak HBM bandwidth:
+    //   fp32 Lightning B=33 H=64: 71.0 -> 74.3; GDN B=64 HV=32: 66.8 -> 68.7
+    //   bf16 GDN B=128 HV=32: 60.4 -> 69.5; Lightning B=33: 61.1 -> 67.2
+    // At 512-1024 tiles it was 9-12 % slower, and KDA (B=256 H=24) 1 %
+    // slower: those keep decode_kernel, or for a bf16 pool the packed kernel.
+    const bool one = var != VAR_KDA && a->T == 1 && !a->inter &&
                      !a->token_slots && !rec && !a->cu_seqlens &&
                      static_cast<int64_t>(a->B) * a->HV >= 2048;
+    // otherwise one token on a bf16 pool with no per-token writes: the
+    // packed tile
+    const bool packed = !one && bs && a->T == 1 && !a->inter &&
+                        !a->token_slots && !rec && !a->cu_seqlens;
     KernelFn fn;
     if (packed)
         fn = var == VAR_LA    ? pick_packed<VAR_LA>(a->K, a->V, bi, bo)
              : var == VAR_GDN ? pick_packed<VAR_GDN>(a->K, a->V, bi, bo)
                               : pick_packed<VAR_KDA>(a->K, a->V, bi, bo);
     else if (one)
-        fn = var == VAR_LA ? pick_one<VAR_LA>(a->K, a->V, bi, bo)
-                           : pick_one<VAR_GDN>(a->K, a->V, bi, bo);
+        fn = var == VAR_LA ? pick_one<VAR_LA>(a->K, a->V, bi, bo, bs)
+                           : pick_one<VAR_GDN>(a->K, a->V, bi, bo, bs);
     else
         fn = var == VAR_LA    ? pick<VAR_LA>(a->K, a->V, bi, bo, bs, rec)
              : var == VAR_GDN ? pick<VAR_GDN>(a->K, a->V, bi, bo, bs, rec)

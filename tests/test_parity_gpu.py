@@ -1530,3 +1530,22 @@ def test_one_token_kernel_token_split_within_rounding(variant):
     split_out = torch.cat(outs, 1).cpu()
     assert _err("rel", split_out, whole["out"]) <= 2e-6
     assert _err("rel", pool.cpu(), whole["backing"]) <= 2e-6
+
+
+@pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN])
+@pytest.mark.parametrize("K,V", SHAPES)
+def test_one_token_kernel_bf16_state(variant, K, V):
+    """The one-token kernel on a bf16 pool (2048 tiles): states widened to
+    fp32, rounded once to nearest even on store; padded and skipped-write
+    requests; sampled against the oracle, every untouched byte checked."""
+    seed = 6500 + 100 * [W.LIGHTNING, W.GDN].index(variant) + \
+        10 * SHAPES.index((K, V))
+    B = 64
+    ridx = list(range(0, 2 * B, 2))
+    widx = [s + 1 for s in ridx]
+    ridx[9] = -1
+    widx[30] = -1
+    wl = W.make("onebf", variant, B=B, T=1, H=16, HV=32, K=K, V=V,
+                pool_size=2 * B, seed=seed, pool_std=0.1, read_idx=ridx,
+                write_idx=widx, state_dtype=torch.bfloat16)
+    run_and_check(wl, reqs=[0, 9, 13, 30, 51, 63])
