@@ -34,6 +34,11 @@
 //    update against one vector operand, bound by HBM traffic of the state.
 //  - Per token and element: one multiply (decay), two FMAs (read-outs) and
 //    one FMA (update); Lightning needs no key read-out.
+//  - Three kernels compute this: decode_kernel (every call), the packed
+//    one-token kernel for bf16 pools and the contiguous-row one-token
+//    kernel for large grids. They perform the same fp32 operations in the
+//    same order, so a request's results do not depend on which one runs:
+//    not on the batch size, nor on how its tokens are split over calls.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -158,28 +163,40 @@ __device__ __forceinline__ float sum8(float x)
     return x;
 }
 
-__device__ __forceinline__ float dpp_row_mirror(float x)
+// Lane moves for rows spread over LPR = 8 NJ consecutive lanes, where lane
+// c + 8 j of a row holds its 16-byte chunk c + 8 j (decode1_kernel).
+// chunk_pass(x, s): lanes with j = s receive the value of lane c + 8 (s - 1):
+// xor 8 inside a 16-lane row (DPP row_ror:8) for s = 1 and 3, xor 24 inside
+// a 32-lane half (ds_swizzle) for s = 2. Other lanes receive values they do
+// not use. s is a compile-time constant after unrolling.
+__device__ __forceinline__ float chunk_pass(float x, int s)
 {
+    if (s == 2)
+        return __int_as_float(
+            __builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x601F));
     return __int_as_float(
-        __builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, true));
+        __builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, true));
 }
 
-// Sum over groups of L = 8, 16 or 32 consecutive lanes, bit-identical in all
-// L lanes (each step adds a lane pair's values in both lanes; the last step
-// swaps the two 16-lane rows of each 32-lane half with ds_swizzle, xor 16).
-template <int L>
-__device__ __forceinline__ float sum_lanes(float x)
+// Every lane c + 8 j of a row takes the value of lane c + 8 (NJ - 1).
+template <int NJ>
+__device__ __forceinline__ float from_last_chunk(float x)
 {
-    x = sum8(x);
-    if constexpr (L >= 16)
-        x += dpp_row_mirror(x);
-    if constexpr (L >= 32)
-        x += __int_as_float(
-            __builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
-    return x;
+    if constexpr (NJ == 1)
+        return x;
+    else if constexpr (NJ == 2)  // lanes c take lane c + 8 (row_ror:8)
+        // one DPP move whose bank mask (lanes 0-7 of each 16-lane row)
+        // leaves lanes 8-15 their own value: no select, so the compiler
+        // cannot narrow the exec mask under the move (a DPP read from an
+        // inactive lane yields 0)
+        return __int_as_float(__builtin_amdgcn_update_dpp(
+            __float_as_int(x), __float_as_int(x), 0x128, 0xF, 0x3, false));
+    else  // lane (lane & 0x07) | 0x18 of each 32-lane half (ds_swizzle)
+        return __int_as_float(
+            __builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x307));
 }
 
-// Sum over the whole wave (prologue only).
+// Sum over the whole wave (token prologues).
 __device__ __forceinline__ float wave_sum(float x)
 {
     x = sum8(x);
@@ -878,12 +895,18 @@ __global__ void __launch_bounds__(V) decode_packed_kernel(const Params p)
 // keeps HBM busier than rows split into 128-byte pieces. A wave owns 8 rows,
 // so a workgroup has V / 8 waves. Lane (cl = lane % LPR, rl = lane / LPR)
 // holds the 16-byte chunk cl of rows 8 wave + RPI j + rl (4 fp32 or 8 bf16
-// columns, widened to fp32 in registers), and a row's dot products are
-// summed over its LPR lanes: a different summation order from
-// decode_kernel's, so the two agree to fp32 rounding, not bit for bit. Every
-// wave forms the token prologue it needs itself (its columns of q and k, its
-// rows of v, the scalars): no LDS and no barrier, and those loads are issued
-// before the tile's. A bf16 state is rounded once, to nearest even, on store.
+// columns, widened to fp32 in registers). Every wave forms the token
+// prologue it needs itself (q and k, its rows of v, the scalars): no LDS and
+// no barrier, and those loads are issued before the tile's. A bf16 state is
+// rounded once, to nearest even, on store.
+// The arithmetic repeats decode_kernel's at T = 1 operation for operation,
+// in the same order, so a request gets the same bits from either kernel
+// whatever the batch size or the split of its tokens over calls: the norms
+// and k.q are summed over the wave with K / 64 elements per lane, as in the
+// prologue, and a row's dot products run one FMA chain per c = cl & 7 over
+// the chunks c, c + 8, ... (handed from lane to lane), closed by the same
+// 8-lane butterfly. The extra lane moves cost ALU time that this
+// memory-bound kernel has to spare.
 template <int VAR, int K, int V, bool BF16IN, bool BF16OUT, bool BF16S>
 __global__ void __launch_bounds__((V / 8) * 64) decode1_kernel(const Params p)
 {
@@ -902,12 +925,15 @@ __global__ void __launch_bounds__((V / 8) * 64) decode1_kernel(const Params p)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int cl = lane % LPR;
     const int rl = lane / LPR;
+    constexpr int NJ = LPR / 8;  // chunks c + 8 j per row and c
+    const int c8 = cl & 7;
+    const int jm = cl >> 3;
 
     const int r = __builtin_amdgcn_readfirstlane(p.ridx[b]);
     const int w = __builtin_amdgcn_readfirstlane(p.widx ? p.widx[b] : r);
-    // lane cl = j (< RPL) writes the output of its row j
-    const bool olane = cl < RPL;
-    const int orow = 8 * wave + RPI * (olane ? cl : 0) + rl;
+    // lane c8 = j of a row's last chunk group writes the output of row j
+    const bool olane = jm == NJ - 1 && c8 < RPL;
+    const int orow = 8 * wave + RPI * (olane ? c8 : 0) + rl;
     const int32_t oidx = b * p.so_b + hv * p.so_h + orow;
     if (r < 0) {
         if (olane)
@@ -915,17 +941,24 @@ __global__ void __launch_bounds__((V / 8) * 64) decode1_kernel(const Params p)
         return;
     }
 
-    // token inputs of this lane
+    // token inputs of this lane: q, k in the prologue's layout (K / 64
+    // elements per lane, for the sums over K) and in the chunk layout
+    constexpr int EPL = K / 64;
     const int h = hv / p.group;
-    const int32_t qo = b * p.sq_b + h * p.sq_h + CPL * cl;
-    const int32_t ko = b * p.sk_b + h * p.sk_h + CPL * cl;
+    const int32_t qb = b * p.sq_b + h * p.sq_h;
+    const int32_t kb = b * p.sk_b + h * p.sk_h;
     const int32_t vo = b * p.sv_b + hv * p.sv_h + 8 * wave + rl;
     const int32_t go = b * p.sg_b + hv * p.sg_h;
-    float qv[CPL], kv[CPL], vv[RPL];
+    float qe[EPL], ke[EPL], qv[CPL], kv[CPL], vv[RPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        qe[i] = load_act<BF16IN>(p.q, qb + lane * EPL + i);
+        ke[i] = load_act<BF16IN>(p.k, kb + lane * EPL + i);
+    }
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-        qv[i] = load_act<BF16IN>(p.q, qo + i);
-        kv[i] = load_act<BF16IN>(p.k, ko + i);
+        qv[i] = load_act<BF16IN>(p.q, qb + CPL * cl + i);
+        kv[i] = load_act<BF16IN>(p.k, kb + CPL * cl + i);
     }
 #pragma unroll
     for (int j = 0; j < RPL; ++j)
@@ -963,20 +996,21 @@ __global__ void __launch_bounds__((V / 8) * 64) decode1_kernel(const Params p)
         }
     }
 
-    // prologue: l2norm over K (the row's lanes hold all K columns), k.q,
-    // beta, decay
+    // prologue: l2norm over K, k.q, beta, decay
     float ssq = 0.f, ssk = 0.f, qk = 0.f;
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-        ssq = fmaf(qv[i], qv[i], ssq);
-        ssk = fmaf(kv[i], kv[i], ssk);
-        qk = fmaf(qv[i], kv[i], qk);
+    for (int i = 0; i < EPL; ++i) {
+        ssq = fmaf(qe[i], qe[i], ssq);
+        ssk = fmaf(ke[i], ke[i], ssk);
+        qk = fmaf(qe[i], ke[i], qk);
     }
-    qk = sum_lanes<LPR>(qk);
     float rq = 1.f, rk = 1.f;
+    qk = wave_sum(qk);
     if (p.flags & LA_F_L2NORM_QK) {
-        rq = __frsqrt_rn(sum_lanes<LPR>(ssq) + kL2Eps);
-        rk = __frsqrt_rn(sum_lanes<LPR>(ssk) + kL2Eps);
+        ssq = wave_sum(ssq);
+        ssk = wave_sum(ssk);
+        rq = __frsqrt_rn(ssq + kL2Eps);
+        rk = __frsqrt_rn(ssk + kL2Eps);
     }
     const float kq = qk * rq * rk;
     f4 kk[G], qq[G];
@@ -998,29 +1032,48 @@ __global__ void __launch_bounds__((V / 8) * 64) decode1_kernel(const Params p)
     if constexpr (VAR != VAR_LA)
         beta = (p.flags & LA_F_BETA_LOGIT) ? 1.f / (1.f + __expf(-bs)) : bs;
 
+    // one FMA chain per row and c8 over chunks c8, c8 + 8, ...: in step s
+    // the lanes of chunk c8 + 8 s extend the chain handed to them
+    auto chain = [&](float acc, const f4 &x, const f4 &y) -> float {
+        acc = fmaf(x.x, y.x, acc);
+        acc = fmaf(x.y, y.y, acc);
+        acc = fmaf(x.z, y.z, acc);
+        acc = fmaf(x.w, y.w, acc);
+        return acc;
+    };
     float mine = 0.f;
 #pragma unroll
     for (int j = 0; j < RPL; ++j) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            S[j][g] *= decay;
         float u = 0.f, wq = 0.f;
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            S[j][g] *= decay;
-            if constexpr (VAR != VAR_LA) {
-                u = fmaf(S[j][g].x, kk[g].x, u);
-                u = fmaf(S[j][g].y, kk[g].y, u);
-                u = fmaf(S[j][g].z, kk[g].z, u);
-                u = fmaf(S[j][g].w, kk[g].w, u);
+        for (int st = 0; st < NJ; ++st) {
+            if (st > 0) {
+                if constexpr (VAR != VAR_LA)
+                    u = chunk_pass(u, st);
+                wq = chunk_pass(wq, st);
             }
-            wq = fmaf(S[j][g].x, qq[g].x, wq);
-            wq = fmaf(S[j][g].y, qq[g].y, wq);
-            wq = fmaf(S[j][g].z, qq[g].z, wq);
-            wq = fmaf(S[j][g].w, qq[g].w, wq);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                if constexpr (VAR != VAR_LA)
+                    u = chain(u, S[j][g], kk[g]);
+                wq = chain(wq, S[j][g], qq[g]);
+            }
         }
+        // the lanes of the last chunk group hold the chains; sum over c8
+        wq = sum8(wq);
+        float c;
+        if constexpr (VAR == VAR_LA) {
+            c = vv[j];
+        } else {
+            u = sum8(u);
+            c = beta * (vv[j] - u);
+        }
+        mine = (jm == NJ - 1 && c8 == j) ? fmaf(c, kq, wq) : mine;
         if constexpr (VAR != VAR_LA)
-            u = sum_lanes<LPR>(u);
-        wq = sum_lanes<LPR>(wq);
-        const float c = (VAR == VAR_LA) ? vv[j] : beta * (vv[j] - u);
-        mine = (cl == j) ? fmaf(c, kq, wq) : mine;
+            c = from_last_chunk<NJ>(c);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             S[j][g].x = fmaf(c, kk[g].x, S[j][g].x);
@@ -1614,16 +1667,22 @@ la_status launch(const la_decode_args *a, void *stream, int var)
     const bool bi = a->qkv_dtype == LA_BF16, bo = a->out_dtype == LA_BF16;
     const bool bs = a->state_dtype == LA_BF16;
     const bool rec = a->factors != nullptr;
-    // One token of Lightning or GDN with no per-token writes, over at least
-    // 2048 tiles: the contiguous-row kernel (either state dtype). Measured on
-    // MI355X with a 4 GiB rotation, % of peak HBM bandwidth:
+    // One token of Lightning or GDN with no per-token writes over at least
+    // 2048 tiles (fp32 pool) or more than 2048 (bf16 pool): the
+    // contiguous-row kernel. All three kernels give identical bits, so the
+    // choice is by speed alone. Measured on MI355X with a 4 GiB rotation,
+    // % of peak HBM bandwidth, previous kernel -> this one:
     //   fp32 Lightning B=33 H=64: 71.0 -> 74.3; GDN B=64 HV=32: 66.8 -> 68.7
-    //   bf16 GDN B=128 HV=32: 60.4 -> 69.5; Lightning B=33: 61.1 -> 67.2
-    // At 512-1024 tiles it was 9-12 % slower, and KDA (B=256 H=24) 1 %
-    // slower: those keep decode_kernel, or for a bf16 pool the packed kernel.
+    //   bf16 GDN B=72..96 HV=32: 57-62 -> 62-67; Lightning H=64
+    //   B=36..48: 62-64 -> 69-71
+    // At 512-1024 fp32 tiles it was 9-12 % slower, and KDA (B=256 H=24) 1 %
+    // slower. On a bf16 pool the packed kernel keeps 2048 tiles in one
+    // resident round and is 3-5 % faster there (GDN B=64 HV=32: 66.2 vs
+    // 62.9; Lightning B=32 H=64: 68.7 vs 67.0).
+    const int64_t tiles = static_cast<int64_t>(a->B) * a->HV;
     const bool one = var != VAR_KDA && a->T == 1 && !a->inter &&
                      !a->token_slots && !rec && !a->cu_seqlens &&
-                     static_cast<int64_t>(a->B) * a->HV >= 2048;
+                     (bs ? tiles > 2048 : tiles >= 2048);
     // otherwise one token on a bf16 pool with no per-token writes: the
     // packed tile
     const bool packed = !one && bs && a->T == 1 && !a->inter &&

@@ -1453,7 +1453,7 @@ def test_hip_graph_capture_replays_match_eager(variant):
         assert torch.equal(_bits(d.backing), _bits(eager[2])), rep
 
 
-# ------------------------------- one-token fp32 kernel (grids >= 2048 tiles)
+# ---------------- one-token kernel (fp32 pools >= 2048 tiles, bf16 > 2048)
 
 
 @pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN])
@@ -1502,15 +1502,18 @@ def test_one_token_kernel_gate_chain():
 
 
 @pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN])
-def test_one_token_kernel_token_split_within_rounding(variant):
-    """T single-token calls (one-token kernel) against one T-token call
-    (decode_kernel): equal to fp32 rounding; the kernels sum each dot
-    product in a different order, so not bit for bit."""
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16],
+                         ids=["f32", "bf16"])
+def test_one_token_kernel_token_split_bit_identical(variant, dtype):
+    """T single-token calls of 2048 tiles (one-token kernel) chained through
+    the pool = one T-token call (decode_kernel), bit for bit: the two
+    kernels perform the same operations in the same order."""
     lad = _lad()
     T = 3
     wl = W.make("onesplit", variant, B=64, T=T, H=16, HV=32, K=128, V=128,
-                pool_size=64, seed=6400 + len(variant),
-                act_dtype=torch.float32)
+                pool_size=64, seed=6400 + len(variant) + T * (dtype ==
+                                                              torch.bfloat16),
+                act_dtype=dtype)
     whole = gpu_run(wl)
     d = wl.to(DEV)
     pool = d.backing
@@ -1527,20 +1530,94 @@ def test_one_token_kernel_token_split_within_rounding(variant):
                                       beta_logit=wl.beta_logit)
         outs.append(o)
     torch.cuda.synchronize()
-    split_out = torch.cat(outs, 1).cpu()
-    assert _err("rel", split_out, whole["out"]) <= 2e-6
-    assert _err("rel", pool.cpu(), whole["backing"]) <= 2e-6
+    assert torch.equal(_bits(torch.cat(outs, 1).cpu()), _bits(whole["out"]))
+    assert torch.equal(_bits(pool.cpu()), _bits(whole["backing"]))
+
+
+def _one_token_batch_invariance(wl, sub=8, **kw):
+    """Outputs and pool of one call over wl's whole batch, and of the same
+    requests in calls of `sub` requests on a second copy of the pool."""
+    lad = _lad()
+    d = wl.to(DEV)
+    pools = [d.backing.clone(), d.backing.clone()]
+    results = []
+    for pool, step in zip(pools, (wl.B, sub)):
+        outs = []
+        for s in range(0, wl.B, step):
+            sl = slice(s, s + step)
+            if wl.variant == W.LIGHTNING:
+                o, _ = lad.la_decode(d.q[sl], d.k[sl], d.v[sl], pool,
+                                     d.read_idx[sl], d.write_idx[sl],
+                                     lam=d.g)
+            else:
+                o, _ = lad.gdn_decode_mtp(
+                    d.q[sl], d.k[sl], d.v[sl], d.g[sl], d.beta[sl], pool,
+                    d.read_idx[sl], d.write_idx[sl], l2norm_qk=wl.l2norm,
+                    beta_logit=wl.beta_logit, **kw)
+            outs.append(o)
+        torch.cuda.synchronize()
+        results.append((torch.cat(outs).cpu(), pool.cpu()))
+    return results
+
+
+@pytest.mark.parametrize("variant,raw", [(W.LIGHTNING, False), (W.GDN, False),
+                                         (W.GDN, True)],
+                         ids=["lightning", "gdn", "gdn_raw"])
+@pytest.mark.parametrize("K,V", SHAPES)
+@pytest.mark.parametrize("state", [torch.float32, torch.bfloat16],
+                         ids=["f32_state", "bf16_state"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16],
+                         ids=["f32", "bf16"])
+def test_one_token_kernel_batch_invariant(variant, raw, K, V, state, dtype):
+    """The same requests in one call of 2304 tiles (one-token kernel) and in
+    calls of 8 requests (256 tiles: decode_kernel, or the packed kernel on a
+    bf16 pool) give the same bits, outputs and stored states; `raw` passes
+    q, k without l2norm and beta without the sigmoid."""
+    B, HV = 72, 32
+    seed = (6700 + 10 * SHAPES.index((K, V)) + (1 if raw else 0)
+            + (2 if state != torch.float32 else 0)
+            + (4 if dtype != torch.float32 else 0)
+            + (100 if variant == W.GDN else 0))
+    wl = W.make("inv", variant, B=B, T=1, H=16, HV=HV, K=K, V=V,
+                pool_size=2 * B, seed=seed, act_dtype=dtype, pool_std=0.1,
+                separate_write=True, state_dtype=state,
+                l2norm=not raw, beta_logit=not raw)
+    if raw:  # small raw keys keep the delta rule contractive
+        wl.q = (wl.q.float() / K ** 0.5).to(dtype)
+        wl.k = (wl.k.float() / K ** 0.5).to(dtype)
+        wl.beta = torch.rand(wl.beta.shape, generator=torch.Generator()
+                             .manual_seed(seed))
+    (wo, wp), (so, sp) = _one_token_batch_invariance(wl)
+    assert torch.isfinite(wo).all()
+    assert torch.equal(_bits(wo), _bits(so))
+    assert torch.equal(_bits(wp), _bits(sp))
+
+
+@pytest.mark.parametrize("lower_bound", [None, -5.0], ids=["softplus", "lb"])
+def test_one_token_kernel_batch_invariant_gate_chain(lower_bound):
+    """Batch invariance across the one-token kernel's grid threshold with
+    the in-kernel gate chain."""
+    wl = W.make("invgate", W.GDN, B=72, T=1, H=16, HV=32, K=128, V=128,
+                pool_size=144, seed=6900, separate_write=True)
+    wl.g = 2 * torch.randn(wl.g.shape, generator=torch.Generator()
+                           .manual_seed(6901))
+    a_log, dt = _gate_inputs(W.GDN, wl.HV, wl.K, 6902)
+    (wo, wp), (so, sp) = _one_token_batch_invariance(
+        wl, A_log=a_log.to(DEV), dt_bias=dt.to(DEV), lower_bound=lower_bound)
+    assert torch.equal(_bits(wo), _bits(so))
+    assert torch.equal(_bits(wp), _bits(sp))
 
 
 @pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN])
 @pytest.mark.parametrize("K,V", SHAPES)
 def test_one_token_kernel_bf16_state(variant, K, V):
-    """The one-token kernel on a bf16 pool (2048 tiles): states widened to
-    fp32, rounded once to nearest even on store; padded and skipped-write
-    requests; sampled against the oracle, every untouched byte checked."""
+    """The one-token kernel on a bf16 pool (2304 tiles; at 2048 and below a
+    bf16 pool takes the packed kernel): states widened to fp32, rounded once
+    to nearest even on store; padded and skipped-write requests; sampled
+    against the oracle, every untouched byte checked."""
     seed = 6500 + 100 * [W.LIGHTNING, W.GDN].index(variant) + \
         10 * SHAPES.index((K, V))
-    B = 64
+    B = 72
     ridx = list(range(0, 2 * B, 2))
     widx = [s + 1 for s in ridx]
     ridx[9] = -1
@@ -1548,4 +1625,4 @@ def test_one_token_kernel_bf16_state(variant, K, V):
     wl = W.make("onebf", variant, B=B, T=1, H=16, HV=32, K=K, V=V,
                 pool_size=2 * B, seed=seed, pool_std=0.1, read_idx=ridx,
                 write_idx=widx, state_dtype=torch.bfloat16)
-    run_and_check(wl, reqs=[0, 9, 13, 30, 51, 63])
+    run_and_check(wl, reqs=[0, 9, 13, 30, 51, 71])
