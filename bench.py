@@ -155,6 +155,7 @@ def make_call(wl, d, inter, out, stream):
             if st != 0:
                 raise bnd.LaDecodeError(st, "replay call")
             return keep
+        step.args = args
         return step
 
     def call():
@@ -162,6 +163,7 @@ def make_call(wl, d, inter, out, stream):
         if st != 0:
             raise bnd.LaDecodeError(st, "decode call")
         return keep
+    call.args = args  # the decode call's argument struct
     return call
 
 
@@ -186,6 +188,20 @@ def copy_probe(dev, stream):
     ms = s.elapsed_time(e) / reps
     del src, dst
     return 2 * n * 4 / (ms * 1e-3) / 1e9
+
+
+def _host():
+    """CPU model and the cores this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu": model, "available_cores": len(os.sched_getaffinity(0))}
 
 
 def cpu_baseline(wl, seconds):
@@ -230,7 +246,7 @@ def cpu_baseline(wl, seconds):
         calls += 1
         tokens += sum(counts[:nb])
     return {"value": tokens / spent, "unit": "tokens/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "host": _host(),
             "sample": "%d calls of the fp64 oracle on %d of %d requests "
                       "(%d tokens) of %s (pool conversion included), %.1f s"
                       % (calls, nb, wl.B, sum(counts[:nb]), wl.name, spent)}
@@ -296,6 +312,8 @@ def main():
     achieved = per_call / (avg_launch_ms * 1e-3) / 1e9
     state_gbps = wl.state_bytes() / (avg_launch_ms * 1e-3) / 1e9
     traffic = read_traffic(wl.name)
+    from linear_attention_recurrent_slot_amd import _binding as bnd
+    kinfo = bnd.kernel_info_of(wl.variant, calls[0].args)
     rec = {
         "metric": METRIC,
         "value": tokens / (ms_per_step * 1e-3),
@@ -330,6 +348,7 @@ def main():
         "bytes_per_call": per_call,
         "state_bytes_per_call": wl.state_bytes(),
         "device_copy_GBps": copy_gbps,
+        "kernel": kinfo,  # the decode call's kernel (the replay's is not listed)
     }
     if args.cpu_seconds > 0:
         rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -298,12 +298,49 @@ la_status la_check_cu_seqlens(int32_t B, int32_t T, int32_t total_tokens,
                               const int32_t *cu_seqlens, int32_t *dev_result,
                               void *stream);
 
+/* Variant codes of la_decode_kernel_info: the decode entry point a query
+ * stands for. */
+typedef enum la_variant {
+    LA_VARIANT_LIGHTNING = 0, /* la_decode      */
+    LA_VARIANT_GDN = 1,       /* gdn_decode_mtp */
+    LA_VARIANT_KDA = 2        /* kda_decode_mtp */
+} la_variant;
+
+/* The kernel a decode call selects, its launch shape and its register
+ * budget on the current device. */
+typedef struct la_kernel_info {
+    const char *kernel;     /* "decode_kernel" (every call),
+                               "decode1_kernel" (one token, large grids),
+                               "decode_packed_kernel" (one token, bf16 pool)
+                               or "none" (B = 0: nothing is launched);
+                               static storage owned by the library */
+    int32_t grid_blocks;    /* workgroups: B * HV                          */
+    int32_t block_threads;  /* threads per workgroup                       */
+    int32_t lds_bytes;      /* dynamic LDS per workgroup                   */
+    int32_t vgprs;          /* architected VGPRs per lane                  */
+    int32_t scratch_bytes;  /* private (spill) memory per lane             */
+    int32_t blocks_per_cu;  /* workgroups resident on one compute unit     */
+    int32_t waves_per_simd; /* blocks_per_cu * waves per workgroup / 4     */
+    int32_t reserved;       /* 0                                           */
+} la_kernel_info;
+
+/* Describe the kernel that the decode call `args` of `variant` would run
+ * (not an operation of the method: a report of this library's dispatch, for
+ * callers that size batches or check occupancy). Host only: launches
+ * nothing and reads no device memory. Runs the entry point's host checks
+ * first and returns the status the call itself would return, leaving *info
+ * untouched on error. LA_ERR_NULL for a NULL info, LA_ERR_ARG for an unknown
+ * variant, LA_ERR_LAUNCH when the HIP runtime cannot report the kernel's
+ * attributes (for instance without a device). */
+la_status la_decode_kernel_info(int32_t variant, const la_decode_args *args,
+                                la_kernel_info *info);
+
 /* Static description of a status code; never NULL. */
 const char *la_status_string(la_status status);
 
 /* Library version as major * 100 + minor (2.00: state_dtype and paged
  * per-token slots in la_decode_args; 2.10: variable-length batches; 2.20:
- * the in-kernel gate chain). */
+ * the in-kernel gate chain; 2.30: la_decode_kernel_info). */
 int32_t la_version(void);
 
 #ifdef __cplusplus

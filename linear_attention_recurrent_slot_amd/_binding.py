@@ -67,6 +67,22 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class KernelInfo(ctypes.Structure):
+    """la_kernel_info: the kernel a decode call selects."""
+    _fields_ = [("kernel", ctypes.c_char_p),
+                ("grid_blocks", ctypes.c_int32),
+                ("block_threads", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32),
+                ("vgprs", ctypes.c_int32),
+                ("scratch_bytes", ctypes.c_int32),
+                ("blocks_per_cu", ctypes.c_int32),
+                ("waves_per_simd", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+VARIANT_CODES = {"lightning": 0, "gdn": 1, "kda": 2}
+
+
 class ReplayArgs(ctypes.Structure):
     """Mirror of la_replay_args."""
     _fields_ = [
@@ -123,6 +139,10 @@ def lib() -> ctypes.CDLL:
         L.la_status_string.argtypes = [ctypes.c_int]
         L.la_version.restype = ctypes.c_int32
         L.la_version.argtypes = []
+        L.la_decode_kernel_info.restype = ctypes.c_int
+        L.la_decode_kernel_info.argtypes = [
+            ctypes.c_int32, ctypes.POINTER(DecodeArgs),
+            ctypes.POINTER(KernelInfo)]
         _lib = L
     return _lib
 
@@ -424,6 +444,50 @@ def kda_decode_mtp(q, k, v, g, beta, pool, read_idx=None, write_idx=None, *,
                 write_idx, out, inter, flags, out_dtype, stream, token_slots,
                 num_accepted, factors, cu_seqlens, max_tokens, A_log,
                 dt_bias, lower_bound)
+
+
+def kernel_info_of(variant: str, args: DecodeArgs) -> dict:
+    """la_decode_kernel_info for a prepared argument struct."""
+    info = KernelInfo()
+    st = lib().la_decode_kernel_info(VARIANT_CODES[variant],
+                                     ctypes.byref(args), ctypes.byref(info))
+    if st != LA_OK:
+        raise LaDecodeError(st, "la_decode_kernel_info")
+    return {"kernel": info.kernel.decode(), "grid_blocks": info.grid_blocks,
+            "block_threads": info.block_threads,
+            "lds_bytes": info.lds_bytes, "vgprs": info.vgprs,
+            "scratch_bytes": info.scratch_bytes,
+            "blocks_per_cu": info.blocks_per_cu,
+            "waves_per_simd": info.waves_per_simd}
+
+
+def kernel_info(variant, q, k, v, g, beta, pool, read_idx=None,
+                write_idx=None, *, out=None, inter=None, l2norm_qk=False,
+                beta_logit=False, out_dtype=torch.float32, token_slots=None,
+                num_accepted=None, factors=None, cu_seqlens=None,
+                max_tokens=None, A_log=None, dt_bias=None, lower_bound=None):
+    """Which kernel the decode call with these arguments would run, with its
+    launch shape, VGPRs and occupancy; launches nothing. variant:
+    "lightning" (g = lam, beta = None), "gdn" or "kda"; the other arguments
+    are those of the matching decode function (out and an inter=True cache
+    are allocated when not given, as the call would)."""
+    flags = 0
+    if variant != "lightning":
+        flags = (LA_F_L2NORM_QK if l2norm_qk else 0) | \
+            (LA_F_BETA_LOGIT if beta_logit else 0)
+    lead = tuple(q.shape[:-2])
+    HV, V, K = v.shape[-2], v.shape[-1], q.shape[-1]
+    if out is None:
+        out = torch.empty(lead + (HV, V), dtype=out_dtype, device=q.device)
+    if inter is True:
+        inter = torch.empty(lead + (HV, V, K), dtype=pool.dtype,
+                            device=q.device)
+    elif inter is False:
+        inter = None
+    args = build_args(variant, q, k, v, g, beta, pool, read_idx, write_idx,
+                      out, inter, flags, token_slots, num_accepted, factors,
+                      cu_seqlens, max_tokens, A_log, dt_bias, lower_bound)
+    return kernel_info_of(variant, args)
 
 
 def check_indices(read_idx, write_idx, pool_size, result=None, stream=None):

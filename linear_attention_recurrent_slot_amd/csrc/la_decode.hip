@@ -1603,13 +1603,24 @@ la_status validate(const la_decode_args *a, int var)
     return LA_OK;
 }
 
-la_status launch(const la_decode_args *a, void *stream, int var)
+// The kernel, launch shape and parameters of a decode call. fn is null
+// when there is nothing to launch (B = 0).
+struct Launch {
+    KernelFn fn = nullptr;
+    const char *name = "none";
+    dim3 grid, block;
+    size_t lds = 0;
+    Params p;
+};
+
+// Host checks, kernel choice and parameter block of a decode call.
+la_status select_kernel(const la_decode_args *a, int var, Launch &L)
 {
     const la_status st = validate(a, var);
     if (st != LA_OK || a->B == 0)
         return st;
 
-    Params p;
+    Params &p = L.p;
     p.B = a->B;
     p.T = a->T;
     p.HV = a->HV;
@@ -1699,26 +1710,76 @@ la_status launch(const la_decode_args *a, void *stream, int var)
         fn = var == VAR_LA    ? pick<VAR_LA>(a->K, a->V, bi, bo, bs, rec)
              : var == VAR_GDN ? pick<VAR_GDN>(a->K, a->V, bi, bo, bs, rec)
                               : pick<VAR_KDA>(a->K, a->V, bi, bo, bs, rec);
-    const int chunk = a->T < kTokChunk ? a->T : kTokChunk;
-    const size_t lds = static_cast<size_t>(chunk) *
-                       lds_floats_per_token(var, a->K, a->V) * sizeof(float);
-    const dim3 grid(static_cast<unsigned>(a->B) * a->HV);
-    // rows per wave: 64 in the packed kernel, 8 in the one-token fp32
-    // kernel, kRowsPerWave otherwise
-    const dim3 block(packed ? a->V
-                     : one  ? (a->V / 8) * 64
-                            : (a->V / kRowsPerWave) * 64);
+    L.fn = fn;
+    L.name = packed ? "decode_packed_kernel"
+             : one  ? "decode1_kernel"
+                    : "decode_kernel";
+    // the one-token kernel stages nothing in LDS
+    const int chunk = one ? 0 : a->T < kTokChunk ? a->T : kTokChunk;
+    L.lds = static_cast<size_t>(chunk) *
+            lds_floats_per_token(var, a->K, a->V) * sizeof(float);
+    L.grid = dim3(static_cast<unsigned>(a->B) * a->HV);
+    // rows per wave: 64 in the packed kernel, 8 in the one-token kernel,
+    // kRowsPerWave otherwise
+    L.block = dim3(packed ? a->V
+                   : one  ? (a->V / 8) * 64
+                          : (a->V / kRowsPerWave) * 64);
+    return LA_OK;
+}
 
-    void *kargs[] = {&p};
-    const hipError_t e =
-        hipLaunchKernel(reinterpret_cast<const void *>(fn), grid, block,
-                        kargs, lds, static_cast<hipStream_t>(stream));
+la_status launch(const la_decode_args *a, void *stream, int var)
+{
+    Launch L;
+    const la_status st = select_kernel(a, var, L);
+    if (st != LA_OK || !L.fn)
+        return st;
+    void *kargs[] = {&L.p};
+    const hipError_t e = hipLaunchKernel(
+        reinterpret_cast<const void *>(L.fn), L.grid, L.block, kargs, L.lds,
+        static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
 }
 
 }  // namespace
 
 extern "C" {
+
+la_status la_decode_kernel_info(int32_t variant, const la_decode_args *args,
+                                la_kernel_info *info)
+{
+    if (!info)
+        return LA_ERR_NULL;
+    if (variant != LA_VARIANT_LIGHTNING && variant != LA_VARIANT_GDN &&
+        variant != LA_VARIANT_KDA)
+        return LA_ERR_ARG;
+    static_assert(LA_VARIANT_LIGHTNING == VAR_LA && LA_VARIANT_GDN == VAR_GDN &&
+                      LA_VARIANT_KDA == VAR_KDA,
+                  "variant codes");
+    Launch L;
+    const la_status st = select_kernel(args, variant, L);
+    if (st != LA_OK)
+        return st;
+    la_kernel_info r = {};
+    r.kernel = L.name;
+    if (L.fn) {
+        hipFuncAttributes at;
+        int nb = 0;
+        const void *f = reinterpret_cast<const void *>(L.fn);
+        if (hipFuncGetAttributes(&at, f) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &nb, f, static_cast<int>(L.block.x), L.lds) != hipSuccess)
+            return LA_ERR_LAUNCH;
+        r.grid_blocks = static_cast<int32_t>(L.grid.x);
+        r.block_threads = static_cast<int32_t>(L.block.x);
+        r.lds_bytes = static_cast<int32_t>(L.lds);
+        r.vgprs = at.numRegs;
+        r.scratch_bytes = static_cast<int32_t>(at.localSizeBytes);
+        r.blocks_per_cu = nb;
+        r.waves_per_simd = nb * static_cast<int32_t>(L.block.x / 64) / 4;
+    }
+    *info = r;
+    return LA_OK;
+}
 
 la_status la_decode(const la_decode_args *args, void *stream)
 {
@@ -1896,6 +1957,6 @@ const char *la_status_string(la_status s)
     return "unknown status";
 }
 
-int32_t la_version(void) { return 220; }
+int32_t la_version(void) { return 230; }
 
 }  // extern "C"

@@ -38,7 +38,8 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("la_decode", "gdn_decode_mtp", "kda_decode_mtp", "la_replay",
               "la_check_indices", "la_check_token_slots",
-              "la_check_cu_seqlens", "la_status_string", "la_version"):
+              "la_check_cu_seqlens", "la_decode_kernel_info",
+              "la_status_string", "la_version"):
         assert n in names
 
 
@@ -72,6 +73,31 @@ def test_struct_layout_matches_ctypes(tmp_path):
     assert int(got["size"]) == ctypes.sizeof(bnd.DecodeArgs)
     for f in fields:
         assert int(got[f]) == getattr(bnd.DecodeArgs, f).offset, f
+
+
+@pytest.mark.parametrize("ctype,cstruct", [("KernelInfo", "la_kernel_info"),
+                                           ("ReplayArgs", "la_replay_args")])
+def test_other_struct_layouts_match_ctypes(tmp_path, ctype, cstruct):
+    """sizeof/offsetof of the other C structs against their ctypes mirrors."""
+    cls = getattr(bnd, ctype)
+    fields = [f for f, _ in cls._fields_]
+    body = "\n".join(
+        '  printf("%s %%zu\\n", offsetof(%s, %s));' % (f, cstruct, f)
+        for f in fields)
+    src = tmp_path / "layout.c"
+    src.write_text(
+        "#include <stdio.h>\n#include <stddef.h>\n#include \"la_decode.h\"\n"
+        "int main(void){\n  printf(\"size %%zu\\n\", sizeof(%s));\n"
+        "%s\n  return 0;\n}\n" % (cstruct, body))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(exe)], check=True)
+    got = dict(ln.split() for ln in
+               subprocess.run([str(exe)], capture_output=True, text=True,
+                              check=True).stdout.splitlines())
+    assert int(got["size"]) == ctypes.sizeof(cls)
+    for f in fields:
+        assert int(got[f]) == getattr(cls, f).offset, f
 
 
 def test_status_strings_and_version(lib):
@@ -233,6 +259,47 @@ def test_host_validation_rejects(lib, name, mutate, variant, code):
         mutate(a)
         st = _status(variant, a)
     assert st == code, (name, bnd.STATUS_NAMES.get(st))
+
+
+def _info_status(variant, a):
+    info = bnd.KernelInfo()
+    st = bnd.lib().la_decode_kernel_info(
+        bnd.VARIANT_CODES[variant], None if a is None else ctypes.byref(a),
+        ctypes.byref(info))
+    return st, info
+
+
+@pytest.mark.parametrize("name,mutate,variant,code", REJECT,
+                         ids=[r[0] for r in REJECT])
+def test_kernel_info_returns_the_call_status(lib, name, mutate, variant,
+                                             code):
+    """The kernel query runs the entry point's host checks: every malformed
+    call gets the status the call itself returns, and *info stays as it
+    was."""
+    if mutate is None:
+        st, info = _info_status(variant, None)
+    else:
+        a = _valid_args(variant)
+        mutate(a)
+        st, info = _info_status(variant, a)
+    assert st == code, (name, bnd.STATUS_NAMES.get(st))
+    assert info.kernel is None and info.grid_blocks == 0
+
+
+def test_kernel_info_own_errors_and_empty_batch(lib):
+    a = _valid_args("gdn")
+    info = bnd.KernelInfo()
+    assert lib.la_decode_kernel_info(1, ctypes.byref(a), None) == 1
+    assert lib.la_decode_kernel_info(3, ctypes.byref(a),
+                                     ctypes.byref(info)) == 6
+    assert lib.la_decode_kernel_info(-1, ctypes.byref(a),
+                                     ctypes.byref(info)) == 6
+    for variant in ("lightning", "gdn", "kda"):
+        a = _valid_args(variant)
+        a.B = 0
+        st, info = _info_status(variant, a)
+        assert st == 0 and info.kernel == b"none"
+        assert info.grid_blocks == 0 and info.block_threads == 0
 
 
 @pytest.mark.parametrize("variant", ["lightning", "gdn", "kda"])

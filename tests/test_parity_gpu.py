@@ -1626,3 +1626,60 @@ def test_one_token_kernel_bf16_state(variant, K, V):
                 pool_size=2 * B, seed=seed, pool_std=0.1, read_idx=ridx,
                 write_idx=widx, state_dtype=torch.bfloat16)
     run_and_check(wl, reqs=[0, 9, 13, 30, 51, 71])
+
+
+# ------------------------------------------------------------ kernel query
+
+
+@pytest.mark.parametrize("case", [
+    # (variant, B, T, HV, state dtype, expected kernel, threads)
+    ("gdn", 64, 1, 32, torch.float32, "decode1_kernel", 1024),
+    ("lightning", 33, 1, 64, torch.float32, "decode1_kernel", 1024),
+    ("gdn", 8, 1, 32, torch.float32, "decode_kernel", 256),
+    ("gdn", 64, 1, 32, torch.bfloat16, "decode_packed_kernel", 128),
+    ("gdn", 72, 1, 32, torch.bfloat16, "decode1_kernel", 1024),
+    ("kda", 96, 1, 24, torch.float32, "decode_kernel", 256),
+    ("kda", 8, 1, 24, torch.bfloat16, "decode_packed_kernel", 128),
+    ("gdn", 16, 4, 32, torch.float32, "decode_kernel", 256),
+], ids=lambda c: "%s_b%d_t%d_%s" % (c[0], c[1], c[2], str(c[4])[6:]))
+def test_kernel_info_reports_the_dispatch(case):
+    """la_decode_kernel_info names the kernel the call runs, with a launch
+    shape that matches the dispatch rule and a plausible register budget;
+    the call itself then runs and matches the oracle."""
+    variant, B, T, HV, state, kernel, threads = case
+    lad = _lad()
+    wl = W.make("info", variant, B=B, T=T, H=HV // 2 if variant == "gdn"
+                else HV, HV=HV, K=128, V=128, pool_size=2 * B, seed=7100 + B,
+                separate_write=True, state_dtype=state,
+                l2norm=variant != W.LIGHTNING)
+    d = wl.to(DEV)
+    kw = {}
+    if variant != W.LIGHTNING:
+        kw = dict(l2norm_qk=wl.l2norm, beta_logit=wl.beta_logit)
+    info = lad.kernel_info(variant, d.q, d.k, d.v, d.g, d.beta, d.pool(),
+                           d.read_idx, d.write_idx, **kw)
+    assert info["kernel"] == kernel
+    assert info["grid_blocks"] == B * HV
+    assert info["block_threads"] == threads
+    assert info["scratch_bytes"] == 0
+    assert 0 < info["vgprs"] <= 512
+    assert info["blocks_per_cu"] >= 1
+    assert info["waves_per_simd"] == info["blocks_per_cu"] * threads // 64 // 4
+    if kernel == "decode1_kernel":
+        assert info["lds_bytes"] == 0 and info["waves_per_simd"] == 8
+    if kernel == "decode_kernel":
+        per_token = (3 if variant == "kda" else 2) * 128 + 128 + 4
+        assert info["lds_bytes"] == min(T, 8) * per_token * 4
+        assert info["waves_per_simd"] >= 3
+    reqs = [0, B // 2, B - 1]
+    run_and_check(wl, reqs=reqs)
+
+
+def test_kernel_info_empty_batch():
+    lad = _lad()
+    wl = W.make("info0", W.GDN, B=2, T=1, H=2, HV=4, K=128, V=128,
+                pool_size=4, seed=7199)
+    d = wl.to(DEV)
+    info = lad.kernel_info("gdn", d.q[:0], d.k[:0], d.v[:0], d.g[:0],
+                           d.beta[:0], d.pool(), d.read_idx[:0])
+    assert info["kernel"] == "none" and info["grid_blocks"] == 0
