@@ -1752,8 +1752,9 @@ la_status la_decode_kernel_info(int32_t variant, const la_decode_args *args,
     if (variant != LA_VARIANT_LIGHTNING && variant != LA_VARIANT_GDN &&
         variant != LA_VARIANT_KDA)
         return LA_ERR_ARG;
-    static_assert(LA_VARIANT_LIGHTNING == VAR_LA && LA_VARIANT_GDN == VAR_GDN &&
-                      LA_VARIANT_KDA == VAR_KDA,
+    static_assert(static_cast<int>(LA_VARIANT_LIGHTNING) == VAR_LA &&
+                      static_cast<int>(LA_VARIANT_GDN) == VAR_GDN &&
+                      static_cast<int>(LA_VARIANT_KDA) == VAR_KDA,
                   "variant codes");
     Launch L;
     const la_status st = select_kernel(args, variant, L);
