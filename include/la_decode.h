@@ -166,8 +166,9 @@ typedef struct la_decode_args {
     int64_t token_slots_stride;
     const int32_t *num_accepted;
 
-    /* Per-token update records (aiter KDA page, advisory review: "cached
-     * (a,k,err) state updates" instead of full per-token states), or NULL:
+    /* Per-token update records (aiter KDA page, advisory review: each
+     * token's update kept as an (a, k, err) triple instead of a full
+     * per-token state), or NULL:
      * [B, T, HV, 2K + V] fp32, contiguous, 16-byte aligned. Record t of
      * (b, hv) holds a_t[K] (the decay: the KDA factors exp(g), or the GDN /
      * Lightning scalar repeated K times), k_t[K] (the key as used, after

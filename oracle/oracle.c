@@ -23,8 +23,8 @@
  *  - FlashInfer "fp32 sibling of #3268" description (4D pool
  *    [pool_size, HV, V, K]; "Separate read/write slots"; "API change -- one
  *    new argument"): the write slot defaults to the read slot and a negative
- *    write slot skips the writeback; a negative read slot is padding
- *    ("read-side -1 padding semantics").
+ *    write slot skips the writeback; a negative read slot is padding (the
+ *    write side mirrors the read side's -1 padding).
  *
  * Storage orientation: the pool stores each state tile as S[v][k] with k
  * contiguous (the [pool_size, HV, V, K] layout). The pages write the update
@@ -57,8 +57,8 @@
  * entry is not negative. A request whose accepted count is outside [1, T]
  * or whose seed entry is negative is padding, as above.
  *
- * Factor records (aiter KDA page, advisory review: "cached (a,k,err) state
- * updates"; its benchmark note: not writing every per-token state saves
+ * Factor records (aiter KDA page, advisory review: each token's update kept
+ * as an (a, k, err) triple rather than as a full state; its benchmark note: not writing every per-token state saves
  * runtime as tokens and batch grow): instead of the state after token t, a
  * record [a | k | err] of 2K + V values lets the state be rebuilt as
  * S_t = S_{t-1} diag(a_t) + err_t k_t^T. Here a_t is the token's decay (the
