@@ -1683,3 +1683,119 @@ def test_kernel_info_empty_batch():
     info = lad.kernel_info("gdn", d.q[:0], d.k[:0], d.v[:0], d.g[:0],
                            d.beta[:0], d.pool(), d.read_idx[:0])
     assert info["kernel"] == "none" and info["grid_blocks"] == 0
+
+
+# ------------------------------------- pools with padded rows and heads
+
+# NaN payloads that no kernel result equals
+_SENTINEL = {torch.float32: 0x7FC0DEAD, torch.bfloat16: 0x7F81}
+
+
+def _padded_pool(wl, row_pad, head_pad):
+    """A device buffer [P, HV + head_pad, V, K + row_pad] filled with a
+    NaN-payload sentinel whose [:, :HV, :, :K] view holds the workload's
+    pool: row and head strides larger than the tile, gaps in between."""
+    P, HV, V, K = wl.backing.shape
+    big = torch.empty((P, HV + head_pad, V, K + row_pad),
+                      dtype=wl.backing.dtype, device=DEV)
+    _bits(big).fill_(_SENTINEL[wl.backing.dtype])
+    big[:, :HV, :, :K] = wl.backing.to(DEV)
+    return big, big[:, :HV, :, :K]
+
+
+def _check_padding(wl, big, row_pad, head_pad):
+    HV, K = wl.HV, wl.K
+    s = _SENTINEL[wl.backing.dtype]
+    b = _bits(big.cpu())
+    if row_pad:
+        assert bool((b[:, :HV, :, K:] == s).all()), "row padding changed"
+    if head_pad:
+        assert bool((b[:, HV:] == s).all()), "head padding changed"
+
+
+PADDED_CASES = {
+    # general kernel, three tokens with the per-token cache
+    "general_gdn_t3": dict(variant=W.GDN, B=5, T=3, H=2, HV=4, K=128, V=128,
+                           pool_size=12, inter=True, pads=(4, 1)),
+    "general_kda_t1_v64": dict(variant=W.KDA, B=8, T=1, H=4, HV=4, K=128,
+                               V=64, pool_size=16, pads=(4, 1)),
+    # one-token kernel (>= 2048 fp32 tiles)
+    "one_token_gdn": dict(variant=W.GDN, B=64, T=1, H=16, HV=32, K=128,
+                          V=128, pool_size=128, pads=(4, 1)),
+    "one_token_lightning_k64": dict(variant=W.LIGHTNING, B=64, T=1, H=32,
+                                    HV=32, K=64, V=128, pool_size=128,
+                                    pads=(8, 0)),
+    # bf16 pools: packed kernel, one-token kernel, general kernel
+    "packed_bf16_lightning": dict(variant=W.LIGHTNING, B=8, T=1, H=4, HV=4,
+                                  K=128, V=128, pool_size=16, pads=(8, 1),
+                                  state_dtype=torch.bfloat16),
+    "one_token_bf16_gdn": dict(variant=W.GDN, B=72, T=1, H=16, HV=32, K=128,
+                               V=128, pool_size=144, pads=(8, 1),
+                               state_dtype=torch.bfloat16),
+    "general_bf16_kda_t2": dict(variant=W.KDA, B=6, T=2, H=2, HV=2, K=128,
+                                V=128, pool_size=12, pads=(16, 1),
+                                state_dtype=torch.bfloat16),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PADDED_CASES))
+def test_padded_rows_and_heads(name):
+    """Pools whose rows and heads are padded (row stride K + pad, head
+    stride with a gap): every kernel path agrees with the oracle, writes
+    only the write slots' tiles, and leaves every padding element's bits
+    as they were."""
+    case = dict(PADDED_CASES[name])
+    row_pad, head_pad = case.pop("pads")
+    variant = case.pop("variant")
+    seed = 7300 + sorted(PADDED_CASES).index(name)
+    wl = W.make("padded_" + name, variant, seed=seed, separate_write=True,
+                write_skip=0.2, l2norm=variant != W.LIGHTNING, **case)
+    lad = _lad()
+    d = wl.to(DEV)
+    big, pool = _padded_pool(wl, row_pad, head_pad)
+    assert pool.stride(2) == wl.K + row_pad
+    inter = None
+    if wl.inter:
+        inter = torch.full((wl.B, wl.T, wl.HV, wl.V, wl.K), float("nan"),
+                           dtype=wl.backing.dtype, device=DEV)
+    if variant == W.LIGHTNING:
+        out, _ = lad.la_decode(d.q, d.k, d.v, pool, d.read_idx, d.write_idx,
+                               lam=d.g, inter=inter)
+    else:
+        fn = lad.gdn_decode_mtp if variant == W.GDN else lad.kda_decode_mtp
+        out, _ = fn(d.q, d.k, d.v, d.g, d.beta, pool, d.read_idx,
+                    d.write_idx, inter=inter, l2norm_qk=wl.l2norm,
+                    beta_logit=wl.beta_logit)
+    torch.cuda.synchronize()
+    got = {"out": out.cpu(), "backing": pool.contiguous().cpu(),
+           "inter": None if inter is None else inter.cpu()}
+    reqs = None if wl.B <= 8 else [0, 1, wl.B // 2, wl.B - 1]
+    errs = check_parity(wl, got, wl.backing, reqs)
+    print("  %s errors %s" % (name, errs), flush=True)
+    _check_padding(wl, big, row_pad, head_pad)
+
+
+@pytest.mark.parametrize("state", [torch.float32, torch.bfloat16],
+                         ids=["f32", "bf16"])
+def test_replay_into_padded_pool(state):
+    """Replay into a pool with padded rows and heads gives the same bits as
+    replay into a contiguous pool, and leaves the padding untouched."""
+    lad = _lad()
+    wl = W.make("padrep", W.KDA, B=6, T=3, H=2, HV=4, K=128, V=128,
+                pool_size=12, seed=7400, separate_write=True,
+                state_dtype=state)
+    d = wl.to(DEV)
+    fac = torch.full((wl.B, wl.T, wl.HV, 2 * wl.K + wl.V), float("nan"),
+                     device=DEV)
+    lad.kda_decode_mtp(d.q, d.k, d.v, d.g, d.beta, d.backing.clone(),
+                       d.read_idx, None, factors=fac, l2norm_qk=True,
+                       beta_logit=True)
+    ntok = torch.tensor([3, 0, 1, 2, 3, 2], dtype=torch.int32, device=DEV)
+    plain = d.backing.clone()
+    lad.replay(fac, plain, d.read_idx, d.write_idx, ntok)
+    pad = 16 if state == torch.bfloat16 else 4
+    big, pool = _padded_pool(wl, pad, 1)
+    lad.replay(fac, pool, d.read_idx, d.write_idx, ntok)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(pool.contiguous()), _bits(plain))
+    _check_padding(wl, big, pad, 1)
