@@ -1799,3 +1799,47 @@ def test_replay_into_padded_pool(state):
     torch.cuda.synchronize()
     assert torch.equal(_bits(pool.contiguous()), _bits(plain))
     _check_padding(wl, big, pad, 1)
+
+
+# ------------------------------------------------- extreme decays and gates
+
+
+@pytest.mark.parametrize("variant", [W.GDN, W.KDA])
+@pytest.mark.parametrize("T,B,HV", [(3, 5, 4), (1, 64, 32)],
+                         ids=["t3_general", "t1_large"])
+def test_extreme_log_decays(variant, T, B, HV):
+    """Log-decays of -60 (the state all but erased: exp(-60) ~ 9e-27), -20
+    and 0 mixed per head and token (per channel for KDA); the T = 1 GDN case
+    runs the one-token kernel."""
+    wl = W.make("xdecay", variant, B=B, T=T, H=HV // 2, HV=HV, K=128,
+                V=128, pool_size=2 * B, seed=7500 + T, separate_write=True,
+                act_dtype=torch.float32)
+    gen = torch.Generator().manual_seed(7501 + T)
+    choice = torch.tensor([-60.0, -20.0, 0.0])
+    wl.g = choice[torch.randint(0, 3, wl.g.shape, generator=gen)]
+    reqs = None if B <= 8 else [0, 7, 33, B - 1]
+    run_and_check(wl, reqs=reqs)
+
+
+@pytest.mark.parametrize("variant", [W.GDN, W.KDA])
+@pytest.mark.parametrize("lower_bound", [None, -5.0], ids=["softplus", "lb"])
+def test_gate_chain_extreme_arguments(variant, lower_bound):
+    """The gate chain far into its tails: x + dt_bias in {-40, -5, 0, 5, 40}
+    (softplus then ~exp(-40), or exactly its argument above 20; the bounded
+    form's sigmoid saturating at both ends)."""
+    wl = W.make("xgate", variant, B=5, T=3, H=2, HV=4, K=128, V=128,
+                pool_size=12, seed=7600, separate_write=True,
+                act_dtype=torch.float32)
+    a_log, dt = _gate_inputs(variant, wl.HV, wl.K, 7601)
+    gen = torch.Generator().manual_seed(7602)
+    z = torch.tensor([-40.0, -5.0, 0.0, 5.0, 40.0])
+    zz = z[torch.randint(0, 5, wl.g.shape, generator=gen)]
+    dt_b = dt.view((1, 1) + tuple(dt.shape))
+    wl.g = (zz - dt_b).float()  # raw gate x = z - dt_bias
+    got, ref = _gate_run(wl, a_log, dt, lower_bound)
+    kind, tol_out, tol_state = _tol(wl)
+    assert _err(kind, got["out"].float(), ref["out"]) <= tol_out
+    for b, w in enumerate(wl.write_idx.tolist()):
+        if w >= 0:
+            assert _err(kind, got["backing"][w].float(),
+                        ref["pool"][w]) <= tol_state, b
