@@ -1843,3 +1843,83 @@ def test_gate_chain_extreme_arguments(variant, lower_bound):
         if w >= 0:
             assert _err(kind, got["backing"][w].float(),
                         ref["pool"][w]) <= tol_state, b
+
+
+# ------------------------------- slots beyond 2^31 elements, every kernel
+
+
+def _far_pool(wl):
+    """The workload's pool as a strided view whose slot stride puts its last
+    slots beyond 2^31 elements from the base (a 4-9 GB buffer)."""
+    P, HV, V, K = wl.backing.shape
+    es = wl.backing.element_size()
+    epc = 16 // es  # slot starts stay 16-byte aligned
+    tile = HV * V * K
+    stride = max(tile, -(-(2 ** 31) // (P - 1)))
+    stride = -(-stride // epc) * epc
+    buf = torch.empty((P - 1) * stride + tile, dtype=wl.backing.dtype,
+                      device=DEV)
+    pool = torch.as_strided(buf, (P, HV, V, K), (stride, V * K, K, 1))
+    pool.copy_(wl.backing.to(DEV))
+    assert (P - 1) * stride >= 2 ** 31
+    return buf, pool
+
+
+FAR_CASES = {
+    "one_token_f32": dict(variant=W.GDN, B=64, H=16, HV=32, pool_size=64),
+    "one_token_bf16": dict(variant=W.GDN, B=72, H=16, HV=32, pool_size=72,
+                           state_dtype=torch.bfloat16),
+    "packed_bf16": dict(variant=W.LIGHTNING, B=8, H=4, HV=4, pool_size=8,
+                        state_dtype=torch.bfloat16),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FAR_CASES))
+def test_far_slots_bit_identical_to_contiguous(name):
+    """One-token calls (the one-token and the packed kernel) whose read and
+    write slots lie beyond 2^31 elements from the pool base give the same
+    bits as the same call on a contiguous pool."""
+    case = dict(FAR_CASES[name])
+    variant = case.pop("variant")
+    wl = W.make("far_" + name, variant, T=1, K=128, V=128,
+                seed=7700 + sorted(FAR_CASES).index(name),
+                l2norm=variant != W.LIGHTNING, **case)
+    lad = _lad()
+    d = wl.to(DEV)
+    buf, far = _far_pool(wl)
+    near = d.backing.clone()
+    outs = []
+    for pool in (near, far):
+        if variant == W.LIGHTNING:
+            o, _ = lad.la_decode(d.q, d.k, d.v, pool, d.read_idx, lam=d.g)
+        else:
+            o, _ = lad.gdn_decode_mtp(d.q, d.k, d.v, d.g, d.beta, pool,
+                                      d.read_idx, l2norm_qk=wl.l2norm,
+                                      beta_logit=wl.beta_logit)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(outs[0]), _bits(outs[1]))
+    assert torch.equal(_bits(near), _bits(far.contiguous()))
+    assert not torch.equal(_bits(near), _bits(d.backing))  # states moved
+    del buf, far
+
+
+def test_replay_far_slots_bit_identical_to_contiguous():
+    """Replay with seed and write slots beyond 2^31 elements."""
+    lad = _lad()
+    wl = W.make("farrep", W.GDN, B=4, T=3, H=2, HV=4, K=128, V=128,
+                pool_size=8, seed=7790, separate_write=True)
+    d = wl.to(DEV)
+    fac = torch.full((wl.B, wl.T, wl.HV, 2 * wl.K + wl.V), float("nan"),
+                     device=DEV)
+    lad.gdn_decode_mtp(d.q, d.k, d.v, d.g, d.beta, d.backing.clone(),
+                       d.read_idx, None, factors=fac, l2norm_qk=True,
+                       beta_logit=True)
+    ntok = torch.tensor([3, 1, 0, 2], dtype=torch.int32, device=DEV)
+    near = d.backing.clone()
+    lad.replay(fac, near, d.read_idx, d.write_idx, ntok)
+    buf, far = _far_pool(wl)
+    lad.replay(fac, far, d.read_idx, d.write_idx, ntok)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(near), _bits(far.contiguous()))
+    del buf, far
