@@ -175,7 +175,8 @@ def decode(variant, q, k, v, g, beta, pool, read_idx, write_idx=None,
     pool_out = pool_in.copy()
     # NaN until the oracle writes it: a position it skips cannot pass as 0
     out = np.full(lead + (HV, V), np.nan, dtype=np.float64)
-    inter_a = np.zeros(lead + (HV, V, K), dtype=np.float64) if inter else None
+    inter_a = (np.full(lead + (HV, V, K), np.nan, dtype=np.float64)
+               if inter else None)
     fac = (np.full(lead + (HV, 2 * K + V), np.nan, dtype=np.float64)
            if factors else None)
     dp = ctypes.c_double

@@ -368,7 +368,7 @@ def test_padding_and_skipped_writes():
                         c["pool"], [2, -1, 5], [1, 3, -1], inter=True)
     # padded request: zero outputs, no cache rows, no pool write
     assert not res["out"][1].any()
-    assert not res["inter"][1].any()
+    assert np.isnan(res["inter"][1]).all()  # no cache row written
     # skipped write: outputs and cache are still computed
     assert np.abs(res["out"][2]).max() > 0 and np.abs(res["inter"][2]).max() > 0
     changed = [s for s in range(6)
