@@ -1923,3 +1923,138 @@ def test_replay_far_slots_bit_identical_to_contiguous():
     torch.cuda.synchronize()
     assert torch.equal(_bits(near), _bits(far.contiguous()))
     del buf, far
+
+
+# ------------------------------------------- random feature combinations
+
+
+def _combo(i):
+    """Configuration i of the combination sweep: a fixed draw over variant,
+    tile shape, T, head grouping, dtypes, flags, gate form, varlen, paged
+    slots, records, cache, strided pool, separate and skipped writes and a
+    padded request."""
+    import random
+    rng = random.Random(8000 + i)
+    variant = rng.choice([W.LIGHTNING, W.GDN, W.KDA])
+    K, V = rng.choice(SHAPES)
+    T = rng.choice([1, 2, 3, 5, 9])
+    HV = rng.choice([2, 4])
+    H = rng.choice([h for h in (1, 2, 4) if HV % h == 0])
+    B = rng.randint(1, 6)
+    paged = rng.random() < 0.25
+    sep = not paged and rng.random() < 0.5
+    cfg = dict(variant=variant, B=B, T=T, H=H, HV=HV, K=K, V=V,
+               act_dtype=rng.choice([torch.float32, torch.bfloat16]),
+               out_dtype=rng.choice([torch.float32, torch.bfloat16]),
+               state_dtype=rng.choice([torch.float32, torch.bfloat16]),
+               l2norm=rng.random() < 0.7, beta_logit=rng.random() < 0.7,
+               stride_mult=rng.choice([1, 1, 2]),
+               inter=rng.random() < 0.4, paged=paged, separate_write=sep,
+               write_skip=0.3 if sep and rng.random() < 0.5 else 0.0,
+               varlen_min=(rng.choice([0, 1]) if rng.random() < 0.3
+                           else None),
+               pool_size=B * T + 3 if paged else (2 * B + 3 if sep
+                                                   else B + 3))
+    gate = None
+    if variant != W.LIGHTNING and rng.random() < 0.35:
+        gate = rng.choice([None, -5.0])  # softplus form, or bounded
+        gate = ("lb", gate) if gate is not None else ("softplus", None)
+    records = rng.random() < 0.35
+    pad = None if paged or rng.random() < 0.7 else rng.randrange(B)
+    return cfg, gate, records, pad
+
+
+def _combo_compare(kind, tol, got, ref, state_bf16, what):
+    """NaN where the oracle wrote nothing, the tolerance elsewhere (plus one
+    bf16 step for values stored in bf16)."""
+    got = got.double()
+    ref = torch.as_tensor(np.asarray(ref, dtype=np.float64))
+    blank = torch.isnan(ref)
+    assert bool(torch.isnan(got[blank]).all()), what + ": wrote a blank row"
+    g, r = got[~blank], ref[~blank]
+    assert bool(torch.isfinite(g).all()), what + ": non-finite value"
+    if g.numel() == 0:
+        return 0.0
+    diff = (g - r).abs()
+    if state_bf16:
+        diff = (diff - r.abs() * 2.0 ** -7).clamp(min=0.0)
+    e = float(diff.max())
+    if kind == "rel":
+        e /= max(float(r.abs().max()), 1e-30)
+    assert e <= tol, (what, e)
+    return e
+
+
+@pytest.mark.parametrize("i", range(48))
+def test_random_feature_combinations(i):
+    """48 fixed draws from the whole feature space, each run through the C
+    ABI and compared with the oracle: outputs, per-token cache, update
+    records, every pool slot (slots the oracle leaves unchanged must keep
+    their bits) and the gaps of strided pools."""
+    cfg, gate, records, pad = _combo(i)
+    variant = cfg.pop("variant")
+    wl = W.make("combo%d" % i, variant, seed=8100 + i, **cfg)
+    if pad is not None:
+        wl.read_idx[pad] = -1
+    lad = _lad()
+    d = wl.to(DEV)
+    m = wl.stride_mult
+    pool = d.backing[::m]
+    varlen = wl.cu_seqlens is not None
+    paged = wl.token_slots is not None
+    lead = (wl.q.shape[0],) if varlen else (wl.B, wl.T)
+    out = torch.full(lead + (wl.HV, wl.V), float("nan"), dtype=wl.out_dtype,
+                     device=DEV)
+    inter = (torch.full(lead + (wl.HV, wl.V, wl.K), float("nan"),
+                        dtype=wl.backing.dtype, device=DEV)
+             if wl.inter else None)
+    fac = (torch.full(lead + (wl.HV, 2 * wl.K + wl.V), float("nan"),
+                      device=DEV) if records else None)
+    kw = dict(out=out, inter=inter, factors=fac, token_slots=d.token_slots,
+              num_accepted=d.num_accepted, out_dtype=wl.out_dtype)
+    okw = dict(token_slots=wl.token_slots, num_accepted=wl.num_accepted)
+    if varlen:
+        kw.update(cu_seqlens=d.cu_seqlens, max_tokens=wl.T)
+        okw.update(cu_seqlens=wl.cu_seqlens, max_tokens=wl.T)
+    if gate is not None:
+        a_log, dt = _gate_inputs(variant, wl.HV, wl.K, 8200 + i)
+        kw.update(A_log=a_log.to(DEV), dt_bias=dt.to(DEV),
+                  lower_bound=gate[1])
+        okw.update(A_log=a_log, dt_bias=dt, lower_bound=gate[1])
+    ridx = None if paged else d.read_idx
+    widx = None if paged else d.write_idx
+    if variant == W.LIGHTNING:
+        lad.la_decode(d.q, d.k, d.v, pool, ridx, widx, lam=d.g, **kw)
+    else:
+        fn = lad.gdn_decode_mtp if variant == W.GDN else lad.kda_decode_mtp
+        fn(d.q, d.k, d.v, d.g, d.beta, pool, ridx, widx,
+           l2norm_qk=wl.l2norm, beta_logit=wl.beta_logit, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.decode(VARIANT_CODE[variant], wl.q, wl.k, wl.v, wl.g,
+                        wl.beta, wl.pool(), None if paged else wl.read_idx,
+                        None if paged else wl.write_idx, flags=_flags(wl),
+                        inter=wl.inter, factors=records, **okw)
+    kind, tol_out, tol_state = _tol(wl)
+    sb = wl.backing.dtype == torch.bfloat16
+    ob = wl.out_dtype == torch.bfloat16
+    _combo_compare(kind, tol_out, out.cpu(), ref["out"], ob, "out")
+    if wl.inter:
+        _combo_compare(kind, tol_state, inter.cpu(), ref["inter"], sb,
+                       "inter")
+    if records:
+        _combo_compare(kind, tol_state, fac.cpu(), ref["factors"], False,
+                       "records")
+    before = wl.backing
+    after = d.backing.cpu()
+    logical_in = wl.pool().double().numpy()
+    for s in range(wl.pool_size):
+        if np.array_equal(ref["pool"][s], logical_in[s]):
+            assert torch.equal(_bits(after[m * s]), _bits(before[m * s])), \
+                "slot %d changed" % s
+        else:
+            _combo_compare(kind, tol_state, after[m * s], ref["pool"][s], sb,
+                           "slot %d" % s)
+    if m > 1:
+        gaps = [j for j in range(before.shape[0]) if j % m]
+        assert torch.equal(_bits(after[gaps]), _bits(before[gaps])), \
+            "a stride gap changed"
