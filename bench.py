@@ -332,7 +332,7 @@ def cpu_baseline(wl, seconds):
 def main():
     args = _parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: this library has no multi-GPU path "
               "(the decode shards by request or head with no exchange; see "
               "the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
