@@ -333,8 +333,8 @@ def main():
     args = _parse()
     if args.gpus != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path "
-              "(the decode shards by request or head with no exchange; see "
-              "the design notes). Run with --gpus 1.", file=sys.stderr)
+              "(the decode shards by request or by value head with no "
+              "exchange between GPUs). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
     import linear_attention_recurrent_slot_amd as lad
