@@ -31,8 +31,7 @@
  * with the mathematical state as K x V (S^T k); in storage that read-out is
  * the row-wise dot product u[v] = sum_k S[v][k] * k[k].
  *
- * Readings where the pages are silent (each is listed with its reason in the
- * design notes of the repository):
+ * Readings where the pages are silent:
  *  - Lightning: the pages name the operation only. The update is the
  *    decay-masked linear-attention recurrence S <- lambda_h * S + v k^T,
  *    o = S q, with the standard per-head decay lambda_h = exp(-2^(-8(h+1)/H))
