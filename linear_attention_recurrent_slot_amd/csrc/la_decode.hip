@@ -224,6 +224,13 @@ constexpr int kStreamPolicy = 2;
 // bf16 kernel (66.1 -> 64.8 %), which keeps kStreamPolicy. sc1 alone, or sc0
 // with or without it and without nt, was 1-9 points slower.
 constexpr int kStorePolicy = 18;
+// Tile loads of a call that writes update records: ordinary cached loads.
+// Such a call is a speculative verify, and the replay that follows re-reads
+// the same seed tiles, which then come from the Infinity Cache. Measured on
+// MI355X (verify + replay, 4 GiB rotation between steps, % of peak HBM
+// bandwidth on the algorithmic bytes): KDA B=64 T=4 60.6 -> 64.9, KDA B=256
+// 68.1 -> 72.4, GDN B=64 64.2 -> 68.6, KDA with a bf16 pool 48.5 -> 50.2.
+constexpr int kRecordLoadPolicy = 0;
 
 __device__ __forceinline__ BufRsrc make_rsrc(const void *base, uint32_t bytes)
 {
@@ -595,7 +602,7 @@ decode_kernel(const Params p)
     f4 S[RPL][CPL];
 #pragma unroll
     for (int i = 0; i < RPL; ++i)
-        IO::template load_row<kStreamPolicy>(
+        IO::template load_row<REC ? kRecordLoadPolicy : kStreamPolicy>(
             S[i], src, lane_off, (wave * kRowsPerWave + i * 8) * row_bytes);
 
     for (int t0 = 0; t0 < Tb; t0 += kTokChunk) {
