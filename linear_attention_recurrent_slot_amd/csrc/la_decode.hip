@@ -61,6 +61,12 @@ enum Variant { VAR_LA = 0, VAR_GDN = 1, VAR_KDA = 2 };
 #endif
 
 constexpr int kRowsPerWave = LA_ROWS_PER_WAVE;
+// Rows per wave of calls that write update records (speculative verify):
+// twice the waves per tile and a smaller register footprint than 32 rows
+// (occupancy 4 instead of 3 for KDA). Measured on MI355X, KDA B=64 T=4
+// verify + replay: 63.3 -> 61.0 us per step (64.9 -> 67.3 % of peak); plain
+// calls keep kRowsPerWave (KDA B=256 T=1: 32 rows 144.2 us, 16 rows 155.0).
+constexpr int kRecordRowsPerWave = 16;
 static_assert(kRowsPerWave == 8 || kRowsPerWave == 16 || kRowsPerWave == 32,
               "8, 16 or 32 rows");
 constexpr int kTokChunk = 8;
@@ -532,10 +538,12 @@ __device__ __forceinline__ bool request_tokens(const int32_t *cu, int32_t total,
 #endif
 
 // REC: also write the per-token update records (a separate instantiation so
-// that the ordinary path carries none of their register cost).
+// that the ordinary path carries none of their register cost). R: state rows
+// per wave (the workgroup has V / R waves); it only distributes rows over
+// waves, each row's arithmetic is the same for every R.
 template <int VAR, int K, int V, bool BF16IN, bool BF16OUT, bool BF16S,
-          bool REC>
-__global__ void __launch_bounds__((V / kRowsPerWave) * 64) LA_OCCUPANCY
+          bool REC, int R>
+__global__ void __launch_bounds__((V / R) * 64) LA_OCCUPANCY
 decode_kernel(const Params p)
 {
     using IO = StateIO<BF16S>;
@@ -543,8 +551,8 @@ decode_kernel(const Params p)
     extern __shared__ f4 lds_raw[];
     float *lds = reinterpret_cast<float *>(lds_raw);
     using L = TokLayout<VAR, K, V>;
-    constexpr int NW = V / kRowsPerWave;  // waves per workgroup
-    constexpr int RPL = kRowsPerWave / 8;  // rows per lane
+    constexpr int NW = V / R;  // waves per workgroup
+    constexpr int RPL = R / 8;  // rows per lane
     constexpr int CPL = K / 32;            // 16-byte chunks per lane and row
     constexpr int TPW = (kTokChunk + NW - 1) / NW;  // prologue tokens per wave
 
@@ -579,7 +587,7 @@ decode_kernel(const Params p)
 
     // Output row written by this lane (lanes with c8 < RPL cover the wave's
     // rows exactly once): row R wave + 8 c8 + rs.
-    const int orow = wave * kRowsPerWave + (c8 & (RPL - 1)) * 8 + rs;
+    const int orow = wave * R + (c8 & (RPL - 1)) * 8 + rs;
     const bool olane = c8 < RPL;
     const int32_t obase = b * p.so_b + tok0 * p.so_t + hv * p.so_h + orow;
 
@@ -603,7 +611,7 @@ decode_kernel(const Params p)
 #pragma unroll
     for (int i = 0; i < RPL; ++i)
         IO::template load_row<REC ? kRecordLoadPolicy : kStreamPolicy>(
-            S[i], src, lane_off, (wave * kRowsPerWave + i * 8) * row_bytes);
+            S[i], src, lane_off, (wave * R + i * 8) * row_bytes);
 
     for (int t0 = 0; t0 < Tb; t0 += kTokChunk) {
         const int nt = min(kTokChunk, Tb - t0);
@@ -613,7 +621,7 @@ decode_kernel(const Params p)
             TokRaw<K, V> rw;
             prologue_load<VAR, K, V, BF16IN>(p, b, hv, tok0 + t0 + tt, lane,
                                              rw);
-            prologue_finish<VAR, K, V>(
+            prologue_finish<VAR, K, V, R>(
                 p, hv, lane, rw, lds + tt * L::size,
                 REC ? factor_record<K, V>(p, flat0 + t0 + tt, hv) : nullptr);
         }
@@ -628,7 +636,7 @@ decode_kernel(const Params p)
             float vr[RPL];
 #pragma unroll
             for (int i = 0; i < RPL; ++i)
-                vr[i] = rec[L::vOff + wave * kRowsPerWave + rs * RPL + i];
+                vr[i] = rec[L::vOff + wave * R + rs * RPL + i];
 
             // decay
             if constexpr (VAR == VAR_KDA) {
@@ -727,7 +735,7 @@ decode_kernel(const Params p)
 #pragma unroll
                     for (int i = 0; i < RPL; ++i)
                         IO::store_row(dst, lane_off,
-                                      (wave * kRowsPerWave + i * 8) * row_bytes,
+                                      (wave * R + i * 8) * row_bytes,
                                       S[i]);
                 }
             }
@@ -743,7 +751,7 @@ decode_kernel(const Params p)
 #pragma unroll
                 for (int i = 0; i < RPL; ++i)
                     IO::store_row(dst, ioff,
-                                  (wave * kRowsPerWave + i * 8) * K * ES, S[i]);
+                                  (wave * R + i * 8) * K * ES, S[i]);
             }
         }
     }
@@ -754,7 +762,7 @@ decode_kernel(const Params p)
 #pragma unroll
         for (int i = 0; i < RPL; ++i)
             IO::store_row(dst, lane_off,
-                          (wave * kRowsPerWave + i * 8) * row_bytes, S[i]);
+                          (wave * R + i * 8) * row_bytes, S[i]);
     }
 }
 
@@ -1345,11 +1353,12 @@ typedef void (*KernelFn)(const Params);
 template <int VAR, int K, int V, bool BF16S, bool REC>
 KernelFn pick_io(bool bf16_in, bool bf16_out)
 {
+    constexpr int R = REC ? kRecordRowsPerWave : kRowsPerWave;
     if (bf16_in)
-        return bf16_out ? decode_kernel<VAR, K, V, true, true, BF16S, REC>
-                        : decode_kernel<VAR, K, V, true, false, BF16S, REC>;
-    return bf16_out ? decode_kernel<VAR, K, V, false, true, BF16S, REC>
-                    : decode_kernel<VAR, K, V, false, false, BF16S, REC>;
+        return bf16_out ? decode_kernel<VAR, K, V, true, true, BF16S, REC, R>
+                        : decode_kernel<VAR, K, V, true, false, BF16S, REC, R>;
+    return bf16_out ? decode_kernel<VAR, K, V, false, true, BF16S, REC, R>
+                    : decode_kernel<VAR, K, V, false, false, BF16S, REC, R>;
 }
 
 template <int VAR, int K, int V>
@@ -1734,9 +1743,10 @@ la_status select_kernel(const la_decode_args *a, int var, Launch &L)
             lds_floats_per_token(var, a->K, a->V) * sizeof(float);
     L.grid = dim3(static_cast<unsigned>(a->B) * a->HV);
     // rows per wave: 64 in the packed kernel, 8 in the one-token kernel,
-    // kRowsPerWave otherwise
+    // kRecordRowsPerWave with records, kRowsPerWave otherwise
     L.block = dim3(packed ? a->V
                    : one  ? (a->V / 8) * 64
+                   : rec  ? (a->V / kRecordRowsPerWave) * 64
                           : (a->V / kRowsPerWave) * 64);
     return LA_OK;
 }
