@@ -2058,3 +2058,63 @@ def test_random_feature_combinations(i):
         gaps = [j for j in range(before.shape[0]) if j % m]
         assert torch.equal(_bits(after[gaps]), _bits(before[gaps])), \
             "a stride gap changed"
+
+
+# ------------------------------------------- sharding by head and by request
+
+
+@pytest.mark.parametrize("variant,B,HV,H", [(W.GDN, 64, 32, 16),
+                                            (W.LIGHTNING, 33, 64, 64),
+                                            (W.KDA, 16, 24, 24)],
+                         ids=["gdn_gva", "lightning", "kda"])
+def test_head_and_request_shards_equal_the_full_call(variant, B, HV, H):
+    """The decode shards with no exchange: running it on head slices (the
+    pool's heads, the matching value heads and their q/k heads) or on
+    request subsets gives the full call's bits. For the GDN and Lightning
+    shapes the full call runs the one-token kernel and the shards the
+    general one."""
+    lad = _lad()
+    wl = W.make("shard", variant, B=B, T=1, H=H, HV=HV, K=128, V=128,
+                pool_size=2 * B, seed=7800 + HV, separate_write=True,
+                l2norm=variant != W.LIGHTNING)
+    d = wl.to(DEV)
+    group = HV // H
+
+    def run(pool, sl_b, h0, h1):
+        q0, q1 = h0 // group, h1 // group
+        q = d.q[sl_b, :, q0:q1]
+        k = d.k[sl_b, :, q0:q1]
+        v = d.v[sl_b, :, h0:h1]
+        sub = pool[:, h0:h1]
+        if variant == W.LIGHTNING:
+            lam = d.g[h0:h1].contiguous() if d.g is not None else None
+            if lam is None:  # the built-in schedule depends on HV: pass it
+                hh = torch.arange(HV, dtype=torch.float64)
+                lam = torch.exp(-torch.exp2(-8.0 * (hh + 1) / HV)).float()[
+                    h0:h1].to(DEV)
+            o, _ = lad.la_decode(q, k, v, sub, d.read_idx[sl_b],
+                                 d.write_idx[sl_b], lam=lam)
+        else:
+            fn = lad.gdn_decode_mtp if variant == W.GDN else \
+                lad.kda_decode_mtp
+            o, _ = fn(q, k, v, d.g[sl_b, :, h0:h1], d.beta[sl_b, :, h0:h1],
+                      sub, d.read_idx[sl_b], d.write_idx[sl_b],
+                      l2norm_qk=wl.l2norm, beta_logit=wl.beta_logit)
+        return o
+
+    full_pool = d.backing.clone()
+    full = run(full_pool, slice(0, B), 0, HV)
+    # four head shards, each keeping whole q/k groups
+    hs = HV // 4
+    heads_pool = d.backing.clone()
+    outs = [run(heads_pool, slice(0, B), i * hs, (i + 1) * hs)
+            for i in range(4)]
+    # two request shards
+    req_pool = d.backing.clone()
+    routs = [run(req_pool, slice(0, B // 2), 0, HV),
+             run(req_pool, slice(B // 2, B), 0, HV)]
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(torch.cat(outs, dim=2)), _bits(full))
+    assert torch.equal(_bits(heads_pool), _bits(full_pool))
+    assert torch.equal(_bits(torch.cat(routs, dim=0)), _bits(full))
+    assert torch.equal(_bits(req_pool), _bits(full_pool))
