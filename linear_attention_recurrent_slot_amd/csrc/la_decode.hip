@@ -1701,22 +1701,34 @@ la_status select_kernel(const la_decode_args *a, int var, Launch &L)
     const bool bi = a->qkv_dtype == LA_BF16, bo = a->out_dtype == LA_BF16;
     const bool bs = a->state_dtype == LA_BF16;
     const bool rec = a->factors != nullptr;
-    // One token of Lightning or GDN with no per-token writes over at least
-    // 2048 tiles (fp32 pool) or more than 2048 (bf16 pool): the
-    // contiguous-row kernel. All three kernels give identical bits, so the
-    // choice is by speed alone. Measured on MI355X with a 4 GiB rotation,
-    // % of peak HBM bandwidth, previous kernel -> this one:
+    // One token of Lightning or GDN with no per-token writes: the
+    // contiguous-row kernel where it is the faster one. All three kernels
+    // give identical bits, so the choice is by speed alone. Measured on
+    // MI355X with a 4 GiB rotation, % of peak HBM bandwidth, previous kernel
+    // -> this one:
     //   fp32 Lightning B=33 H=64: 71.0 -> 74.3; GDN B=64 HV=32: 66.8 -> 68.7
     //   bf16 GDN B=72..96 HV=32: 57-62 -> 62-67; Lightning H=64
     //   B=36..48: 62-64 -> 69-71
     // At 512-1024 fp32 tiles it was 9-12 % slower, and KDA (B=256 H=24) 1 %
     // slower. On a bf16 pool the packed kernel keeps 2048 tiles in one
     // resident round and is 3-5 % faster there (GDN B=64 HV=32: 66.2 vs
-    // 62.9; Lightning B=32 H=64: 68.7 vs 67.0).
+    // 62.9; Lightning B=32 H=64: 68.7 vs 67.0); above that the one-token
+    // kernel beats the general one at every head count measured (HV 8-64,
+    // 2.5-6 points). On fp32 pools at K = V = 128 the general kernel wins
+    // below 32 value heads (GDN HV=16 B=256: 67.8 vs 64.7; HV=24 B=256:
+    // 70.2 vs 66.5; Lightning HV=16 B=256: 69.4 vs 66.8) and at 32 heads
+    // beyond 4096 tiles (GDN B=256: 71.3 vs 70.1), while the one-token kernel
+    // wins from 48 heads at every size (HV=64 B=128: 78.6 vs 73.7). The
+    // other tile shapes need 4096 tiles (GDN K=V=64 HV=32: 57.4 vs 65.5 at
+    // 2048 tiles, 66.5 vs 64.5 at 8192).
     const int64_t tiles = static_cast<int64_t>(a->B) * a->HV;
+    const bool wide = a->K == 128 && a->V == 128
+                          ? tiles >= 2048 &&
+                                (a->HV >= 48 || (a->HV >= 32 && tiles <= 4096))
+                          : tiles >= 4096;
     const bool one = var != VAR_KDA && a->T == 1 && !a->inter &&
                      !a->token_slots && !rec && !a->cu_seqlens &&
-                     (bs ? tiles > 2048 : tiles >= 2048);
+                     (bs ? tiles > 2048 : wide);
     // otherwise one token on a bf16 pool with no per-token writes: the
     // packed tile
     const bool packed = !one && bs && a->T == 1 && !a->inter &&

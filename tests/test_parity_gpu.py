@@ -1463,14 +1463,14 @@ def test_hip_graph_capture_replays_match_eager(variant):
                                        (torch.bfloat16, torch.bfloat16)],
                          ids=["f32", "bf16", "bf16_out_bf16"])
 def test_one_token_kernel_parity(variant, K, V, dtype, out):
-    """Lightning/GDN, T = 1, fp32 pool, B * HV = 2048 tiles: the
-    contiguous-row one-token kernel. Padded requests, separate and skipped
-    writes on a strided pool; sampled requests against the oracle, every
-    untouched byte checked."""
+    """Lightning/GDN, T = 1, fp32 pool, B * HV = 2048 tiles at K = V = 128
+    and 4096 at the other shapes: the contiguous-row one-token kernel.
+    Padded requests, separate and skipped writes on a strided pool; sampled
+    requests against the oracle, every untouched byte checked."""
     seed = (6000 + 100 * [W.LIGHTNING, W.GDN].index(variant)
             + 10 * SHAPES.index((K, V)) + (5 if dtype != torch.float32 else 0)
             + (2 if out != torch.float32 else 0))
-    B, HV = 64, 32
+    B, HV = (64 if (K, V) == (128, 128) else 128), 32
     ridx = list(range(0, 2 * B, 2))
     widx = [s + 1 for s in ridx]
     for b in (3, 17, 40):
@@ -1481,13 +1481,15 @@ def test_one_token_kernel_parity(variant, K, V, dtype, out):
                 pool_size=2 * B, seed=seed, act_dtype=dtype, pool_std=0.1,
                 stride_mult=2 if K == V else 1, read_idx=ridx,
                 write_idx=widx, out_dtype=out)
-    run_and_check(wl, reqs=[0, 3, 5, 11, 17, 22, 40, 47, 63])
+    assert _kernel_name(wl) == "decode1_kernel"
+    run_and_check(wl, reqs=[0, 3, 5, 11, 17, 22, 40, 47, 63, B - 1])
 
 
 def test_one_token_kernel_gate_chain():
     """The gate chain (both forms) in the one-token GDN kernel."""
     wl = W.make("onegate", W.GDN, B=64, T=1, H=16, HV=32, K=128, V=128,
                 pool_size=128, seed=6300, separate_write=True)
+    assert _kernel_name(wl) == "decode1_kernel"
     wl.g = 2 * torch.randn(wl.g.shape, generator=torch.Generator()
                            .manual_seed(6301))
     a_log, dt = _gate_inputs(W.GDN, wl.HV, wl.K, 6302)
@@ -1534,6 +1536,17 @@ def test_one_token_kernel_token_split_bit_identical(variant, dtype):
     assert torch.equal(_bits(pool.cpu()), _bits(whole["backing"]))
 
 
+def _kernel_name(wl):
+    """The kernel la_decode_kernel_info names for wl's call."""
+    lad = _lad()
+    d = wl.to(DEV)
+    kw = {}
+    if wl.variant != W.LIGHTNING:
+        kw = dict(l2norm_qk=wl.l2norm, beta_logit=wl.beta_logit)
+    return lad.kernel_info(wl.variant, d.q, d.k, d.v, d.g, d.beta, d.pool(),
+                           d.read_idx, d.write_idx, **kw)["kernel"]
+
+
 def _one_token_batch_invariance(wl, sub=8, **kw):
     """Outputs and pool of one call over wl's whole batch, and of the same
     requests in calls of `sub` requests on a second copy of the pool."""
@@ -1569,11 +1582,14 @@ def _one_token_batch_invariance(wl, sub=8, **kw):
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16],
                          ids=["f32", "bf16"])
 def test_one_token_kernel_batch_invariant(variant, raw, K, V, state, dtype):
-    """The same requests in one call of 2304 tiles (one-token kernel) and in
-    calls of 8 requests (256 tiles: decode_kernel, or the packed kernel on a
-    bf16 pool) give the same bits, outputs and stored states; `raw` passes
-    q, k without l2norm and beta without the sigmoid."""
+    """The same requests in one call of 2304 tiles (one-token kernel; 4352
+    for an fp32 pool at the shapes other than K = V = 128) and in calls of
+    8 requests (256 tiles: decode_kernel, or the packed kernel on a bf16
+    pool) give the same bits, outputs and stored states; `raw` passes q, k
+    without l2norm and beta without the sigmoid."""
     B, HV = 72, 32
+    if state == torch.float32 and (K, V) != (128, 128):
+        B = 136
     seed = (6700 + 10 * SHAPES.index((K, V)) + (1 if raw else 0)
             + (2 if state != torch.float32 else 0)
             + (4 if dtype != torch.float32 else 0)
@@ -1587,6 +1603,7 @@ def test_one_token_kernel_batch_invariant(variant, raw, K, V, state, dtype):
         wl.k = (wl.k.float() / K ** 0.5).to(dtype)
         wl.beta = torch.rand(wl.beta.shape, generator=torch.Generator()
                              .manual_seed(seed))
+    assert _kernel_name(wl) == "decode1_kernel"
     (wo, wp), (so, sp) = _one_token_batch_invariance(wl)
     assert torch.isfinite(wo).all()
     assert torch.equal(_bits(wo), _bits(so))
@@ -1625,6 +1642,7 @@ def test_one_token_kernel_bf16_state(variant, K, V):
     wl = W.make("onebf", variant, B=B, T=1, H=16, HV=32, K=K, V=V,
                 pool_size=2 * B, seed=seed, pool_std=0.1, read_idx=ridx,
                 write_idx=widx, state_dtype=torch.bfloat16)
+    assert _kernel_name(wl) == "decode1_kernel"
     run_and_check(wl, reqs=[0, 9, 13, 30, 51, 71])
 
 
@@ -1641,7 +1659,16 @@ def test_one_token_kernel_bf16_state(variant, K, V):
     ("kda", 96, 1, 24, torch.float32, "decode_kernel", 256),
     ("kda", 8, 1, 24, torch.bfloat16, "decode_packed_kernel", 128),
     ("gdn", 16, 4, 32, torch.float32, "decode_kernel", 256),
-], ids=lambda c: "%s_b%d_t%d_%s" % (c[0], c[1], c[2], str(c[4])[6:]))
+    # fp32 pools: fewer than 32 value heads, or 32 heads beyond 4096 tiles,
+    # take the general kernel; 48 or more heads the one-token kernel
+    ("gdn", 128, 1, 16, torch.float32, "decode_kernel", 256),
+    ("lightning", 96, 1, 24, torch.float32, "decode_kernel", 256),
+    ("gdn", 136, 1, 32, torch.float32, "decode_kernel", 256),
+    ("gdn", 128, 1, 32, torch.float32, "decode1_kernel", 1024),
+    ("gdn", 96, 1, 48, torch.float32, "decode1_kernel", 1024),
+    ("gdn", 136, 1, 16, torch.bfloat16, "decode1_kernel", 1024),
+], ids=lambda c: "%s_b%d_t%d_hv%d_%s" % (c[0], c[1], c[2], c[3],
+                                      str(c[4])[6:]))
 def test_kernel_info_reports_the_dispatch(case):
     """la_decode_kernel_info names the kernel the call runs, with a launch
     shape that matches the dispatch rule and a plausible register budget;
