@@ -49,6 +49,9 @@ def _parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU time budget of the oracle baseline (0: skip)")
     ap.add_argument("--no-copy-probe", action="store_true")
+    ap.add_argument("--head-shards", type=int, default=1,
+                    help="measure one GPU's share when this many GPUs split "
+                         "the value heads (1: the whole workload)")
     return ap.parse_args()
 
 
@@ -344,6 +347,8 @@ def main():
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     wl = workloads.named(args.workload)
+    if args.head_shards > 1:
+        wl = workloads.head_shard(wl, args.head_shards)
     per_call = wl.state_bytes() + wl.io_bytes()
     pool_bytes = wl.backing.numel() * wl.backing.element_size()
     R = args.rotate or min(ROTATE_MAX, max(2, math.ceil(ROTATE_BYTES / per_call)))
@@ -415,7 +420,7 @@ def main():
                    "spec_records_replay": wl.replay_tokens is not None,
                    "varlen_tokens": (wl.tokens if wl.cu_seqlens is not None
                                      else None),
-                   "rotation": R},
+                   "rotation": R, "head_shards": args.head_shards},
         "roofline": {"bound": "hbm", "achieved": achieved,
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic},

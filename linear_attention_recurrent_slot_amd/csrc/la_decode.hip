@@ -67,6 +67,20 @@ constexpr int kRowsPerWave = LA_ROWS_PER_WAVE;
 // verify + replay: 63.3 -> 61.0 us per step (64.9 -> 67.3 % of peak); plain
 // calls keep kRowsPerWave (KDA B=256 T=1: 32 rows 144.2 us, 16 rows 155.0).
 constexpr int kRecordRowsPerWave = 16;
+// Rows per wave of grids that fill less than one resident round: the same
+// tiles over twice the waves keep more loads in flight on an underfilled
+// chip. Used while B * HV * (V / 16) <= kSmallGridWaves, which at V = 128
+// is 512 tiles: 4096 waves, the resident capacity of this instance (82-89
+// VGPRs, two 8-wave workgroups per CU, 4 waves per SIMD), where 32 rows per
+// wave leave at most 2 waves per SIMD. Measured on MI355X, % of peak HBM bandwidth,
+// 32 -> 16 rows: GDN B=16 HV=32 63.5 -> 66.9; KDA B=16 H=24 62.4 -> 64.6;
+// GDN B=64 HV=8 63.7 -> 66.2; GDN B=16 HV=32 T=4 53.6 -> 65.7; KDA B=16
+// H=24 T=8 35.6 -> 43.8; GDN K=V=64 B=32 HV=32 T=4 42.0 -> 49.5. Two
+// grids lost 1-3 % (Lightning B=33 H=8 47.2 -> 46.3; GDN B=32 HV=8 T=4
+// with the cache 62.5 -> 60.9). At 768 tiles two rounds are needed and 16
+// rows lose (GDN B=24 HV=32: 72.5 -> 62.7).
+constexpr int kSmallGridRowsPerWave = 16;
+constexpr int64_t kSmallGridWaves = 4096;
 static_assert(kRowsPerWave == 8 || kRowsPerWave == 16 || kRowsPerWave == 32,
               "8, 16 or 32 rows");
 constexpr int kTokChunk = 8;
@@ -1350,10 +1364,9 @@ check_cu_seqlens_kernel(int32_t B, int32_t T, int32_t total,
 
 typedef void (*KernelFn)(const Params);
 
-template <int VAR, int K, int V, bool BF16S, bool REC>
+template <int VAR, int K, int V, bool BF16S, bool REC, int R>
 KernelFn pick_io(bool bf16_in, bool bf16_out)
 {
-    constexpr int R = REC ? kRecordRowsPerWave : kRowsPerWave;
     if (bf16_in)
         return bf16_out ? decode_kernel<VAR, K, V, true, true, BF16S, REC, R>
                         : decode_kernel<VAR, K, V, true, false, BF16S, REC, R>;
@@ -1362,13 +1375,21 @@ KernelFn pick_io(bool bf16_in, bool bf16_out)
 }
 
 template <int VAR, int K, int V>
-KernelFn pick_dtype(bool bf16_in, bool bf16_out, bool bf16_state, bool rec)
+KernelFn pick_dtype(bool bf16_in, bool bf16_out, bool bf16_state, bool rec,
+                    bool small)
 {
+    constexpr int RR = kRecordRowsPerWave, RS = kSmallGridRowsPerWave;
+    constexpr int RP = kRowsPerWave;
     if (rec)
-        return bf16_state ? pick_io<VAR, K, V, true, true>(bf16_in, bf16_out)
-                          : pick_io<VAR, K, V, false, true>(bf16_in, bf16_out);
-    return bf16_state ? pick_io<VAR, K, V, true, false>(bf16_in, bf16_out)
-                      : pick_io<VAR, K, V, false, false>(bf16_in, bf16_out);
+        return bf16_state
+                   ? pick_io<VAR, K, V, true, true, RR>(bf16_in, bf16_out)
+                   : pick_io<VAR, K, V, false, true, RR>(bf16_in, bf16_out);
+    if (small)
+        return bf16_state
+                   ? pick_io<VAR, K, V, true, false, RS>(bf16_in, bf16_out)
+                   : pick_io<VAR, K, V, false, false, RS>(bf16_in, bf16_out);
+    return bf16_state ? pick_io<VAR, K, V, true, false, RP>(bf16_in, bf16_out)
+                      : pick_io<VAR, K, V, false, false, RP>(bf16_in, bf16_out);
 }
 
 template <int VAR, int K, int V>
@@ -1419,13 +1440,13 @@ KernelFn pick_one(int K, int V, bool bi, bool bo, bool bs)
 }
 
 template <int VAR>
-KernelFn pick(int K, int V, bool bi, bool bo, bool bs, bool rec)
+KernelFn pick(int K, int V, bool bi, bool bo, bool bs, bool rec, bool small)
 {
     if (K == 128)
-        return V == 128 ? pick_dtype<VAR, 128, 128>(bi, bo, bs, rec)
-                        : pick_dtype<VAR, 128, 64>(bi, bo, bs, rec);
-    return V == 128 ? pick_dtype<VAR, 64, 128>(bi, bo, bs, rec)
-                    : pick_dtype<VAR, 64, 64>(bi, bo, bs, rec);
+        return V == 128 ? pick_dtype<VAR, 128, 128>(bi, bo, bs, rec, small)
+                        : pick_dtype<VAR, 128, 64>(bi, bo, bs, rec, small);
+    return V == 128 ? pick_dtype<VAR, 64, 128>(bi, bo, bs, rec, small)
+                    : pick_dtype<VAR, 64, 64>(bi, bo, bs, rec, small);
 }
 
 int lds_floats_per_token(int var, int K, int V)
@@ -1733,6 +1754,9 @@ la_status select_kernel(const la_decode_args *a, int var, Launch &L)
     // packed tile
     const bool packed = !one && bs && a->T == 1 && !a->inter &&
                         !a->token_slots && !rec && !a->cu_seqlens;
+    // a grid of the general kernel that fills less than one resident round
+    const bool small = !packed && !one && !rec &&
+                       tiles * (a->V / kSmallGridRowsPerWave) <= kSmallGridWaves;
     KernelFn fn;
     if (packed)
         fn = var == VAR_LA    ? pick_packed<VAR_LA>(a->K, a->V, bi, bo)
@@ -1742,9 +1766,11 @@ la_status select_kernel(const la_decode_args *a, int var, Launch &L)
         fn = var == VAR_LA ? pick_one<VAR_LA>(a->K, a->V, bi, bo, bs)
                            : pick_one<VAR_GDN>(a->K, a->V, bi, bo, bs);
     else
-        fn = var == VAR_LA    ? pick<VAR_LA>(a->K, a->V, bi, bo, bs, rec)
-             : var == VAR_GDN ? pick<VAR_GDN>(a->K, a->V, bi, bo, bs, rec)
-                              : pick<VAR_KDA>(a->K, a->V, bi, bo, bs, rec);
+        fn = var == VAR_LA
+                 ? pick<VAR_LA>(a->K, a->V, bi, bo, bs, rec, small)
+             : var == VAR_GDN
+                 ? pick<VAR_GDN>(a->K, a->V, bi, bo, bs, rec, small)
+                 : pick<VAR_KDA>(a->K, a->V, bi, bo, bs, rec, small);
     L.fn = fn;
     L.name = packed ? "decode_packed_kernel"
              : one  ? "decode1_kernel"
@@ -1755,11 +1781,13 @@ la_status select_kernel(const la_decode_args *a, int var, Launch &L)
             lds_floats_per_token(var, a->K, a->V) * sizeof(float);
     L.grid = dim3(static_cast<unsigned>(a->B) * a->HV);
     // rows per wave: 64 in the packed kernel, 8 in the one-token kernel,
-    // kRecordRowsPerWave with records, kRowsPerWave otherwise
-    L.block = dim3(packed ? a->V
-                   : one  ? (a->V / 8) * 64
-                   : rec  ? (a->V / kRecordRowsPerWave) * 64
-                          : (a->V / kRowsPerWave) * 64);
+    // kRecordRowsPerWave with records, kSmallGridRowsPerWave on small grids,
+    // kRowsPerWave otherwise
+    L.block = dim3(packed  ? a->V
+                   : one   ? (a->V / 8) * 64
+                   : rec   ? (a->V / kRecordRowsPerWave) * 64
+                   : small ? (a->V / kSmallGridRowsPerWave) * 64
+                           : (a->V / kRowsPerWave) * 64);
     return LA_OK;
 }
 

@@ -7,6 +7,7 @@ import sys
 
 import numpy as np
 import pytest
+import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
@@ -67,3 +68,43 @@ def test_range_call_equals_the_full_call(name):
         for j in changed:
             assert any(np.array_equal(got["pool"][j], full["pool"][s])
                        for s in range(pool.shape[0])), j
+
+
+SHARD_CASES = dict(CASES)
+SHARD_CASES["lightning_decays"] = lambda: W.make(
+    "c", W.LIGHTNING, B=3, T=2, H=4, HV=4, K=64, V=64, pool_size=5, seed=6,
+    lightning_decay=0.5 + 0.5 * torch.rand(4, generator=torch.Generator()
+                                           .manual_seed(7)))
+
+
+@pytest.mark.parametrize("name", sorted(SHARD_CASES))
+def test_head_shard_is_the_full_call_on_its_heads(name):
+    """bench.py --head-shards measures one GPU's share of the heads. Value
+    heads do not interact, so that share computes exactly the full call's
+    results on its heads: outputs, cached states and stored states."""
+    wl = SHARD_CASES[name]()
+    n = 2
+    if name == "lightning_in_place":  # built-in decays depend on HV
+        sh = W.head_shard(wl, n)
+        assert sh.g is None and sh.HV == wl.HV // n
+        return
+    _, _, full = _full(wl)
+    sh = W.head_shard(wl, n)
+    hv = wl.HV // n
+    assert (sh.H, sh.HV) == (wl.H // n, hv)
+    assert sh.backing.is_contiguous()
+    assert torch.equal(sh.backing, wl.backing[:, :hv])
+    _, _, got = _full(sh)
+    np.testing.assert_array_equal(got["out"], full["out"][..., :hv, :])
+    np.testing.assert_array_equal(got["pool"], full["pool"][:, :hv])
+    if wl.inter:
+        np.testing.assert_array_equal(got["inter"],
+                                      full["inter"][..., :hv, :, :])
+
+
+def test_head_shard_rejects_uneven_splits():
+    wl = CASES["dense_gdn"]()
+    with pytest.raises(ValueError):
+        W.head_shard(wl, 3)
+    with pytest.raises(ValueError):
+        W.head_shard(wl, 4)  # H = 2 cannot be split four ways

@@ -1646,6 +1646,63 @@ def test_one_token_kernel_bf16_state(variant, K, V):
     run_and_check(wl, reqs=[0, 9, 13, 30, 51, 71])
 
 
+# ------------------------------------------------ small-grid instance
+
+
+@pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN, W.KDA])
+@pytest.mark.parametrize("T,state", [(1, torch.float32), (4, torch.float32),
+                                     (4, torch.bfloat16)],
+                         ids=["t1_f32_state", "t4_f32_state", "t4_bf16_state"])
+def test_small_grid_instance_bit_identical(variant, T, state):
+    """Grids of at most 512 tiles (V = 128) run the general kernel at 16
+    rows per wave, larger ones at 32. The same requests give the same bits
+    in a call of 1280 tiles and in calls of 512 tiles; padded and
+    skipped-write requests included. (One bf16 token runs the packed kernel
+    at these sizes.)"""
+    lad = _lad()
+    B, HV = 40, 32
+    H = HV // 2 if variant == W.GDN else HV
+    seed = 8100 + 10 * T + [W.LIGHTNING, W.GDN, W.KDA].index(variant) + \
+        (5 if state != torch.float32 else 0)
+    ridx = torch.randperm(2 * B, generator=torch.Generator()
+                          .manual_seed(seed))[:B].tolist()
+    ridx[7] = -1
+    wl = W.make("small", variant, B=B, T=T, H=H, HV=HV, K=128, V=128,
+                pool_size=3 * B, seed=seed, separate_write=True,
+                write_skip=0.1, read_idx=ridx, state_dtype=state,
+                l2norm=variant != W.LIGHTNING)
+    d = wl.to(DEV)
+    kw = {}
+    if variant != W.LIGHTNING:
+        kw = dict(l2norm_qk=wl.l2norm, beta_logit=wl.beta_logit)
+
+    def call(pool, sl):
+        if variant == W.LIGHTNING:
+            return lad.la_decode(d.q[sl], d.k[sl], d.v[sl], pool,
+                                 d.read_idx[sl], d.write_idx[sl], lam=d.g)[0]
+        fn = lad.gdn_decode_mtp if variant == W.GDN else lad.kda_decode_mtp
+        return fn(d.q[sl], d.k[sl], d.v[sl], d.g[sl], d.beta[sl], pool,
+                  d.read_idx[sl], d.write_idx[sl], **kw)[0]
+
+    def threads(sl):
+        g = d.g if variant == W.LIGHTNING else d.g[sl]
+        beta = None if d.beta is None else d.beta[sl]
+        return lad.kernel_info(variant, d.q[sl], d.k[sl], d.v[sl], g, beta,
+                               d.pool(), d.read_idx[sl], d.write_idx[sl],
+                               **kw)["block_threads"]
+    assert threads(slice(0, B)) == 256 and threads(slice(0, 16)) == 512
+    whole_pool = d.backing.clone()
+    whole = call(whole_pool, slice(0, B))
+    part_pool = d.backing.clone()
+    parts = torch.cat([call(part_pool, slice(s, min(s + 16, B)))
+                       for s in range(0, B, 16)])
+    torch.cuda.synchronize()
+    assert torch.isfinite(whole.float()).all()
+    assert torch.equal(_bits(whole.cpu()), _bits(parts.cpu()))
+    assert torch.equal(_bits(whole_pool.cpu()), _bits(part_pool.cpu()))
+    run_and_check(wl, reqs=[0, 7, 20, B - 1])
+
+
 # ------------------------------------------------------------ kernel query
 
 
@@ -1653,12 +1710,15 @@ def test_one_token_kernel_bf16_state(variant, K, V):
     # (variant, B, T, HV, state dtype, expected kernel, threads)
     ("gdn", 64, 1, 32, torch.float32, "decode1_kernel", 1024),
     ("lightning", 33, 1, 64, torch.float32, "decode1_kernel", 1024),
-    ("gdn", 8, 1, 32, torch.float32, "decode_kernel", 256),
+    ("gdn", 8, 1, 32, torch.float32, "decode_kernel", 512),
     ("gdn", 64, 1, 32, torch.bfloat16, "decode_packed_kernel", 128),
     ("gdn", 72, 1, 32, torch.bfloat16, "decode1_kernel", 1024),
     ("kda", 96, 1, 24, torch.float32, "decode_kernel", 256),
     ("kda", 8, 1, 24, torch.bfloat16, "decode_packed_kernel", 128),
-    ("gdn", 16, 4, 32, torch.float32, "decode_kernel", 256),
+    ("gdn", 16, 4, 32, torch.float32, "decode_kernel", 512),
+    ("gdn", 17, 4, 32, torch.float32, "decode_kernel", 256),
+    ("kda", 21, 1, 24, torch.float32, "decode_kernel", 512),
+    ("kda", 22, 1, 24, torch.float32, "decode_kernel", 256),
     # fp32 pools: fewer than 32 value heads, or 32 heads beyond 4096 tiles,
     # take the general kernel; 48 or more heads the one-token kernel
     ("gdn", 128, 1, 16, torch.float32, "decode_kernel", 256),

@@ -277,6 +277,35 @@ def make(name, variant, B, T, H, HV, K, V, pool_size, *, seed,
         replay_tokens=replay_tokens), gen, varlen_min)
 
 
+def head_shard(wl: Workload, n: int) -> Workload:
+    """One GPU's share of ``wl`` when n GPUs split the heads: value heads
+    [0, HV/n) with their pool heads, and the q/k heads [0, H/n) that serve
+    exactly those value heads (each group of HV/H value heads stays on one
+    GPU). Requests and slots are unchanged. The pool becomes a contiguous
+    buffer of the shard's heads, as a GPU holding only its heads would
+    allocate it. A Lightning workload without explicit decays keeps none, so
+    the kernel's built-in schedule is that of HV/n heads: other values, the
+    same cost."""
+    if n < 1 or wl.HV % n or wl.H % n:
+        raise ValueError("H=%d and HV=%d must both be multiples of %d"
+                         % (wl.H, wl.HV, n))
+    h, hv = wl.H // n, wl.HV // n
+
+    def heads(t, dim, m):
+        return None if t is None else t.narrow(dim, 0, m).contiguous()
+
+    if wl.variant == GDN:
+        g = heads(wl.g, -1, hv)
+    elif wl.variant == KDA:
+        g = heads(wl.g, -2, hv)
+    else:
+        g = heads(wl.g, 0, hv)
+    return dataclasses.replace(
+        wl, name="%s_hs%d" % (wl.name, n), H=h, HV=hv,
+        q=heads(wl.q, -2, h), k=heads(wl.k, -2, h), v=heads(wl.v, -2, hv),
+        g=g, beta=heads(wl.beta, -1, hv), backing=heads(wl.backing, 1, hv))
+
+
 # The named workloads. Each is the shape, distribution and index structure of
 # one decode setting; the seed is fixed per workload.
 
