@@ -562,6 +562,86 @@ def test_side_stream():
     check_parity(wl, got, before)
 
 
+@pytest.mark.parametrize("variant,T", [(W.GDN, 1), (W.KDA, 2)],
+                         ids=["gdn_t1", "kda_t2"])
+def test_concurrent_streams_on_disjoint_slots(variant, T):
+    """Two calls on two streams, issued back to back with no synchronisation
+    between them, on disjoint halves of one batch (disjoint read and write
+    slots of one pool): the pool and outputs equal those of the single call
+    over the whole batch, bit for bit."""
+    lad = _lad()
+    B, HV = 64, 32 if variant == W.GDN else 24
+    H = HV // 2 if variant == W.GDN else HV
+    wl = W.make("streams", variant, B=B, T=T, H=H, HV=HV, K=128, V=128,
+                pool_size=3 * B, seed=9300 + T, separate_write=True)
+    d = wl.to(DEV)
+    fn = lad.gdn_decode_mtp if variant == W.GDN else lad.kda_decode_mtp
+
+    def call(pool, sl):
+        return fn(d.q[sl], d.k[sl], d.v[sl], d.g[sl], d.beta[sl], pool,
+                  d.read_idx[sl], d.write_idx[sl], l2norm_qk=wl.l2norm,
+                  beta_logit=wl.beta_logit)[0]
+    whole_pool = d.backing.clone()
+    whole = call(whole_pool, slice(0, B))
+    torch.cuda.synchronize()
+    pool = d.backing.clone()
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for s, sl in zip(streams, (slice(0, B // 2), slice(B // 2, B))):
+        with torch.cuda.stream(s):
+            outs.append(call(pool, sl))
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(torch.cat(outs).cpu()), _bits(whole.cpu()))
+    assert torch.equal(_bits(pool.cpu()), _bits(whole_pool.cpu()))
+
+
+def test_host_threads_share_the_library():
+    """The library keeps no state between calls: four host threads, each
+    with its own stream, pool and inputs, call it at the same time and get
+    the results of the same calls made one after another."""
+    import threading
+    lad = _lad()
+    wls = [W.make("thr%d" % i, W.GDN, B=16, T=2, H=8, HV=16, K=128, V=128,
+                  pool_size=32, seed=9400 + i, separate_write=True)
+           for i in range(4)]
+    devs = [wl.to(DEV) for wl in wls]
+
+    def call(d, wl, pool):
+        return lad.gdn_decode_mtp(d.q, d.k, d.v, d.g, d.beta, pool,
+                                  d.read_idx, d.write_idx,
+                                  l2norm_qk=wl.l2norm,
+                                  beta_logit=wl.beta_logit)[0]
+    serial = []
+    for d, wl in zip(devs, wls):
+        pool = d.backing.clone()
+        serial.append((call(d, wl, pool), pool))
+    torch.cuda.synchronize()
+    pools = [d.backing.clone() for d in devs]
+    torch.cuda.synchronize()
+    results = [None] * 4
+    errors = []
+
+    def work(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                results[i] = call(devs[i], wls[i], pools[i])
+            s.synchronize()
+        except Exception as e:  # reported below, on the main thread
+            errors.append(e)
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for i in range(4):
+        assert torch.equal(_bits(results[i].cpu()), _bits(serial[i][0].cpu()))
+        assert torch.equal(_bits(pools[i].cpu()), _bits(serial[i][1].cpu()))
+
+
 # ------------------------------------------------ paged per-token state slots
 
 
