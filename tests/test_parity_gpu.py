@@ -379,6 +379,42 @@ def test_packed_qkv_views_bit_identical(variant):
     assert torch.equal(packed["backing"], plain["backing"])
 
 
+PACKED_QKV_KERNELS = {
+    # name: (variant, B, T, H, HV, state dtype, kernel)
+    "one_token_gdn": (W.GDN, 64, 1, 16, 32, torch.float32, "decode1_kernel"),
+    "one_token_lightning": (W.LIGHTNING, 33, 1, 64, 64, torch.float32,
+                            "decode1_kernel"),
+    "packed_bf16_kda": (W.KDA, 8, 1, 8, 8, torch.bfloat16,
+                        "decode_packed_kernel"),
+    "general_32_rows_gdn": (W.GDN, 40, 2, 16, 32, torch.float32,
+                            "decode_kernel"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PACKED_QKV_KERNELS))
+def test_packed_qkv_views_every_kernel(name):
+    """Fused q/k/v views give the contiguous bits in each kernel, with
+    their own strides read per request, token and head."""
+    variant, B, T, H, HV, state, kernel = PACKED_QKV_KERNELS[name]
+    K = V = 128
+
+    def make():
+        return W.make("pkk", variant, B=B, T=T, H=H, HV=HV, K=K, V=V,
+                      pool_size=2 * B, seed=5100 + B + T, state_dtype=state,
+                      separate_write=True, l2norm=variant != W.LIGHTNING)
+    wl = make()
+    assert _kernel_name(wl) == kernel
+    fused = torch.cat([wl.q.reshape(B, T, H * K), wl.k.reshape(B, T, H * K),
+                       wl.v.reshape(B, T, HV * V)], dim=-1).to(DEV)
+    qv = fused[..., : H * K].unflatten(-1, (H, K))
+    kv = fused[..., H * K: 2 * H * K].unflatten(-1, (H, K))
+    vv = fused[..., 2 * H * K:].unflatten(-1, (HV, V))
+    packed = gpu_run(wl, q=qv, k=kv, v=vv)
+    plain = gpu_run(make())
+    assert torch.equal(_bits(packed["out"]), _bits(plain["out"]))
+    assert torch.equal(_bits(packed["backing"]), _bits(plain["backing"]))
+
+
 # --------------------------------------------------------- token splitting
 
 
