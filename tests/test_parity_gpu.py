@@ -1460,6 +1460,45 @@ def test_gate_chain_parity(variant, lower_bound, T, state):
 
 
 @pytest.mark.parametrize("variant", [W.GDN, W.KDA])
+@pytest.mark.parametrize("lower_bound", [None, -5.0], ids=["softplus", "lb"])
+def test_gate_chain_general_kernel_32_rows(variant, lower_bound):
+    """The gate chain in the general kernel at 32 rows per wave (a grid of
+    1280 tiles, T = 2, no update records) against the oracle."""
+    lad = _lad()
+    seed = 5200 + 10 * [W.GDN, W.KDA].index(variant) + (
+        5 if lower_bound is None else 0)
+    HV = 32
+    wl = W.make("gate32", variant, B=40, T=2, H=16 if variant == W.GDN
+                else HV, HV=HV, K=128, V=128, pool_size=96, seed=seed,
+                separate_write=True, write_skip=0.1)
+    wl.g = 2 * torch.randn(wl.g.shape, generator=torch.Generator()
+                           .manual_seed(seed + 1))
+    a_log, dt = _gate_inputs(variant, HV, wl.K, seed + 2)
+    d = wl.to(DEV)
+    fn = lad.gdn_decode_mtp if variant == W.GDN else lad.kda_decode_mtp
+    kw = dict(l2norm_qk=wl.l2norm, beta_logit=wl.beta_logit,
+              A_log=a_log.to(DEV), dt_bias=dt.to(DEV),
+              lower_bound=lower_bound)
+    info = lad.kernel_info(variant, d.q, d.k, d.v, d.g, d.beta, d.pool(),
+                           d.read_idx, d.write_idx, **kw)
+    assert info["kernel"] == "decode_kernel" and info["block_threads"] == 256
+    out, _ = fn(d.q, d.k, d.v, d.g, d.beta, d.pool(), d.read_idx,
+                d.write_idx, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.decode(VARIANT_CODE[variant], wl.q, wl.k, wl.v, wl.g,
+                        wl.beta, wl.pool(), wl.read_idx, wl.write_idx,
+                        flags=_flags(wl), A_log=a_log, dt_bias=dt,
+                        lower_bound=lower_bound)
+    kind, tol_out, tol_state = _tol(wl)
+    assert _err(kind, out.cpu().float(), ref["out"]) <= tol_out
+    backing = d.backing.cpu()
+    for b, w in enumerate(wl.write_idx.tolist()):
+        if w >= 0:
+            assert _err(kind, backing[w].float(), ref["pool"][w]) <= \
+                tol_state, b
+
+
+@pytest.mark.parametrize("variant", [W.GDN, W.KDA])
 def test_gate_chain_closed_form_on_gpu(variant):
     """x + dt_bias = 0 with A_log = 0: every decay is 1/2 (softplus(0) =
     ln 2); in the bounded form exp(lb / 2) for any A_log."""
