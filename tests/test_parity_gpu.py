@@ -2360,3 +2360,50 @@ def test_head_and_request_shards_equal_the_full_call(variant, B, HV, H):
     assert torch.equal(_bits(heads_pool), _bits(full_pool))
     assert torch.equal(_bits(torch.cat(routs, dim=0)), _bits(full))
     assert torch.equal(_bits(req_pool), _bits(full_pool))
+
+
+def _medium_combo(i):
+    """Draw i of the medium-grid sweep: a grid that runs the general kernel
+    at 32 rows per wave (more than one small-grid round of tiles, and no
+    one-token or packed kernel)."""
+    import random
+    rng = random.Random(9700 + i)
+    variant = rng.choice([W.LIGHTNING, W.GDN, W.KDA])
+    K, V = rng.choice(SHAPES)
+    HV = rng.choice([16, 24, 32])
+    H = rng.choice([h for h in (HV // 2, HV) if HV % h == 0])
+    state = rng.choice([torch.float32, torch.bfloat16])
+    T = rng.choice([1, 2, 3, 4]) if state == torch.float32 else \
+        rng.choice([2, 3, 4])
+    lo = 4096 * 16 // V + 1   # first grid beyond the small-grid instance
+    B = rng.randint(-(-lo // HV), 2047 // HV)
+    return dict(variant=variant, B=B, T=T, H=H, HV=HV, K=K, V=V,
+                pool_size=2 * B + 3, state_dtype=state,
+                act_dtype=rng.choice([torch.float32, torch.bfloat16]),
+                out_dtype=rng.choice([torch.float32, torch.bfloat16]),
+                stride_mult=rng.choice([1, 2]),
+                separate_write=rng.random() < 0.5, write_skip=0.1,
+                inter=rng.random() < 0.4,
+                l2norm=variant != W.LIGHTNING and rng.random() < 0.8)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_medium_grids_general_kernel(i):
+    """12 fixed draws of medium grids (the 32-row general kernel): variant,
+    tile shape, head count, dtypes, strided pools, separate and skipped
+    writes, the per-token cache and a padded request; sampled requests
+    against the oracle, every untouched byte of the pool checked."""
+    cfg = _medium_combo(i)
+    variant = cfg.pop("variant")
+    wl = W.make("medium%d" % i, variant, seed=9800 + i, **cfg)
+    wl.read_idx[wl.B // 3] = -1
+    assert _kernel_name(wl) == "decode_kernel"
+    lad = _lad()
+    d = wl.to(DEV)
+    kw = {}
+    if variant != W.LIGHTNING:
+        kw = dict(l2norm_qk=wl.l2norm, beta_logit=wl.beta_logit)
+    info = lad.kernel_info(variant, d.q, d.k, d.v, d.g, d.beta, d.pool(),
+                           d.read_idx, d.write_idx, **kw)
+    assert info["block_threads"] == (wl.V // 32) * 64, info
+    run_and_check(wl, reqs=sorted({0, wl.B // 3, wl.B // 2, wl.B - 1}))
