@@ -80,9 +80,12 @@ constexpr int kRecordRowsPerWave = 16;
 // with the cache 62.5 -> 60.9). At 768 tiles two rounds are needed and 16
 // rows lose (GDN B=24 HV=32: 72.5 -> 62.7).
 constexpr int kSmallGridRowsPerWave = 16;
-// Calls with fewer value heads than this take their pairs in XCD-chunked
-// order (xcd_pair); see select_kernel for the measurements.
-constexpr int kXcdOrderMaxHeads = 48;
+// Pairs per XCD block (xcd_block_pair): calls with fewer value heads than
+// kXcdRangeMaxHeads give each XCD one contiguous range of pairs, i.e. whole
+// requests; the others deal blocks of kXcdBlockPairs pairs. See
+// xcd_block_for for the measurements.
+constexpr int kXcdRangeMaxHeads = 48;
+constexpr int kXcdBlockPairs = 32;
 constexpr int64_t kSmallGridWaves = 4096;
 static_assert(kRowsPerWave == 8 || kRowsPerWave == 16 || kRowsPerWave == 32,
               "8, 16 or 32 rows");
@@ -122,26 +125,31 @@ struct Params {
     const float *A_log;    // [HV]
     const float *dt_bias;  // [HV] (GDN) or [HV, K] (KDA)
     float lower_bound;
-    int32_t xcd_order;  // 1: workgroups take pairs in XCD-chunked order
+    int32_t xcd_block;  // pairs per block dealt to the XCDs (pair_of_block)
 };
 
 // ---------------------------------------------------------------- helpers
 
 // The dispatcher hands workgroup i to XCD i % 8 (eight XCDs, round robin).
-// In XCD-chunked order workgroup i takes pair xcd_pair(i, n), so that XCD x
-// works through the contiguous pairs [x n / 8, (x + 1) n / 8) (the first
-// n % 8 XCDs one more), i.e. through whole requests, instead of every
-// eighth pair of every request. A permutation of [0, n) for any n.
-__device__ __forceinline__ int xcd_pair(int i, int n)
+// Workgroups take their (request, value head) pairs in blocks of C
+// consecutive pairs dealt round robin to the XCDs: XCD x gets blocks x,
+// x + 8, ... C = 1 is the plain order (each XCD takes every eighth pair);
+// C = n / 8 gives each XCD one contiguous range. Workgroups beyond the last
+// whole round of 8 C keep the plain order, so the map is a permutation of
+// [0, n) for every n and C >= 1.
+__device__ __forceinline__ int xcd_block_pair(int i, int n, int C)
 {
-    const int per = n >> 3, rem = n & 7, x = i & 7, j = i >> 3;
-    return x * per + min(x, rem) + j;
+    const int nfull = (n / (8 * C)) * (8 * C);
+    if (i >= nfull)
+        return i;
+    const int x = i & 7, g = i >> 3;
+    return ((g / C) * 8 + x) * C + (g % C);
 }
 
-__device__ __forceinline__ int pair_of_block(int xcd_order)
+__device__ __forceinline__ int pair_of_block(int xcd_block)
 {
-    const int i = blockIdx.x;
-    return xcd_order ? xcd_pair(i, gridDim.x) : i;
+    return xcd_block > 1 ? xcd_block_pair(blockIdx.x, gridDim.x, xcd_block)
+                         : static_cast<int>(blockIdx.x);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h)
@@ -591,7 +599,7 @@ decode_kernel(const Params p)
     constexpr int CPL = K / 32;            // 16-byte chunks per lane and row
     constexpr int TPW = (kTokChunk + NW - 1) / NW;  // prologue tokens per wave
 
-    const int pair = pair_of_block(p.xcd_order);
+    const int pair = pair_of_block(p.xcd_block);
     const int b = pair / p.HV;
     const int hv = pair - b * p.HV;
     const int lane = threadIdx.x & 63;
@@ -819,7 +827,7 @@ __global__ void __launch_bounds__(V) decode_packed_kernel(const Params p)
     extern __shared__ f4 lds_raw[];
     float *lds = reinterpret_cast<float *>(lds_raw);
 
-    const int pair = pair_of_block(p.xcd_order);
+    const int pair = pair_of_block(p.xcd_block);
     const int b = pair / p.HV;
     const int hv = pair - b * p.HV;
     const int lane = threadIdx.x & 63;
@@ -975,7 +983,7 @@ __global__ void __launch_bounds__((V / 8) * 64) decode1_kernel(const Params p)
     constexpr int RPI = 64 / LPR;   // rows per load instruction
     constexpr int RPL = 8 / RPI;    // rows per lane
 
-    const int pair = pair_of_block(p.xcd_order);
+    const int pair = pair_of_block(p.xcd_block);
     const int b = pair / p.HV;
     const int hv = pair - b * p.HV;
     const int lane = threadIdx.x & 63;
@@ -1162,7 +1170,7 @@ __global__ void __launch_bounds__((V / 8) * 64) decode1_kernel(const Params p)
 
 struct ReplayParams {
     int32_t B, T, HV;
-    int32_t xcd_order;
+    int32_t xcd_block;
     const float *factors;
     void *pool;
     int64_t sp_slot, sp_head, sp_row;
@@ -1189,7 +1197,7 @@ replay_kernel(const ReplayParams p)
     __shared__ f4 recs[kTokChunk * RS / 4];
     const float *lrec = reinterpret_cast<const float *>(recs);
 
-    const int pair = pair_of_block(p.xcd_order);
+    const int pair = pair_of_block(p.xcd_block);
     const int b = pair / p.HV;
     const int hv = pair - b * p.HV;
     const int lane = threadIdx.x & 63;
@@ -1668,6 +1676,28 @@ la_status validate(const la_decode_args *a, int var)
     return LA_OK;
 }
 
+// Pairs per XCD block for a grid of B * HV pairs. Below 48 value heads one
+// contiguous range per XCD (whole requests on one XCD); from 48 heads blocks
+// of 32 pairs. Measured on MI355X against the plain order (each XCD takes
+// every eighth pair), % of peak HBM bandwidth:
+//   ranges, < 48 heads: KDA B=256 H=24 70.7 -> 72.3; GDN B=256 HV=32
+//   71.3 -> 73.2; GDN B=32 T=4 with the cache 65.9 -> 67.4; paged GDN B=64
+//   T=4 65.1 -> 67.2; one-token GDN B=64 HV=32 69.1 -> 70.3 (four slot
+//   draws: +0.3 to +1.9); bf16 one-token GDN HV=16..32 +2.3 to +2.7.
+//   Ranges at 64 heads lose (GDN HV=64 T=2 73.2 -> 69.3; one-token
+//   Lightning H=64 74.6 -> 68.8).
+//   32-pair blocks, >= 48 heads: Lightning B=33 H=64 74.0 -> 75.1; GDN
+//   HV=48 71.8 -> 72.7, HV=96 74.6 -> 76.1; Lightning K=V=64 H=64 71.1 ->
+//   74.2; GDN HV=64 T=2 and Lightning H=64 B=64 unchanged.
+// The packed kernel keeps the plain order (13 bf16 shapes: -2.5 to +2.7).
+int xcd_block_for(int B, int HV)
+{
+    const int64_t n = static_cast<int64_t>(B) * HV;
+    if (HV >= kXcdRangeMaxHeads)
+        return kXcdBlockPairs;
+    return n >= 16 ? static_cast<int>(n / 8) : 1;
+}
+
 // The kernel, launch shape and parameters of a decode call. fn is null
 // when there is nothing to launch (B = 0).
 struct Launch {
@@ -1792,18 +1822,7 @@ la_status select_kernel(const la_decode_args *a, int var, Launch &L)
              : var == VAR_GDN
                  ? pick<VAR_GDN>(a->K, a->V, bi, bo, bs, rec, small)
                  : pick<VAR_KDA>(a->K, a->V, bi, bo, bs, rec, small);
-    // Order of the pairs over the workgroups. XCD-chunked order (each XCD
-    // works through whole requests) measured faster below 48 value heads,
-    // in the general kernel at every such shape tried and in the one-token
-    // kernel (which runs at 32 heads or more there); from 48 heads the
-    // plain order (each XCD takes every eighth head of every request) was
-    // faster. The packed kernel keeps the plain order (mixed results). On
-    // MI355X, % of peak HBM bandwidth, plain -> XCD-chunked: KDA B=256
-    // H=24 70.7 -> 72.3; GDN B=256 HV=32 71.3 -> 73.2; GDN B=32 T=4 with the
-    // cache 65.9 -> 67.4; paged GDN B=64 T=4 65.1 -> 67.2; one-token GDN
-    // B=64 HV=32 69.1 -> 70.3 (four slot draws: +0.3 to +1.9); but GDN
-    // HV=64 T=2 73.2 -> 69.3, one-token Lightning H=64 74.6 -> 68.8.
-    p.xcd_order = !packed && a->HV < kXcdOrderMaxHeads;
+    p.xcd_block = packed ? 1 : xcd_block_for(a->B, a->HV);
     L.fn = fn;
     L.name = packed ? "decode_packed_kernel"
              : one  ? "decode1_kernel"
@@ -1939,7 +1958,7 @@ la_status la_replay(const la_replay_args *a, void *stream)
     p.B = a->B;
     p.T = a->T;
     p.HV = a->HV;
-    p.xcd_order = a->HV < kXcdOrderMaxHeads;  // as the decode kernels
+    p.xcd_block = xcd_block_for(a->B, a->HV);  // as the decode kernels
     p.factors = a->factors;
     p.pool = a->pool;
     p.sp_slot = a->sp.slot;
