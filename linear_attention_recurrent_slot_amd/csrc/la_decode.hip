@@ -85,6 +85,12 @@ constexpr int kSmallGridRowsPerWave = 16;
 // requests; the others deal blocks of kXcdBlockPairs pairs. See
 // xcd_block_for for the measurements.
 constexpr int kXcdRangeMaxHeads = 48;
+// Largest grid of the packed one-token bf16 kernel. Beyond it the general
+// kernel (in XCD ranges) is faster for KDA, B * 24 tiles, % of peak HBM
+// bandwidth, packed -> general: 2304 60.3 -> 59.9, 3072 62.5 -> 62.4,
+// 3840 62.8 -> 64.7, 4608 63.0 -> 65.5, 6144 62.8 -> 67.7, 9216 63.7 ->
+// 69.3.
+constexpr int64_t kPackedMaxTiles = 3072;
 constexpr int kXcdBlockPairs = 32;
 constexpr int64_t kSmallGridWaves = 4096;
 static_assert(kRowsPerWave == 8 || kRowsPerWave == 16 || kRowsPerWave == 32,
@@ -1802,9 +1808,11 @@ la_status select_kernel(const la_decode_args *a, int var, Launch &L)
                      !a->token_slots && !rec && !a->cu_seqlens &&
                      (bs ? tiles > 2048 : wide);
     // otherwise one token on a bf16 pool with no per-token writes: the
-    // packed tile
+    // packed tile, up to kPackedMaxTiles (KDA only reaches beyond: the
+    // other variants take the one-token kernel there)
     const bool packed = !one && bs && a->T == 1 && !a->inter &&
-                        !a->token_slots && !rec && !a->cu_seqlens;
+                        !a->token_slots && !rec && !a->cu_seqlens &&
+                        tiles <= kPackedMaxTiles;
     // a grid of the general kernel that fills less than one resident round
     const bool small = !packed && !one && !rec &&
                        tiles * (a->V / kSmallGridRowsPerWave) <= kSmallGridWaves;

@@ -1887,6 +1887,8 @@ def test_small_grid_instance_bit_identical(variant, T, state):
     ("gdn", 72, 1, 32, torch.bfloat16, "decode1_kernel", 1024),
     ("kda", 96, 1, 24, torch.float32, "decode_kernel", 256),
     ("kda", 8, 1, 24, torch.bfloat16, "decode_packed_kernel", 128),
+    ("kda", 128, 1, 24, torch.bfloat16, "decode_packed_kernel", 128),
+    ("kda", 129, 1, 24, torch.bfloat16, "decode_kernel", 256),
     ("gdn", 16, 4, 32, torch.float32, "decode_kernel", 512),
     ("gdn", 17, 4, 32, torch.float32, "decode_kernel", 256),
     ("kda", 21, 1, 24, torch.float32, "decode_kernel", 512),
