@@ -80,19 +80,19 @@ constexpr int kRecordRowsPerWave = 16;
 // with the cache 62.5 -> 60.9). At 768 tiles two rounds are needed and 16
 // rows lose (GDN B=24 HV=32: 72.5 -> 62.7).
 constexpr int kSmallGridRowsPerWave = 16;
+constexpr int64_t kSmallGridWaves = 4096;
 // Pairs per XCD block (xcd_block_pair): calls with fewer value heads than
 // kXcdRangeMaxHeads give each XCD one contiguous range of pairs, i.e. whole
 // requests; the others deal blocks of kXcdBlockPairs pairs. See
 // xcd_block_for for the measurements.
 constexpr int kXcdRangeMaxHeads = 48;
+constexpr int kXcdBlockPairs = 32;
 // Largest grid of the packed one-token bf16 kernel. Beyond it the general
 // kernel (in XCD ranges) is faster for KDA, B * 24 tiles, % of peak HBM
 // bandwidth, packed -> general: 2304 60.3 -> 59.9, 3072 62.5 -> 62.4,
 // 3840 62.8 -> 64.7, 4608 63.0 -> 65.5, 6144 62.8 -> 67.7, 9216 63.7 ->
 // 69.3.
 constexpr int64_t kPackedMaxTiles = 3072;
-constexpr int kXcdBlockPairs = 32;
-constexpr int64_t kSmallGridWaves = 4096;
 static_assert(kRowsPerWave == 8 || kRowsPerWave == 16 || kRowsPerWave == 32,
               "8, 16 or 32 rows");
 constexpr int kTokChunk = 8;
