@@ -1695,7 +1695,10 @@ la_status validate(const la_decode_args *a, int var)
 //   32-pair blocks, >= 48 heads: Lightning B=33 H=64 74.0 -> 75.1; GDN
 //   HV=48 71.8 -> 72.7, HV=96 74.6 -> 76.1; Lightning K=V=64 H=64 71.1 ->
 //   74.2; GDN HV=64 T=2 and Lightning H=64 B=64 unchanged.
-// The packed kernel keeps the plain order (13 bf16 shapes: -2.5 to +2.7).
+// The packed kernel keeps the plain order (13 bf16 shapes: -2.5 to +2.7),
+// and so does the small-grid instance, where ranges lost up to 4.5 points
+// (GDN B=32 HV=16 T=4 with the cache, 512 tiles: 66.6 -> 62.1; GDN B=64
+// HV=8: 66.7 -> 64.8).
 int xcd_block_for(int B, int HV)
 {
     const int64_t n = static_cast<int64_t>(B) * HV;
@@ -1830,7 +1833,8 @@ la_status select_kernel(const la_decode_args *a, int var, Launch &L)
              : var == VAR_GDN
                  ? pick<VAR_GDN>(a->K, a->V, bi, bo, bs, rec, small)
                  : pick<VAR_KDA>(a->K, a->V, bi, bo, bs, rec, small);
-    p.xcd_block = packed ? 1 : xcd_block_for(a->B, a->HV);
+    // the packed kernel and the small-grid instance keep the plain order
+    p.xcd_block = packed || small ? 1 : xcd_block_for(a->B, a->HV);
     L.fn = fn;
     L.name = packed ? "decode_packed_kernel"
              : one  ? "decode1_kernel"
