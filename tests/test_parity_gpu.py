@@ -1801,12 +1801,15 @@ def test_one_token_kernel_bf16_state(variant, K, V):
     run_and_check(wl, reqs=[0, 9, 13, 30, 51, 71])
 
 
-@pytest.mark.parametrize("variant,B,H,HV,K", [
-    (W.GDN, 67, 5, 25, 64),         # one range per XCD, 3 pairs past them
-    (W.LIGHTNING, 33, 48, 48, 128),  # 32-pair blocks, 48 pairs past them
-    (W.KDA, 9, 7, 7, 64),           # 63 pairs: ranges of 7, 7 past them
-], ids=["ranges_gdn", "blocks_lightning", "ranges_kda"])
-def test_xcd_block_order_covers_every_pair(variant, B, H, HV, K):
+@pytest.mark.parametrize("variant,B,H,HV,K,kernel", [
+    # one range per XCD, 3 pairs past them
+    (W.GDN, 67, 5, 25, 64, "decode_kernel"),
+    # 32-pair blocks, 48 pairs past them
+    (W.LIGHTNING, 33, 48, 48, 128, "decode_kernel"),
+    # 2079 pairs in the one-token kernel: ranges of 259, 7 past them
+    (W.GDN, 63, 11, 33, 128, "decode1_kernel"),
+], ids=["ranges_gdn", "blocks_lightning", "ranges_one_token"])
+def test_xcd_block_order_covers_every_pair(variant, B, H, HV, K, kernel):
     """Workgroups take their pairs in XCD blocks (whole ranges below 48
     value heads, 32-pair blocks from 48) with the pairs past the last whole
     round in plain order: every request's outputs and stored state match the
@@ -1814,7 +1817,7 @@ def test_xcd_block_order_covers_every_pair(variant, B, H, HV, K):
     wl = W.make("xcd", variant, B=B, T=1, H=H, HV=HV, K=K, V=K,
                 pool_size=2 * B + 1, seed=9900 + B, separate_write=True,
                 act_dtype=torch.float32, l2norm=variant != W.LIGHTNING)
-    assert _kernel_name(wl) == "decode_kernel"
+    assert _kernel_name(wl) == kernel
     run_and_check(wl)
 
 
