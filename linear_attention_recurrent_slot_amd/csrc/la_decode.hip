@@ -96,6 +96,18 @@ constexpr int64_t kPackedMaxTiles = 3072;
 static_assert(kRowsPerWave == 8 || kRowsPerWave == 16 || kRowsPerWave == 32,
               "8, 16 or 32 rows");
 constexpr int kTokChunk = 8;
+// Tokens per LDS round of 32-row grids that write a state per token (cache or
+// paged slots). Why two tokens per round beat eight there is not
+// established: an extra barrier every two tokens alone did not reproduce
+// the gain, so it is the interleaving of the later tokens' prologue with
+// the state writes rather than the synchronisation. Measured on MI355X,
+// % of peak HBM bandwidth, 8 -> 2 tokens per round: GDN B=32 HV=32 T=4 with the cache 66.9 -> 70.6; paged GDN B=64
+// T=4 67.2 -> 69.9; Lightning B=16 H=64 T=4 with the cache 68.5 -> 71.6;
+// GDN B=32 T=8 with the cache 71.3 -> 73.0; KDA B=64 T=4 with the cache
+// 67.4 -> 68.4. Varlen batches (T_b ~ U{1..4}) lost 0.4-0.6 points and keep
+// eight; without per-token writes fewer tokens per round lose (update
+// records: KDA B=64 T=4 verify + replay 67.9 -> 62.3).
+constexpr int kCacheTokChunk = 2;
 constexpr float kL2Eps = 1e-6f;
 
 // Activation strides are 32-bit: the host checks that every element offset
@@ -591,7 +603,7 @@ __device__ __forceinline__ bool request_tokens(const int32_t *cu, int32_t total,
 // per wave (the workgroup has V / R waves); it only distributes rows over
 // waves, each row's arithmetic is the same for every R.
 template <int VAR, int K, int V, bool BF16IN, bool BF16OUT, bool BF16S,
-          bool REC, int R>
+          bool REC, int R, int CH>
 __global__ void __launch_bounds__((V / R) * 64) LA_OCCUPANCY
 decode_kernel(const Params p)
 {
@@ -603,7 +615,6 @@ decode_kernel(const Params p)
     constexpr int NW = V / R;  // waves per workgroup
     constexpr int RPL = R / 8;  // rows per lane
     constexpr int CPL = K / 32;            // 16-byte chunks per lane and row
-    constexpr int TPW = (kTokChunk + NW - 1) / NW;  // prologue tokens per wave
 
     const int pair = pair_of_block(p.xcd_block);
     const int b = pair / p.HV;
@@ -662,8 +673,8 @@ decode_kernel(const Params p)
         IO::template load_row<REC ? kRecordLoadPolicy : kStreamPolicy>(
             S[i], src, lane_off, (wave * R + i * 8) * row_bytes);
 
-    for (int t0 = 0; t0 < Tb; t0 += kTokChunk) {
-        const int nt = min(kTokChunk, Tb - t0);
+    for (int t0 = 0; t0 < Tb; t0 += CH) {
+        const int nt = min(CH, Tb - t0);
         if (t0 > 0)
             lds_barrier();  // every wave is done with the previous chunk
         for (int tt = wave; tt < nt; tt += NW) {
@@ -1399,32 +1410,39 @@ check_cu_seqlens_kernel(int32_t B, int32_t T, int32_t total,
 
 typedef void (*KernelFn)(const Params);
 
-template <int VAR, int K, int V, bool BF16S, bool REC, int R>
+template <int VAR, int K, int V, bool BF16S, bool REC, int R, int CH>
 KernelFn pick_io(bool bf16_in, bool bf16_out)
 {
     if (bf16_in)
-        return bf16_out ? decode_kernel<VAR, K, V, true, true, BF16S, REC, R>
-                        : decode_kernel<VAR, K, V, true, false, BF16S, REC, R>;
-    return bf16_out ? decode_kernel<VAR, K, V, false, true, BF16S, REC, R>
-                    : decode_kernel<VAR, K, V, false, false, BF16S, REC, R>;
+        return bf16_out
+                   ? decode_kernel<VAR, K, V, true, true, BF16S, REC, R, CH>
+                   : decode_kernel<VAR, K, V, true, false, BF16S, REC, R, CH>;
+    return bf16_out
+               ? decode_kernel<VAR, K, V, false, true, BF16S, REC, R, CH>
+               : decode_kernel<VAR, K, V, false, false, BF16S, REC, R, CH>;
 }
 
 template <int VAR, int K, int V>
 KernelFn pick_dtype(bool bf16_in, bool bf16_out, bool bf16_state, bool rec,
-                    bool small)
+                    bool small, bool cache)
 {
     constexpr int RR = kRecordRowsPerWave, RS = kSmallGridRowsPerWave;
     constexpr int RP = kRowsPerWave;
+    constexpr int C8 = kTokChunk, C2 = kCacheTokChunk;
+    const bool bi = bf16_in, bo = bf16_out;
     if (rec)
-        return bf16_state
-                   ? pick_io<VAR, K, V, true, true, RR>(bf16_in, bf16_out)
-                   : pick_io<VAR, K, V, false, true, RR>(bf16_in, bf16_out);
+        return bf16_state ? pick_io<VAR, K, V, true, true, RR, C8>(bi, bo)
+                          : pick_io<VAR, K, V, false, true, RR, C8>(bi, bo);
     if (small)
-        return bf16_state
-                   ? pick_io<VAR, K, V, true, false, RS>(bf16_in, bf16_out)
-                   : pick_io<VAR, K, V, false, false, RS>(bf16_in, bf16_out);
-    return bf16_state ? pick_io<VAR, K, V, true, false, RP>(bf16_in, bf16_out)
-                      : pick_io<VAR, K, V, false, false, RP>(bf16_in, bf16_out);
+        return bf16_state ? pick_io<VAR, K, V, true, false, RS, C8>(bi, bo)
+                          : pick_io<VAR, K, V, false, false, RS, C8>(bi, bo);
+    if constexpr (V == 128)
+        if (cache)
+            return bf16_state
+                       ? pick_io<VAR, K, V, true, false, RP, C2>(bi, bo)
+                       : pick_io<VAR, K, V, false, false, RP, C2>(bi, bo);
+    return bf16_state ? pick_io<VAR, K, V, true, false, RP, C8>(bi, bo)
+                      : pick_io<VAR, K, V, false, false, RP, C8>(bi, bo);
 }
 
 template <int VAR, int K, int V>
@@ -1475,13 +1493,15 @@ KernelFn pick_one(int K, int V, bool bi, bool bo, bool bs)
 }
 
 template <int VAR>
-KernelFn pick(int K, int V, bool bi, bool bo, bool bs, bool rec, bool small)
+KernelFn pick(int K, int V, bool bi, bool bo, bool bs, bool rec, bool small,
+              bool cache)
 {
     if (K == 128)
-        return V == 128 ? pick_dtype<VAR, 128, 128>(bi, bo, bs, rec, small)
-                        : pick_dtype<VAR, 128, 64>(bi, bo, bs, rec, small);
-    return V == 128 ? pick_dtype<VAR, 64, 128>(bi, bo, bs, rec, small)
-                    : pick_dtype<VAR, 64, 64>(bi, bo, bs, rec, small);
+        return V == 128
+                   ? pick_dtype<VAR, 128, 128>(bi, bo, bs, rec, small, cache)
+                   : pick_dtype<VAR, 128, 64>(bi, bo, bs, rec, small, cache);
+    return V == 128 ? pick_dtype<VAR, 64, 128>(bi, bo, bs, rec, small, cache)
+                    : pick_dtype<VAR, 64, 64>(bi, bo, bs, rec, small, cache);
 }
 
 int lds_floats_per_token(int var, int K, int V)
@@ -1819,6 +1839,11 @@ la_status select_kernel(const la_decode_args *a, int var, Launch &L)
     // a grid of the general kernel that fills less than one resident round
     const bool small = !packed && !one && !rec &&
                        tiles * (a->V / kSmallGridRowsPerWave) <= kSmallGridWaves;
+    // other grids that write a state per token stage kCacheTokChunk tokens
+    // per LDS round (at V = 128: at V = 64 the KDA instance would need 129
+    // VGPRs, one wave per SIMD less)
+    const bool cache = !packed && !one && !rec && !small && a->V == 128 &&
+                       !a->cu_seqlens && (a->inter || a->token_slots);
     KernelFn fn;
     if (packed)
         fn = var == VAR_LA    ? pick_packed<VAR_LA>(a->K, a->V, bi, bo)
@@ -1829,10 +1854,10 @@ la_status select_kernel(const la_decode_args *a, int var, Launch &L)
                            : pick_one<VAR_GDN>(a->K, a->V, bi, bo, bs);
     else
         fn = var == VAR_LA
-                 ? pick<VAR_LA>(a->K, a->V, bi, bo, bs, rec, small)
+                 ? pick<VAR_LA>(a->K, a->V, bi, bo, bs, rec, small, cache)
              : var == VAR_GDN
-                 ? pick<VAR_GDN>(a->K, a->V, bi, bo, bs, rec, small)
-                 : pick<VAR_KDA>(a->K, a->V, bi, bo, bs, rec, small);
+                 ? pick<VAR_GDN>(a->K, a->V, bi, bo, bs, rec, small, cache)
+                 : pick<VAR_KDA>(a->K, a->V, bi, bo, bs, rec, small, cache);
     // the packed kernel and the small-grid instance keep the plain order
     p.xcd_block = packed || small ? 1 : xcd_block_for(a->B, a->HV);
     L.fn = fn;
@@ -1840,7 +1865,8 @@ la_status select_kernel(const la_decode_args *a, int var, Launch &L)
              : one  ? "decode1_kernel"
                     : "decode_kernel";
     // the one-token kernel stages nothing in LDS
-    const int chunk = one ? 0 : a->T < kTokChunk ? a->T : kTokChunk;
+    const int ch = cache ? kCacheTokChunk : kTokChunk;  // the instance's CH
+    const int chunk = one ? 0 : a->T < ch ? a->T : ch;
     L.lds = static_cast<size_t>(chunk) *
             lds_floats_per_token(var, a->K, a->V) * sizeof(float);
     L.grid = dim3(static_cast<unsigned>(a->B) * a->HV);
