@@ -113,6 +113,11 @@ constexpr int kTokChunk = 8;
 // eight; without per-token writes fewer tokens per round lose (update
 // records: KDA B=64 T=4 verify + replay 67.9 -> 62.3).
 constexpr int kCacheTokChunk = 2;
+// Tokens per LDS round of 32-row KDA grids with more than four tokens and no
+// per-token state writes. Measured on MI355X, KDA B=256 H=24 T=8, % of peak
+// HBM bandwidth, 8 -> 4 tokens per round: 65.1 -> 66.9 and 65.4 -> 67.2 in
+// two runs; GDN B=64 HV=32 T=8 lost 2.8 points the same way and keeps 8.
+constexpr int kKdaTokChunk = 4;
 constexpr float kL2Eps = 1e-6f;
 
 // Activation strides are 32-bit: the host checks that every element offset
@@ -1429,11 +1434,11 @@ KernelFn pick_io(bool bf16_in, bool bf16_out)
 
 template <int VAR, int K, int V>
 KernelFn pick_dtype(bool bf16_in, bool bf16_out, bool bf16_state, bool rec,
-                    bool small, bool cache)
+                    bool small, int ch)
 {
     constexpr int RR = kRecordRowsPerWave, RS = kSmallGridRowsPerWave;
     constexpr int RP = kRowsPerWave;
-    constexpr int C8 = kTokChunk, C2 = kCacheTokChunk;
+    constexpr int C8 = kTokChunk, C4 = kKdaTokChunk, C2 = kCacheTokChunk;
     const bool bi = bf16_in, bo = bf16_out;
     if (rec)
         return bf16_state ? pick_io<VAR, K, V, true, true, RR, C8>(bi, bo)
@@ -1442,10 +1447,15 @@ KernelFn pick_dtype(bool bf16_in, bool bf16_out, bool bf16_state, bool rec,
         return bf16_state ? pick_io<VAR, K, V, true, false, RS, C8>(bi, bo)
                           : pick_io<VAR, K, V, false, false, RS, C8>(bi, bo);
     if constexpr (V == 128)
-        if (cache)
+        if (ch == C2)
             return bf16_state
                        ? pick_io<VAR, K, V, true, false, RP, C2>(bi, bo)
                        : pick_io<VAR, K, V, false, false, RP, C2>(bi, bo);
+    if constexpr (VAR == VAR_KDA)
+        if (ch == C4)
+            return bf16_state
+                       ? pick_io<VAR, K, V, true, false, RP, C4>(bi, bo)
+                       : pick_io<VAR, K, V, false, false, RP, C4>(bi, bo);
     return bf16_state ? pick_io<VAR, K, V, true, false, RP, C8>(bi, bo)
                       : pick_io<VAR, K, V, false, false, RP, C8>(bi, bo);
 }
@@ -1499,14 +1509,14 @@ KernelFn pick_one(int K, int V, bool bi, bool bo, bool bs)
 
 template <int VAR>
 KernelFn pick(int K, int V, bool bi, bool bo, bool bs, bool rec, bool small,
-              bool cache)
+              int ch)
 {
     if (K == 128)
         return V == 128
-                   ? pick_dtype<VAR, 128, 128>(bi, bo, bs, rec, small, cache)
-                   : pick_dtype<VAR, 128, 64>(bi, bo, bs, rec, small, cache);
-    return V == 128 ? pick_dtype<VAR, 64, 128>(bi, bo, bs, rec, small, cache)
-                    : pick_dtype<VAR, 64, 64>(bi, bo, bs, rec, small, cache);
+                   ? pick_dtype<VAR, 128, 128>(bi, bo, bs, rec, small, ch)
+                   : pick_dtype<VAR, 128, 64>(bi, bo, bs, rec, small, ch);
+    return V == 128 ? pick_dtype<VAR, 64, 128>(bi, bo, bs, rec, small, ch)
+                    : pick_dtype<VAR, 64, 64>(bi, bo, bs, rec, small, ch);
 }
 
 int lds_floats_per_token(int var, int K, int V)
@@ -1849,6 +1859,14 @@ la_status select_kernel(const la_decode_args *a, int var, Launch &L)
     // VGPRs, one wave per SIMD less)
     const bool cache = !packed && !one && !rec && !small && a->V == 128 &&
                        !a->cu_seqlens && (a->inter || a->token_slots);
+    // tokens per LDS round: the CH of the general-kernel instance picked
+    // below, which the LDS allocation must match
+    const bool kda_mid = var == VAR_KDA && !packed && !one && !rec &&
+                         !small && !cache && !a->inter && !a->token_slots &&
+                         a->T > kKdaTokChunk;
+    const int ch = cache ? kCacheTokChunk
+                   : kda_mid ? kKdaTokChunk
+                             : kTokChunk;
     KernelFn fn;
     if (packed)
         fn = var == VAR_LA    ? pick_packed<VAR_LA>(a->K, a->V, bi, bo)
@@ -1859,10 +1877,10 @@ la_status select_kernel(const la_decode_args *a, int var, Launch &L)
                            : pick_one<VAR_GDN>(a->K, a->V, bi, bo, bs);
     else
         fn = var == VAR_LA
-                 ? pick<VAR_LA>(a->K, a->V, bi, bo, bs, rec, small, cache)
+                 ? pick<VAR_LA>(a->K, a->V, bi, bo, bs, rec, small, ch)
              : var == VAR_GDN
-                 ? pick<VAR_GDN>(a->K, a->V, bi, bo, bs, rec, small, cache)
-                 : pick<VAR_KDA>(a->K, a->V, bi, bo, bs, rec, small, cache);
+                 ? pick<VAR_GDN>(a->K, a->V, bi, bo, bs, rec, small, ch)
+                 : pick<VAR_KDA>(a->K, a->V, bi, bo, bs, rec, small, ch);
     // the packed kernel and the small-grid instance keep the plain order
     p.xcd_block = packed || small ? 1 : xcd_block_for(a->B, a->HV);
     L.fn = fn;
@@ -1870,7 +1888,6 @@ la_status select_kernel(const la_decode_args *a, int var, Launch &L)
              : one  ? "decode1_kernel"
                     : "decode_kernel";
     // the one-token kernel stages nothing in LDS
-    const int ch = cache ? kCacheTokChunk : kTokChunk;  // the instance's CH
     const int chunk = one ? 0 : a->T < ch ? a->T : ch;
     L.lds = static_cast<size_t>(chunk) *
             lds_floats_per_token(var, a->K, a->V) * sizeof(float);
