@@ -29,8 +29,8 @@
 //    all 8 lanes, so the rank-1 update needs no broadcast.
 //  - The per-token prologue (l2norm of q and k, beta sigmoid, exp of the
 //    gate, the k.q product, v) is computed once per workgroup for up to 8
-//    tokens at a time (2 when each token's state is written), one token per
-//    wave, and staged in LDS.
+//    tokens at a time (2 when each token's state is written, 4 for KDA
+//    calls of more than 4 tokens), one token per wave, and staged in LDS.
 //  - Instances: 32 rows per wave; 16 on grids that fill less than one
 //    resident round and with update records.
 //  - Workgroups take their pairs in XCD blocks (xcd_block_pair): whole
