@@ -32,7 +32,7 @@ METRIC = ("decode tokens/sec and achieved HBM GB/s (% of peak), K=V=128 fp32 "
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
 ROTATE_BYTES = 4 << 30  # bytes the rotated copies span (16 x the MALL)
 ROTATE_MAX = 512
-DEFAULT_WORKLOAD = "lightning_b33_h64"
+DEFAULT_WORKLOAD = "kda_b256_t8"
 KERNEL_SRC = os.path.join(ROOT, "linear_attention_recurrent_slot_amd", "csrc",
                           "la_decode.hip")
 PROFILES = os.path.join(ROOT, "profiles")

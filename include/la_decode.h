@@ -272,7 +272,9 @@ la_status la_replay(const la_replay_args *args, void *stream);
  *   4 = two requests write the same slot,
  *   8 = a request writes a slot another request reads.
  * 0 means the index set is valid. write_idx may be NULL (= read_idx).
- * Asynchronous on `stream`; B == 0 writes 0. */
+ * Asynchronous on `stream`: a one-thread kernel clears *dev_result, then
+ * one workgroup per request compares it with every other request and ORs
+ * its findings in. B == 0 writes 0. */
 la_status la_check_indices(int32_t B, int32_t pool_size,
                            const int32_t *read_idx, const int32_t *write_idx,
                            int32_t *dev_result, void *stream);
@@ -322,7 +324,10 @@ typedef struct la_kernel_info {
     int32_t scratch_bytes;  /* private (spill) memory per lane             */
     int32_t blocks_per_cu;  /* workgroups resident on one compute unit     */
     int32_t waves_per_simd; /* blocks_per_cu * waves per workgroup / 4     */
-    int32_t reserved;       /* 0                                           */
+    int32_t tokens_per_round; /* token records staged in LDS per round (the
+                               instance's; lds_bytes holds min(T, this) of
+                               them); 0 for decode1_kernel, which stages
+                               nothing                                     */
 } la_kernel_info;
 
 /* Describe the kernel that the decode call `args` of `variant` would run

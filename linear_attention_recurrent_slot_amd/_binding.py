@@ -77,7 +77,7 @@ class KernelInfo(ctypes.Structure):
                 ("scratch_bytes", ctypes.c_int32),
                 ("blocks_per_cu", ctypes.c_int32),
                 ("waves_per_simd", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("tokens_per_round", ctypes.c_int32)]
 
 
 VARIANT_CODES = {"lightning": 0, "gdn": 1, "kda": 2}
@@ -458,7 +458,8 @@ def kernel_info_of(variant: str, args: DecodeArgs) -> dict:
             "lds_bytes": info.lds_bytes, "vgprs": info.vgprs,
             "scratch_bytes": info.scratch_bytes,
             "blocks_per_cu": info.blocks_per_cu,
-            "waves_per_simd": info.waves_per_simd}
+            "waves_per_simd": info.waves_per_simd,
+            "tokens_per_round": info.tokens_per_round}
 
 
 def kernel_info(variant, q, k, v, g, beta, pool, read_idx=None,

@@ -1300,26 +1300,51 @@ replay_kernel(const ReplayParams p)
     }
 }
 
-// Validator of the device preconditions (one workgroup).
-__global__ void __launch_bounds__(1024)
-check_indices_kernel(int32_t B, int32_t pool_size, const int32_t *ridx,
-                     const int32_t *widx, int32_t *result)
+// Validators of the device preconditions. A one-thread kernel clears the
+// result word (a kernel rather than a memset, so that the call can be
+// captured into a graph), then the checking grid runs one workgroup per
+// request, which compares that request with every other one and ORs what it
+// finds into the word: the quadratic scan is spread over B workgroups.
+constexpr int kCheckThreads = 256;
+
+__global__ void __launch_bounds__(64) clear_result_kernel(int32_t *result)
+{
+    if (threadIdx.x == 0)
+        *result = 0;
+}
+
+// OR of the workgroup's flags into *result: one global atomic per
+// workgroup that found something.
+__device__ __forceinline__ void or_flags(int32_t f, int32_t *result)
 {
     __shared__ int32_t flags;
     if (threadIdx.x == 0)
         flags = 0;
     __syncthreads();
+    if (f)
+        atomicOr(&flags, f);
+    __syncthreads();
+    if (threadIdx.x == 0 && flags)
+        atomicOr(result, flags);
+}
+
+// Request i = blockIdx.x against every request j != i.
+__global__ void __launch_bounds__(kCheckThreads)
+check_indices_kernel(int32_t B, int32_t pool_size, const int32_t *ridx,
+                     const int32_t *widx, int32_t *result)
+{
+    const int i = blockIdx.x;
+    const int32_t r = ridx[i];
+    const int32_t w = widx ? widx[i] : r;
     int32_t f = 0;
-    for (int i = threadIdx.x; i < B; i += blockDim.x) {
-        const int32_t r = ridx[i];
-        const int32_t w = widx ? widx[i] : r;
+    if (threadIdx.x == 0) {
         if (r >= pool_size)
             f |= 1;
         if (r >= 0 && w >= pool_size)
             f |= 2;
-        if (r < 0 || w < 0)
-            continue;
-        for (int j = 0; j < B; ++j) {
+    }
+    if (r >= 0 && w >= 0) {
+        for (int j = threadIdx.x; j < B; j += kCheckThreads) {
             if (j == i)
                 continue;
             const int32_t rj = ridx[j];
@@ -1332,63 +1357,55 @@ check_indices_kernel(int32_t B, int32_t pool_size, const int32_t *ridx,
                 f |= 8;
         }
     }
-    if (f)
-        atomicOr(&flags, f);
-    __syncthreads();
-    if (threadIdx.x == 0)
-        *result = flags;
+    or_flags(f, result);
 }
 
-// Validator of the paged per-token slot table (one workgroup).
-__global__ void __launch_bounds__(1024)
+// Paged per-token slot table: request i = blockIdx.x; its seed and table
+// entries against every active request j != i.
+__global__ void __launch_bounds__(kCheckThreads)
 check_token_slots_kernel(int32_t B, int32_t T, int32_t pool_size,
                          const int32_t *tab, int64_t stride,
                          const int32_t *nacc, int32_t *result)
 {
-    __shared__ int32_t flags;
-    if (threadIdx.x == 0)
-        flags = 0;
-    __syncthreads();
+    const int i = blockIdx.x;
+    const int32_t *row = tab + i * stride;
+    const int32_t na = nacc[i];
     int32_t f = 0;
-    for (int i = threadIdx.x; i < B; i += blockDim.x) {
-        const int32_t na = nacc[i];
-        if (na < 1 || na > T) {
+    if (na < 1 || na > T) {
+        if (threadIdx.x == 0)
             f |= 16;
-            continue;
-        }
-        const int32_t seed = tab[i * stride + na - 1];
-        if (seed >= pool_size)
+    } else {
+        const int32_t seed = row[na - 1];
+        if (threadIdx.x == 0 && seed >= pool_size)
             f |= 1;
-        if (seed < 0)
-            continue;
-        for (int t = 0; t < T; ++t) {
-            const int32_t s = tab[i * stride + t];
-            if (s >= pool_size)
-                f |= 2;
-            if (s < 0)
-                continue;
-            for (int j = 0; j < B; ++j) {
+        if (seed >= 0) {
+            for (int t = threadIdx.x; t < T; t += kCheckThreads)
+                if (row[t] >= pool_size)
+                    f |= 2;
+            for (int j = threadIdx.x; j < B; j += kCheckThreads) {
                 if (j == i)
                     continue;
                 const int32_t nj = nacc[j];
                 if (nj < 1 || nj > T)
                     continue;
-                const int32_t sj = tab[j * stride + nj - 1];
+                const int32_t *rowj = tab + j * stride;
+                const int32_t sj = rowj[nj - 1];
                 if (sj < 0)
                     continue;
-                if (sj == s)
-                    f |= 8;
-                for (int u = 0; u < T; ++u)
-                    if (tab[j * stride + u] == s)
-                        f |= 4;
+                for (int t = 0; t < T; ++t) {
+                    const int32_t s = row[t];
+                    if (s < 0)
+                        continue;
+                    if (sj == s)
+                        f |= 8;
+                    for (int u = 0; u < T; ++u)
+                        if (rowj[u] == s)
+                            f |= 4;
+                }
             }
         }
     }
-    if (f)
-        atomicOr(&flags, f);
-    __syncthreads();
-    if (threadIdx.x == 0)
-        *result = flags;
+    or_flags(f, result);
 }
 
 // Validator of varlen offsets (one workgroup): bit 1 = an offset outside
@@ -1420,20 +1437,35 @@ check_cu_seqlens_kernel(int32_t B, int32_t T, int32_t total,
 
 typedef void (*KernelFn)(const Params);
 
+// A decode_kernel instance: its entry, its rows per wave (the workgroup has
+// V / rows waves) and its tokens per LDS round (CH; the launch's LDS is
+// min(T, CH) token records). The launch shape is read from here, so it
+// always matches the instance that runs.
+struct Instance {
+    KernelFn fn;
+    int rows;
+    int ch;
+};
+
 template <int VAR, int K, int V, bool BF16S, bool REC, int R, int CH>
-KernelFn pick_io(bool bf16_in, bool bf16_out)
+Instance pick_io(bool bf16_in, bool bf16_out)
 {
+    KernelFn fn;
     if (bf16_in)
-        return bf16_out
-                   ? decode_kernel<VAR, K, V, true, true, BF16S, REC, R, CH>
-                   : decode_kernel<VAR, K, V, true, false, BF16S, REC, R, CH>;
-    return bf16_out
-               ? decode_kernel<VAR, K, V, false, true, BF16S, REC, R, CH>
-               : decode_kernel<VAR, K, V, false, false, BF16S, REC, R, CH>;
+        fn = bf16_out
+                 ? decode_kernel<VAR, K, V, true, true, BF16S, REC, R, CH>
+                 : decode_kernel<VAR, K, V, true, false, BF16S, REC, R, CH>;
+    else
+        fn = bf16_out
+                 ? decode_kernel<VAR, K, V, false, true, BF16S, REC, R, CH>
+                 : decode_kernel<VAR, K, V, false, false, BF16S, REC, R, CH>;
+    return {fn, R, CH};
 }
 
+// ch: the tokens per round the call asks for (kTokChunk, kKdaTokChunk or
+// kCacheTokChunk); records and small grids always take kTokChunk.
 template <int VAR, int K, int V>
-KernelFn pick_dtype(bool bf16_in, bool bf16_out, bool bf16_state, bool rec,
+Instance pick_dtype(bool bf16_in, bool bf16_out, bool bf16_state, bool rec,
                     bool small, int ch)
 {
     constexpr int RR = kRecordRowsPerWave, RS = kSmallGridRowsPerWave;
@@ -1508,7 +1540,7 @@ KernelFn pick_one(int K, int V, bool bi, bool bo, bool bs)
 }
 
 template <int VAR>
-KernelFn pick(int K, int V, bool bi, bool bo, bool bs, bool rec, bool small,
+Instance pick(int K, int V, bool bi, bool bo, bool bs, bool rec, bool small,
               int ch)
 {
     if (K == 128)
@@ -1749,6 +1781,7 @@ struct Launch {
     const char *name = "none";
     dim3 grid, block;
     size_t lds = 0;
+    int ch = 0;  // tokens per LDS round of the instance
     Params p;
 };
 
@@ -1859,47 +1892,44 @@ la_status select_kernel(const la_decode_args *a, int var, Launch &L)
     // VGPRs, one wave per SIMD less)
     const bool cache = !packed && !one && !rec && !small && a->V == 128 &&
                        !a->cu_seqlens && (a->inter || a->token_slots);
-    // tokens per LDS round: the CH of the general-kernel instance picked
-    // below, which the LDS allocation must match
+    // tokens per LDS round asked of the general kernel
     const bool kda_mid = var == VAR_KDA && !packed && !one && !rec &&
                          !small && !cache && !a->inter && !a->token_slots &&
                          a->T > kKdaTokChunk;
     const int ch = cache ? kCacheTokChunk
                    : kda_mid ? kKdaTokChunk
                              : kTokChunk;
-    KernelFn fn;
+    // rows per wave and tokens per round of the instance that runs: 64 rows
+    // and one token in the packed kernel, 8 rows and no LDS in the one-token
+    // kernel
+    Instance inst;
     if (packed)
-        fn = var == VAR_LA    ? pick_packed<VAR_LA>(a->K, a->V, bi, bo)
-             : var == VAR_GDN ? pick_packed<VAR_GDN>(a->K, a->V, bi, bo)
-                              : pick_packed<VAR_KDA>(a->K, a->V, bi, bo);
+        inst = {var == VAR_LA    ? pick_packed<VAR_LA>(a->K, a->V, bi, bo)
+                : var == VAR_GDN ? pick_packed<VAR_GDN>(a->K, a->V, bi, bo)
+                                 : pick_packed<VAR_KDA>(a->K, a->V, bi, bo),
+                64, 1};
     else if (one)
-        fn = var == VAR_LA ? pick_one<VAR_LA>(a->K, a->V, bi, bo, bs)
-                           : pick_one<VAR_GDN>(a->K, a->V, bi, bo, bs);
+        inst = {var == VAR_LA ? pick_one<VAR_LA>(a->K, a->V, bi, bo, bs)
+                              : pick_one<VAR_GDN>(a->K, a->V, bi, bo, bs),
+                8, 0};
     else
-        fn = var == VAR_LA
-                 ? pick<VAR_LA>(a->K, a->V, bi, bo, bs, rec, small, ch)
-             : var == VAR_GDN
-                 ? pick<VAR_GDN>(a->K, a->V, bi, bo, bs, rec, small, ch)
-                 : pick<VAR_KDA>(a->K, a->V, bi, bo, bs, rec, small, ch);
+        inst = var == VAR_LA
+                   ? pick<VAR_LA>(a->K, a->V, bi, bo, bs, rec, small, ch)
+               : var == VAR_GDN
+                   ? pick<VAR_GDN>(a->K, a->V, bi, bo, bs, rec, small, ch)
+                   : pick<VAR_KDA>(a->K, a->V, bi, bo, bs, rec, small, ch);
     // the packed kernel and the small-grid instance keep the plain order
     p.xcd_block = packed || small ? 1 : xcd_block_for(a->B, a->HV);
-    L.fn = fn;
+    L.fn = inst.fn;
     L.name = packed ? "decode_packed_kernel"
              : one  ? "decode1_kernel"
                     : "decode_kernel";
-    // the one-token kernel stages nothing in LDS
-    const int chunk = one ? 0 : a->T < ch ? a->T : ch;
+    L.ch = inst.ch;
+    const int chunk = a->T < inst.ch ? a->T : inst.ch;
     L.lds = static_cast<size_t>(chunk) *
             lds_floats_per_token(var, a->K, a->V) * sizeof(float);
     L.grid = dim3(static_cast<unsigned>(a->B) * a->HV);
-    // rows per wave: 64 in the packed kernel, 8 in the one-token kernel,
-    // kRecordRowsPerWave with records, kSmallGridRowsPerWave on small grids,
-    // kRowsPerWave otherwise
-    L.block = dim3(packed  ? a->V
-                   : one   ? (a->V / 8) * 64
-                   : rec   ? (a->V / kRecordRowsPerWave) * 64
-                   : small ? (a->V / kSmallGridRowsPerWave) * 64
-                           : (a->V / kRowsPerWave) * 64);
+    L.block = dim3((a->V / inst.rows) * 64);
     return LA_OK;
 }
 
@@ -1913,6 +1943,21 @@ la_status launch(const la_decode_args *a, void *stream, int var)
     const hipError_t e = hipLaunchKernel(
         reinterpret_cast<const void *>(L.fn), L.grid, L.block, kargs, L.lds,
         static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
+}
+
+// The clearing kernel, then (B > 0) the checking grid of B workgroups.
+la_status launch_check(const void *kernel, int32_t B, void **kargs,
+                       int32_t *dev_result, void *stream)
+{
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    void *cargs[] = {&dev_result};
+    hipError_t e = hipLaunchKernel(
+        reinterpret_cast<const void *>(clear_result_kernel), dim3(1),
+        dim3(64), cargs, 0, st);
+    if (e == hipSuccess && B > 0)
+        e = hipLaunchKernel(kernel, dim3(static_cast<unsigned>(B)),
+                            dim3(kCheckThreads), kargs, 0, st);
     return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
 }
 
@@ -1953,6 +1998,7 @@ la_status la_decode_kernel_info(int32_t variant, const la_decode_args *args,
         r.scratch_bytes = static_cast<int32_t>(at.localSizeBytes);
         r.blocks_per_cu = nb;
         r.waves_per_simd = nb * static_cast<int32_t>(L.block.x / 64) / 4;
+        r.tokens_per_round = L.ch;
     }
     *info = r;
     return LA_OK;
@@ -2063,10 +2109,8 @@ la_status la_check_indices(int32_t B, int32_t pool_size,
         !aligned(write_idx, 4))
         return LA_ERR_ALIGN;
     void *kargs[] = {&B, &pool_size, &read_idx, &write_idx, &dev_result};
-    const hipError_t e = hipLaunchKernel(
-        reinterpret_cast<const void *>(check_indices_kernel), dim3(1),
-        dim3(1024), kargs, 0, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
+    return launch_check(reinterpret_cast<const void *>(check_indices_kernel),
+                        B, kargs, dev_result, stream);
 }
 
 la_status la_check_token_slots(int32_t B, int32_t T, int32_t pool_size,
@@ -2086,10 +2130,9 @@ la_status la_check_token_slots(int32_t B, int32_t T, int32_t pool_size,
         return LA_ERR_ALIGN;
     void *kargs[] = {&B, &T, &pool_size, &token_slots, &table_stride,
                      &num_accepted, &dev_result};
-    const hipError_t e = hipLaunchKernel(
-        reinterpret_cast<const void *>(check_token_slots_kernel), dim3(1),
-        dim3(1024), kargs, 0, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? LA_OK : LA_ERR_LAUNCH;
+    return launch_check(
+        reinterpret_cast<const void *>(check_token_slots_kernel), B, kargs,
+        dev_result, stream);
 }
 
 la_status la_check_cu_seqlens(int32_t B, int32_t T, int32_t total_tokens,
