@@ -4,8 +4,9 @@ One step = one library call (gather, per-token prologue, decay, read-outs,
 rank-1 update, outputs, optional per-token cache, writeback) over one batch
 of synthetic input resident in HBM. Prints one JSON line.
 
-Timing: W untimed warm-up calls, then K timed calls bracketed by
-torch.cuda.synchronize(). Two HIP events on the stream the kernels are
+Timing: untimed calls for 0.3 s of wall time (the GPU reaches its steady
+clocks after the idle setup), W untimed warm-up calls, then K timed calls
+bracketed by torch.cuda.synchronize(). Two HIP events on the stream the kernels are
 launched on bracket the K back-to-back launches; their elapsed time / K is
 the kernel's average launch duration used for the roofline. The calls
 rotate over R independent copies of the pool and inputs, R x bytes-per-call
@@ -32,6 +33,7 @@ METRIC = ("decode tokens/sec and achieved HBM GB/s (% of peak), K=V=128 fp32 "
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
 ROTATE_BYTES = 4 << 30  # bytes the rotated copies span (16 x the MALL)
 ROTATE_MAX = 512
+SETTLE_SECONDS = 0.3  # untimed calls before the warm-up (steady clocks)
 DEFAULT_WORKLOAD = "kda_b256_t8"
 KERNEL_SRC = os.path.join(ROOT, "linear_attention_recurrent_slot_amd", "csrc",
                           "la_decode.hip")
@@ -368,6 +370,19 @@ def main():
                                     wl.pool_size)
         if int(bad.item()) != 0:
             raise RuntimeError("workload index set violates the preconditions")
+
+    # Bring the GPU to its steady clocks before the W warm-up calls: the
+    # setup above leaves it idle, and a short timed run (K = 20) would
+    # otherwise see the first calls at a lower clock. Untimed calls for
+    # SETTLE_SECONDS of wall time.
+    t_settle = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t_settle < SETTLE_SECONDS:
+        calls[i % R]()
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
 
     for i in range(args.warmup):
         calls[i % R]()
