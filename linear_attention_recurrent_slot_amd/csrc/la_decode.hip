@@ -92,12 +92,23 @@ constexpr int64_t kSmallGridWaves = 4096;
 // xcd_block_for for the measurements.
 constexpr int kXcdRangeMaxHeads = 48;
 constexpr int kXcdBlockPairs = 32;
-// Largest grid of the packed one-token bf16 kernel. Beyond it the general
-// kernel (in XCD ranges) is faster for KDA, B * 24 tiles, % of peak HBM
-// bandwidth, packed -> general: 2304 60.3 -> 59.9, 3072 62.5 -> 62.4,
-// 3840 62.8 -> 64.7, 4608 63.0 -> 65.5, 6144 62.8 -> 67.7, 9216 63.7 ->
-// 69.3.
-constexpr int64_t kPackedMaxTiles = 3072;
+// Workgroups per K = V = 128 tile of the one-token kernel: its waves are
+// independent (no LDS, no barrier), so a tile's 16 waves run as
+// 2^kOneSplitLog2 workgroups, and each XCD takes whole tiles in turn (the
+// parts of a tile share an L2 for its q, k, v). Measured on MI355X at
+// steady clocks, % of peak HBM bandwidth, one workgroup per tile (XCD
+// ranges or 32-pair blocks) -> 4 workgroups in whole tiles: GDN B=64 HV=32
+// 69.9 -> 74.6, Lightning B=33 H=64 74.9 -> 79.3 (2 workgroups in XCD
+// ranges or blocks: 71.4 and 77.8; 8 workgroups: 70.8 and 73.6; 4
+// workgroups in XCD ranges or blocks of tiles: 74.5 and 78.0, better only
+// at 16 value heads). Other tile shapes keep one workgroup per tile in XCD
+// ranges (K = V = 64, GDN B=256 HV=32, us per call: 46.2; split in 2 or 4
+// workgroups: 51.9 and 52.6; K = 64, V = 128: 89.0 against 91.1 split in
+// 4).
+#ifndef LA_ONE_SPLIT_LOG2
+#define LA_ONE_SPLIT_LOG2 2
+#endif
+constexpr int kOneSplitLog2 = LA_ONE_SPLIT_LOG2;
 static_assert(kRowsPerWave == 8 || kRowsPerWave == 16 || kRowsPerWave == 32,
               "8, 16 or 32 rows");
 constexpr int kTokChunk = 8;
@@ -154,6 +165,7 @@ struct Params {
     const float *dt_bias;  // [HV] (GDN) or [HV, K] (KDA)
     float lower_bound;
     int32_t xcd_block;  // pairs per block dealt to the XCDs (pair_of_block)
+    int32_t split_log2;  // decode1_kernel: log2 of the workgroups per tile
 };
 
 // ---------------------------------------------------------------- helpers
@@ -983,7 +995,7 @@ __global__ void __launch_bounds__(V) decode_packed_kernel(const Params p)
     store_out<BF16OUT>(p.out, oidx, mine);
 }
 
-// One token of Lightning or GDN with no per-token writes. Each load
+// One token with no per-token writes (any variant). Each load
 // instruction of a wave reads 1 KiB of contiguous tile bytes (64 lanes x
 // 16 B: 2 to 8 whole rows); on MI355X an in-place tile update moved that way
 // keeps HBM busier than rows split into 128-byte pieces. A wave owns 8 rows,
@@ -1004,7 +1016,6 @@ __global__ void __launch_bounds__(V) decode_packed_kernel(const Params p)
 template <int VAR, int K, int V, bool BF16IN, bool BF16OUT, bool BF16S>
 __global__ void __launch_bounds__((V / 8) * 64) decode1_kernel(const Params p)
 {
-    static_assert(VAR != VAR_KDA, "KDA one-token calls use decode_kernel");
     constexpr uint32_t ES = BF16S ? 2u : 4u;  // state bytes per element
     constexpr int CPL = 16 / ES;    // columns per lane (one chunk per row)
     constexpr int G = CPL / 4;      // 4-column groups per chunk
@@ -1012,11 +1023,16 @@ __global__ void __launch_bounds__((V / 8) * 64) decode1_kernel(const Params p)
     constexpr int RPI = 64 / LPR;   // rows per load instruction
     constexpr int RPL = 8 / RPI;    // rows per lane
 
-    const int pair = pair_of_block(p.xcd_block);
+    // workgroup -> (pair, part); part p of a tile split over 2^split_log2
+    // workgroups takes its waves p * NW / 2^split_log2 ...
+    const int blk = pair_of_block(p.xcd_block);
+    const int pair = blk >> p.split_log2;
+    const int part = blk - (pair << p.split_log2);
     const int b = pair / p.HV;
     const int hv = pair - b * p.HV;
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(
+        (threadIdx.x >> 6) + (part * (V / 8) >> p.split_log2));
     const int cl = lane % LPR;
     const int rl = lane / LPR;
     constexpr int NJ = LPR / 8;  // chunks c + 8 j per row and c
@@ -1062,6 +1078,17 @@ __global__ void __launch_bounds__((V / 8) * 64) decode1_kernel(const Params p)
         gs = p.g[go] + (p.gate ? p.dt_bias[hv] : 0.f);
     if constexpr (VAR != VAR_LA)
         bs = p.beta[b * p.sb_b + hv * p.sb_h];
+    // KDA: the raw gates (with dt_bias in the gate chain) in the
+    // prologue's layout, K / 64 channels per lane, as prologue_load forms
+    // them; read in the chunk layout instead, every lane would fetch 4 or 8
+    // gates for 2 to 4 rows, as many load instructions as the tile takes
+    float ev[EPL];
+    if constexpr (VAR == VAR_KDA) {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            ev[i] = p.g[go + lane * EPL + i] +
+                    (p.gate ? p.dt_bias[hv * K + lane * EPL + i] : 0.f);
+    }
 
     // the tile rows of this lane
     const uint32_t row_bytes = static_cast<uint32_t>(p.sp_row) * ES;
@@ -1115,13 +1142,35 @@ __global__ void __launch_bounds__((V / 8) * 64) decode1_kernel(const Params p)
         qq[g] = f4{qv[4 * g] * rq, qv[4 * g + 1] * rq, qv[4 * g + 2] * rq,
                    qv[4 * g + 3] * rq};
     }
-    float decay;
-    if constexpr (VAR == VAR_LA)
-        decay = p.g ? p.g[hv]
-                    : __expf(-exp2f(-8.f * static_cast<float>(hv + 1) /
-                                    static_cast<float>(p.HV)));
-    else
-        decay = __expf(p.gate ? gate_chain(p, gs, p.A_log[hv]) : gs);
+    // decay of each 4-column group: one factor (Lightning, GDN) or the
+    // per-column KDA factors, computed as prologue_finish computes them
+    f4 dec[G];
+    if constexpr (VAR == VAR_KDA) {
+        const float a_log = p.gate ? p.A_log[hv] : 0.f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            ev[i] = __expf(p.gate ? gate_chain(p, ev[i], a_log) : ev[i]);
+        // channel CPL cl + i of the chunk layout is element i % EPL of
+        // lane (CPL cl + i) / EPL
+        float e[CPL];
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+            e[i] = __shfl(ev[i % EPL], (CPL / EPL) * cl + i / EPL);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            dec[g] = f4{e[4 * g], e[4 * g + 1], e[4 * g + 2], e[4 * g + 3]};
+    } else {
+        float decay;
+        if constexpr (VAR == VAR_LA)
+            decay = p.g ? p.g[hv]
+                        : __expf(-exp2f(-8.f * static_cast<float>(hv + 1) /
+                                        static_cast<float>(p.HV)));
+        else
+            decay = __expf(p.gate ? gate_chain(p, gs, p.A_log[hv]) : gs);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            dec[g] = f4{decay, decay, decay, decay};
+    }
     float beta = 1.f;
     if constexpr (VAR != VAR_LA)
         beta = (p.flags & LA_F_BETA_LOGIT) ? 1.f / (1.f + __expf(-bs)) : bs;
@@ -1140,7 +1189,7 @@ __global__ void __launch_bounds__((V / 8) * 64) decode1_kernel(const Params p)
     for (int j = 0; j < RPL; ++j) {
 #pragma unroll
         for (int g = 0; g < G; ++g)
-            S[j][g] *= decay;
+            S[j][g] *= dec[g];
         float u = 0.f, wq = 0.f;
 #pragma unroll
         for (int st = 0; st < NJ; ++st) {
@@ -1852,40 +1901,35 @@ la_status select_kernel(const la_decode_args *a, int var, Launch &L)
     const bool bi = a->qkv_dtype == LA_BF16, bo = a->out_dtype == LA_BF16;
     const bool bs = a->state_dtype == LA_BF16;
     const bool rec = a->factors != nullptr;
-    // One token of Lightning or GDN with no per-token writes: the
-    // contiguous-row kernel where it is the faster one. All three kernels
-    // give identical bits, so the choice is by speed alone. Measured on
-    // MI355X with a 4 GiB rotation, % of peak HBM bandwidth, previous kernel
-    // -> this one:
-    //   fp32 Lightning B=33 H=64: 71.0 -> 74.3; GDN B=64 HV=32: 66.8 -> 68.7
-    //   bf16 GDN B=72..96 HV=32: 57-62 -> 62-67; Lightning H=64
-    //   B=36..48: 62-64 -> 69-71
-    // At 512-1024 fp32 tiles it was 9-12 % slower, and KDA (B=256 H=24) 1 %
-    // slower. On a bf16 pool the packed kernel keeps 2048 tiles in one
-    // resident round and is 3-5 % faster there (GDN B=64 HV=32: 66.2 vs
-    // 62.9; Lightning B=32 H=64: 68.7 vs 67.0); above that the one-token
-    // kernel beats the general one at every head count measured (HV 8-64,
-    // 2.5-6 points). On fp32 pools at K = V = 128 the general kernel wins
-    // below 32 value heads (GDN HV=16 B=256: 67.8 vs 64.7; HV=24 B=256:
-    // 70.2 vs 66.5; Lightning HV=16 B=256: 69.4 vs 66.8) and at 32 heads
-    // beyond 4096 tiles (GDN B=256: 71.3 vs 70.1), while the one-token kernel
-    // wins from 48 heads at every size (HV=64 B=128: 78.6 vs 73.7). The
-    // other tile shapes need 4096 tiles (GDN K=V=64 HV=32: 57.4 vs 65.5 at
-    // 2048 tiles, 66.5 vs 64.5 at 8192).
+    // One token with no per-token writes: the contiguous-row kernel where
+    // it is the faster one. All three kernels give identical bits, so the
+    // choice is by speed alone. Measured on MI355X at steady clocks with a
+    // 4 GiB rotation (the one-token kernel in 4 workgroups per tile),
+    // general -> one-token kernel, us per call:
+    //   fp32 K = V = 128, 2048 tiles or more, any head count: GDN B=64
+    //   HV=32 48.3 -> 45.3; GDN HV=16 B=256 97.8 -> 95.5; HV=24 B=256
+    //   141.4 -> 136.7; HV=32 B=256 184.9 -> 178.1; Lightning H=16 B=256
+    //   96.5 -> 92.5; Lightning B=33 H=64 -> 44.1
+    //   KDA H=24 B=96 55.4 -> 52.3, B=256 141.2 -> 136.6
+    //   1024 tiles: Lightning H=64 B=16 24.4 -> 23.1, but GDN HV=32 B=32
+    //   24.0 -> 24.5 and HV=16 B=64 24.8 -> 26.1 (48 or more heads only)
+    //   K = V = 64: 2048 tiles 12.8 -> 14.4; 8192 tiles: GDN 51.5 -> 46.2,
+    //   KDA 51.4 -> 46.6
+    // On a bf16 pool the packed kernel keeps up to 2048 tiles (GDN HV=32,
+    // packed against one-token kernel: 1024 tiles 13.2 against 15.1, 2048
+    // tiles 25.0 against 24.7, a tie);
+    // beyond, the one-token kernel: KDA H=24 B=96 32.3 -> 28.1 and B=128
+    // 41.2 -> 37.3 (packed), B=256 76.5 -> 72.7 (general).
     const int64_t tiles = static_cast<int64_t>(a->B) * a->HV;
     const bool wide = a->K == 128 && a->V == 128
-                          ? tiles >= 2048 &&
-                                (a->HV >= 48 || (a->HV >= 32 && tiles <= 4096))
+                          ? tiles >= 2048 || (a->HV >= 48 && tiles >= 1024)
                           : tiles >= 4096;
-    const bool one = var != VAR_KDA && a->T == 1 && !a->inter &&
-                     !a->token_slots && !rec && !a->cu_seqlens &&
-                     (bs ? tiles > 2048 : wide);
-    // otherwise one token on a bf16 pool with no per-token writes: the
-    // packed tile, up to kPackedMaxTiles (KDA only reaches beyond: the
-    // other variants take the one-token kernel there)
+    const bool one = a->T == 1 && !a->inter && !a->token_slots && !rec &&
+                     !a->cu_seqlens && (bs ? tiles > 2048 : wide);
+    // otherwise one token on a bf16 pool with no per-token writes (up to
+    // 2048 tiles): the packed tile
     const bool packed = !one && bs && a->T == 1 && !a->inter &&
-                        !a->token_slots && !rec && !a->cu_seqlens &&
-                        tiles <= kPackedMaxTiles;
+                        !a->token_slots && !rec && !a->cu_seqlens;
     // a grid of the general kernel that fills less than one resident round
     const bool small = !packed && !one && !rec &&
                        tiles * (a->V / kSmallGridRowsPerWave) <= kSmallGridWaves;
@@ -1911,8 +1955,9 @@ la_status select_kernel(const la_decode_args *a, int var, Launch &L)
                                  : pick_packed<VAR_KDA>(a->K, a->V, bi, bo),
                 64, 1};
     else if (one)
-        inst = {var == VAR_LA ? pick_one<VAR_LA>(a->K, a->V, bi, bo, bs)
-                              : pick_one<VAR_GDN>(a->K, a->V, bi, bo, bs),
+        inst = {var == VAR_LA    ? pick_one<VAR_LA>(a->K, a->V, bi, bo, bs)
+                : var == VAR_GDN ? pick_one<VAR_GDN>(a->K, a->V, bi, bo, bs)
+                                 : pick_one<VAR_KDA>(a->K, a->V, bi, bo, bs),
                 8, 0};
     else
         inst = var == VAR_LA
@@ -1920,8 +1965,13 @@ la_status select_kernel(const la_decode_args *a, int var, Launch &L)
                : var == VAR_GDN
                    ? pick<VAR_GDN>(a->K, a->V, bi, bo, bs, rec, small, ch)
                    : pick<VAR_KDA>(a->K, a->V, bi, bo, bs, rec, small, ch);
-    // the packed kernel and the small-grid instance keep the plain order
-    p.xcd_block = packed || small ? 1 : xcd_block_for(a->B, a->HV);
+    // the packed kernel and the small-grid instance keep the plain order;
+    // the one-token kernel at K = V = 128 splits tiles and deals them whole
+    // (blocks of 2^split_log2 workgroups) in turn
+    p.split_log2 = one && a->K == 128 && a->V == 128 ? kOneSplitLog2 : 0;
+    p.xcd_block = p.split_log2    ? 1 << p.split_log2
+                  : packed || small ? 1
+                                    : xcd_block_for(a->B, a->HV);
     L.fn = inst.fn;
     L.name = packed ? "decode_packed_kernel"
              : one  ? "decode1_kernel"
@@ -1930,8 +1980,8 @@ la_status select_kernel(const la_decode_args *a, int var, Launch &L)
     const int chunk = a->T < inst.ch ? a->T : inst.ch;
     L.lds = static_cast<size_t>(chunk) *
             lds_floats_per_token(var, a->K, a->V) * sizeof(float);
-    L.grid = dim3(static_cast<unsigned>(a->B) * a->HV);
-    L.block = dim3((a->V / inst.rows) * 64);
+    L.grid = dim3((static_cast<unsigned>(a->B) * a->HV) << p.split_log2);
+    L.block = dim3(((a->V / inst.rows) * 64) >> p.split_log2);
     return LA_OK;
 }
 

@@ -405,6 +405,7 @@ PACKED_QKV_KERNELS = {
                             "decode1_kernel"),
     "packed_bf16_kda": (W.KDA, 8, 1, 8, 8, torch.bfloat16,
                         "decode_packed_kernel"),
+    "one_token_kda": (W.KDA, 96, 1, 24, 24, torch.float32, "decode1_kernel"),
     "general_32_rows_gdn": (W.GDN, 40, 2, 16, 32, torch.float32,
                             "decode_kernel"),
 }
@@ -1640,18 +1641,18 @@ def test_hip_graph_capture_replays_match_eager(variant):
 # ---------------- one-token kernel (fp32 pools >= 2048 tiles, bf16 > 2048)
 
 
-@pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN])
+@pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN, W.KDA])
 @pytest.mark.parametrize("K,V", SHAPES)
 @pytest.mark.parametrize("dtype,out", [(torch.float32, torch.float32),
                                        (torch.bfloat16, torch.float32),
                                        (torch.bfloat16, torch.bfloat16)],
                          ids=["f32", "bf16", "bf16_out_bf16"])
 def test_one_token_kernel_parity(variant, K, V, dtype, out):
-    """Lightning/GDN, T = 1, fp32 pool, B * HV = 2048 tiles at K = V = 128
-    and 4096 at the other shapes: the contiguous-row one-token kernel.
-    Padded requests, separate and skipped writes on a strided pool; sampled
-    requests against the oracle, every untouched byte checked."""
-    seed = (6000 + 100 * [W.LIGHTNING, W.GDN].index(variant)
+    """T = 1, fp32 pool, B * HV = 2048 tiles at K = V = 128 and 4096 at the
+    other shapes: the contiguous-row one-token kernel (4 workgroups per
+    tile). Padded requests, separate and skipped writes on a strided pool;
+    every request against the oracle, every untouched byte checked."""
+    seed = (6000 + 100 * [W.LIGHTNING, W.GDN, W.KDA].index(variant)
             + 10 * SHAPES.index((K, V)) + (5 if dtype != torch.float32 else 0)
             + (2 if out != torch.float32 else 0))
     B, HV = (64 if (K, V) == (128, 128) else 128), 32
@@ -1669,25 +1670,42 @@ def test_one_token_kernel_parity(variant, K, V, dtype, out):
     run_and_check(wl)
 
 
-def test_one_token_kernel_gate_chain():
-    """The gate chain (both forms) in the one-token GDN kernel."""
-    wl = W.make("onegate", W.GDN, B=64, T=1, H=16, HV=32, K=128, V=128,
-                pool_size=128, seed=6300, separate_write=True)
-    assert _kernel_name(wl) == "decode1_kernel"
+@pytest.mark.parametrize("variant", [W.GDN, W.KDA])
+def test_one_token_kernel_gate_chain(variant):
+    """The gate chain (both forms) in the one-token kernel (a call without
+    update records, which would take the general kernel)."""
+    lad = _lad()
+    seed = 6300 + 10 * [W.GDN, W.KDA].index(variant)
+    wl = W.make("onegate", variant, B=64, T=1, H=16, HV=32, K=128, V=128,
+                pool_size=128, seed=seed, separate_write=True)
     wl.g = 2 * torch.randn(wl.g.shape, generator=torch.Generator()
-                           .manual_seed(6301))
-    a_log, dt = _gate_inputs(W.GDN, wl.HV, wl.K, 6302)
+                           .manual_seed(seed + 1))
+    a_log, dt = _gate_inputs(variant, wl.HV, wl.K, seed + 2)
+    fn = lad.gdn_decode_mtp if variant == W.GDN else lad.kda_decode_mtp
     for lb in (None, -5.0):
-        got, ref = _gate_run(wl, a_log, dt, lb)
+        d = wl.to(DEV)
+        kw = dict(l2norm_qk=wl.l2norm, beta_logit=wl.beta_logit,
+                  A_log=a_log.to(DEV), dt_bias=dt.to(DEV), lower_bound=lb)
+        info = lad.kernel_info(variant, d.q, d.k, d.v, d.g, d.beta,
+                               d.pool(), d.read_idx, d.write_idx, **kw)
+        assert info["kernel"] == "decode1_kernel"
+        out, _ = fn(d.q, d.k, d.v, d.g, d.beta, d.pool(), d.read_idx,
+                    d.write_idx, **kw)
+        torch.cuda.synchronize()
+        ref = oracle.decode(VARIANT_CODE[variant], wl.q, wl.k, wl.v, wl.g,
+                            wl.beta, wl.pool(), wl.read_idx, wl.write_idx,
+                            flags=_flags(wl), A_log=a_log, dt_bias=dt,
+                            lower_bound=lb)
         kind, tol_out, tol_state = _tol(wl)
-        assert _err(kind, got["out"].float(), ref["out"]) <= tol_out
+        assert _err(kind, out.cpu().float(), ref["out"]) <= tol_out
+        got = d.backing.cpu()
         for b, w in enumerate(wl.write_idx.tolist()):
             if w >= 0:
-                assert _err(kind, got["backing"][w].float(),
-                            ref["pool"][w]) <= tol_state, b
+                assert _err(kind, got[w].float(), ref["pool"][w]) <= \
+                    tol_state, b
 
 
-@pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN])
+@pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN, W.KDA])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16],
                          ids=["f32", "bf16"])
 def test_one_token_kernel_token_split_bit_identical(variant, dtype):
@@ -1700,6 +1718,12 @@ def test_one_token_kernel_token_split_bit_identical(variant, dtype):
                 pool_size=64, seed=6400 + len(variant) + T * (dtype ==
                                                               torch.bfloat16),
                 act_dtype=dtype)
+    step = dataclasses.replace(wl, T=1, q=wl.q[:, :1], k=wl.k[:, :1],
+                               v=wl.v[:, :1],
+                               g=wl.g if variant == W.LIGHTNING
+                               else wl.g[:, :1],
+                               beta=None if wl.beta is None else wl.beta[:, :1])
+    assert _kernel_name(step) == "decode1_kernel"
     whole = gpu_run(wl)
     d = wl.to(DEV)
     pool = d.backing
@@ -1710,10 +1734,11 @@ def test_one_token_kernel_token_split_bit_identical(variant, dtype):
             o, _ = lad.la_decode(d.q[:, sl], d.k[:, sl], d.v[:, sl], pool,
                                  d.read_idx, lam=d.g)
         else:
-            o, _ = lad.gdn_decode_mtp(d.q[:, sl], d.k[:, sl], d.v[:, sl],
-                                      d.g[:, sl], d.beta[:, sl], pool,
-                                      d.read_idx, l2norm_qk=wl.l2norm,
-                                      beta_logit=wl.beta_logit)
+            fn = (lad.gdn_decode_mtp if variant == W.GDN
+                  else lad.kda_decode_mtp)
+            o, _ = fn(d.q[:, sl], d.k[:, sl], d.v[:, sl], d.g[:, sl],
+                      d.beta[:, sl], pool, d.read_idx, l2norm_qk=wl.l2norm,
+                      beta_logit=wl.beta_logit)
         outs.append(o)
     torch.cuda.synchronize()
     assert torch.equal(_bits(torch.cat(outs, 1).cpu()), _bits(whole["out"]))
@@ -1747,7 +1772,9 @@ def _one_token_batch_invariance(wl, sub=8, **kw):
                                      d.read_idx[sl], d.write_idx[sl],
                                      lam=d.g)
             else:
-                o, _ = lad.gdn_decode_mtp(
+                fn = (lad.gdn_decode_mtp if wl.variant == W.GDN
+                      else lad.kda_decode_mtp)
+                o, _ = fn(
                     d.q[sl], d.k[sl], d.v[sl], d.g[sl], d.beta[sl], pool,
                     d.read_idx[sl], d.write_idx[sl], l2norm_qk=wl.l2norm,
                     beta_logit=wl.beta_logit, **kw)
@@ -1758,8 +1785,8 @@ def _one_token_batch_invariance(wl, sub=8, **kw):
 
 
 @pytest.mark.parametrize("variant,raw", [(W.LIGHTNING, False), (W.GDN, False),
-                                         (W.GDN, True)],
-                         ids=["lightning", "gdn", "gdn_raw"])
+                                         (W.GDN, True), (W.KDA, False)],
+                         ids=["lightning", "gdn", "gdn_raw", "kda"])
 @pytest.mark.parametrize("K,V", SHAPES)
 @pytest.mark.parametrize("state", [torch.float32, torch.bfloat16],
                          ids=["f32_state", "bf16_state"])
@@ -1777,7 +1804,8 @@ def test_one_token_kernel_batch_invariant(variant, raw, K, V, state, dtype):
     seed = (6700 + 10 * SHAPES.index((K, V)) + (1 if raw else 0)
             + (2 if state != torch.float32 else 0)
             + (4 if dtype != torch.float32 else 0)
-            + (100 if variant == W.GDN else 0))
+            + (100 if variant == W.GDN else 0)
+            + (200 if variant == W.KDA else 0))
     wl = W.make("inv", variant, B=B, T=1, H=16, HV=HV, K=K, V=V,
                 pool_size=2 * B, seed=seed, act_dtype=dtype, pool_std=0.1,
                 separate_write=True, state_dtype=state,
@@ -1794,29 +1822,31 @@ def test_one_token_kernel_batch_invariant(variant, raw, K, V, state, dtype):
     assert torch.equal(_bits(wp), _bits(sp))
 
 
+@pytest.mark.parametrize("variant", [W.GDN, W.KDA])
 @pytest.mark.parametrize("lower_bound", [None, -5.0], ids=["softplus", "lb"])
-def test_one_token_kernel_batch_invariant_gate_chain(lower_bound):
+def test_one_token_kernel_batch_invariant_gate_chain(variant, lower_bound):
     """Batch invariance across the one-token kernel's grid threshold with
     the in-kernel gate chain."""
-    wl = W.make("invgate", W.GDN, B=72, T=1, H=16, HV=32, K=128, V=128,
-                pool_size=144, seed=6900, separate_write=True)
+    seed = 6900 + 10 * [W.GDN, W.KDA].index(variant)
+    wl = W.make("invgate", variant, B=72, T=1, H=16, HV=32, K=128, V=128,
+                pool_size=144, seed=seed, separate_write=True)
     wl.g = 2 * torch.randn(wl.g.shape, generator=torch.Generator()
-                           .manual_seed(6901))
-    a_log, dt = _gate_inputs(W.GDN, wl.HV, wl.K, 6902)
+                           .manual_seed(seed + 1))
+    a_log, dt = _gate_inputs(variant, wl.HV, wl.K, seed + 2)
     (wo, wp), (so, sp) = _one_token_batch_invariance(
         wl, A_log=a_log.to(DEV), dt_bias=dt.to(DEV), lower_bound=lower_bound)
     assert torch.equal(_bits(wo), _bits(so))
     assert torch.equal(_bits(wp), _bits(sp))
 
 
-@pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN])
+@pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN, W.KDA])
 @pytest.mark.parametrize("K,V", SHAPES)
 def test_one_token_kernel_bf16_state(variant, K, V):
     """The one-token kernel on a bf16 pool (2304 tiles; at 2048 and below a
     bf16 pool takes the packed kernel): states widened to fp32, rounded once
     to nearest even on store; padded and skipped-write requests; sampled
     against the oracle, every untouched byte checked."""
-    seed = 6500 + 100 * [W.LIGHTNING, W.GDN].index(variant) + \
+    seed = 6500 + 100 * [W.LIGHTNING, W.GDN, W.KDA].index(variant) + \
         10 * SHAPES.index((K, V))
     B = 72
     ridx = list(range(0, 2 * B, 2))
@@ -1833,14 +1863,17 @@ def test_one_token_kernel_bf16_state(variant, K, V):
 @pytest.mark.parametrize("variant,B,H,HV,K,kernel", [
     # one range per XCD, 3 pairs past them
     (W.GDN, 67, 5, 25, 64, "decode_kernel"),
-    # 32-pair blocks, 48 pairs past them
-    (W.LIGHTNING, 33, 48, 48, 128, "decode_kernel"),
-    # 2079 pairs in the one-token kernel: ranges of 259, 7 past them
+    # 32-pair blocks, 48 pairs past them (816 tiles: below the one-token
+    # kernel's threshold)
+    (W.LIGHTNING, 17, 48, 48, 128, "decode_kernel"),
+    # 2079 pairs in the one-token kernel: 8316 workgroups (4 per tile),
+    # whole tiles dealt to the XCDs in turn, 28 workgroups past them
     (W.GDN, 63, 11, 33, 128, "decode1_kernel"),
 ], ids=["ranges_gdn", "blocks_lightning", "ranges_one_token"])
 def test_xcd_block_order_covers_every_pair(variant, B, H, HV, K, kernel):
-    """Workgroups take their pairs in XCD blocks (whole ranges below 48
-    value heads, 32-pair blocks from 48) with the pairs past the last whole
+    """Workgroups take their pairs in XCD blocks (general kernel: whole
+    ranges below 48 value heads, 32-pair blocks from 48; one-token kernel:
+    one tile's workgroups at a time) with the workgroups past the last whole
     round in plain order: every request's outputs and stored state match the
     oracle, and nothing else in the pool changes."""
     wl = W.make("xcd", variant, B=B, T=1, H=H, HV=HV, K=K, V=K,
@@ -1913,28 +1946,31 @@ def test_small_grid_instance_bit_identical(variant, T, state):
 @pytest.mark.parametrize("case", [
     # (variant, B, T, HV, state dtype, expected kernel, threads, cache,
     #  tokens per LDS round)
-    ("gdn", 64, 1, 32, torch.float32, "decode1_kernel", 1024, False, 0),
-    ("lightning", 33, 1, 64, torch.float32, "decode1_kernel", 1024, False, 0),
+    # one token: the one-token kernel (4 workgroups of 64 threads per tile
+    # row group: 256 threads) on fp32 pools at K = V = 128 from 2048 tiles,
+    # or from 1024 tiles with 48 or more value heads; on bf16 pools beyond
+    # 2048 tiles (the packed kernel up to there)
+    ("gdn", 64, 1, 32, torch.float32, "decode1_kernel", 256, False, 0),
+    ("lightning", 33, 1, 64, torch.float32, "decode1_kernel", 256, False, 0),
+    ("kda", 96, 1, 24, torch.float32, "decode1_kernel", 256, False, 0),
+    ("gdn", 128, 1, 16, torch.float32, "decode1_kernel", 256, False, 0),
+    ("lightning", 96, 1, 24, torch.float32, "decode1_kernel", 256, False, 0),
+    ("gdn", 136, 1, 32, torch.float32, "decode1_kernel", 256, False, 0),
+    ("gdn", 96, 1, 48, torch.float32, "decode1_kernel", 256, False, 0),
+    ("lightning", 16, 1, 64, torch.float32, "decode1_kernel", 256, False, 0),
+    ("lightning", 15, 1, 64, torch.float32, "decode_kernel", 256, False, 8),
+    ("gdn", 32, 1, 32, torch.float32, "decode_kernel", 256, False, 8),
     ("gdn", 8, 1, 32, torch.float32, "decode_kernel", 512, False, 8),
-    ("gdn", 64, 1, 32, torch.bfloat16, "decode_packed_kernel", 128, False, 1),
-    ("gdn", 72, 1, 32, torch.bfloat16, "decode1_kernel", 1024, False, 0),
-    ("kda", 96, 1, 24, torch.float32, "decode_kernel", 256, False, 8),
-    ("kda", 8, 1, 24, torch.bfloat16, "decode_packed_kernel", 128, False, 1),
-    ("kda", 128, 1, 24, torch.bfloat16, "decode_packed_kernel", 128, False,
-     1),
-    ("kda", 129, 1, 24, torch.bfloat16, "decode_kernel", 256, False, 8),
-    ("gdn", 16, 4, 32, torch.float32, "decode_kernel", 512, False, 8),
-    ("gdn", 17, 4, 32, torch.float32, "decode_kernel", 256, False, 8),
     ("kda", 21, 1, 24, torch.float32, "decode_kernel", 512, False, 8),
     ("kda", 22, 1, 24, torch.float32, "decode_kernel", 256, False, 8),
-    # fp32 pools: fewer than 32 value heads, or 32 heads beyond 4096 tiles,
-    # take the general kernel; 48 or more heads the one-token kernel
-    ("gdn", 128, 1, 16, torch.float32, "decode_kernel", 256, False, 8),
-    ("lightning", 96, 1, 24, torch.float32, "decode_kernel", 256, False, 8),
-    ("gdn", 136, 1, 32, torch.float32, "decode_kernel", 256, False, 8),
-    ("gdn", 128, 1, 32, torch.float32, "decode1_kernel", 1024, False, 0),
-    ("gdn", 96, 1, 48, torch.float32, "decode1_kernel", 1024, False, 0),
-    ("gdn", 136, 1, 16, torch.bfloat16, "decode1_kernel", 1024, False, 0),
+    ("gdn", 64, 1, 32, torch.bfloat16, "decode_packed_kernel", 128, False, 1),
+    ("kda", 8, 1, 24, torch.bfloat16, "decode_packed_kernel", 128, False, 1),
+    ("gdn", 72, 1, 32, torch.bfloat16, "decode1_kernel", 256, False, 0),
+    ("kda", 128, 1, 24, torch.bfloat16, "decode1_kernel", 256, False, 0),
+    ("gdn", 136, 1, 16, torch.bfloat16, "decode1_kernel", 256, False, 0),
+    # several tokens: the general kernel
+    ("gdn", 16, 4, 32, torch.float32, "decode_kernel", 512, False, 8),
+    ("gdn", 17, 4, 32, torch.float32, "decode_kernel", 256, False, 8),
     # tokens per LDS round: four for KDA beyond four tokens on 32-row grids
     # (a partial last round at T = 5..7), two on 32-row grids that cache
     # every token, eight on small grids and otherwise
@@ -1967,7 +2003,9 @@ def test_kernel_info_reports_the_dispatch(case):
     info = lad.kernel_info(variant, d.q, d.k, d.v, d.g, d.beta, d.pool(),
                            d.read_idx, d.write_idx, inter=inter, **kw)
     assert info["kernel"] == kernel
-    assert info["grid_blocks"] == B * HV
+    # the one-token kernel runs each tile as 4 workgroups of 4 waves
+    assert info["grid_blocks"] == B * HV * (4 if kernel == "decode1_kernel"
+                                            else 1)
     assert info["block_threads"] == threads
     assert info["scratch_bytes"] == 0
     assert 0 < info["vgprs"] <= 512
