@@ -34,16 +34,20 @@
 //  - Instances: 32 rows per wave; 16 on grids that fill less than one
 //    resident round and with update records.
 //  - Workgroups take their pairs in XCD blocks (xcd_block_pair): whole
-//    requests per XCD below 48 value heads, 32-pair blocks from 48.
+//    requests per XCD below 48 value heads, 32-pair blocks from 48; the
+//    split one-token kernel deals whole tiles to the XCDs in turn.
 //  - No MFMA: per token the work is two matrix-vector products and a rank-1
 //    update against one vector operand, bound by HBM traffic of the state.
 //  - Per token and element: one multiply (decay), two FMAs (read-outs) and
 //    one FMA (update); Lightning needs no key read-out.
-//  - Three kernels compute this: decode_kernel (every call), the packed
-//    one-token kernel for bf16 pools and the contiguous-row one-token
-//    kernel for large grids. They perform the same fp32 operations in the
-//    same order, so a request's results do not depend on which one runs:
-//    not on the batch size, nor on how its tokens are split over calls.
+//  - Three kernels compute this: decode_kernel (the general one, which
+//    serves every call), the packed one-token kernel for bf16 pools up to
+//    2048 tiles and the contiguous-row one-token kernel for larger grids
+//    (decode1_kernel: each load instruction reads 1 KiB of contiguous tile
+//    bytes, a wave owns 8 rows, and a 128 x 128 tile runs as 4 workgroups
+//    with no LDS). They perform the same fp32 operations in the same order,
+//    so a request's results do not depend on which one runs: not on the
+//    batch size, nor on how its tokens are split over calls.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -125,9 +129,14 @@ constexpr int kTokChunk = 8;
 // records: KDA B=64 T=4 verify + replay 67.9 -> 62.3).
 constexpr int kCacheTokChunk = 2;
 // Tokens per LDS round of 32-row KDA grids with more than four tokens and no
-// per-token state writes. Measured on MI355X, KDA B=256 H=24 T=8, % of peak
-// HBM bandwidth, 8 -> 4 tokens per round: 65.1 -> 66.9 and 65.4 -> 67.2 in
-// two runs; GDN B=64 HV=32 T=8 lost 2.8 points the same way and keeps 8.
+// per-token state writes. Measured on MI355X at steady clocks (HIP events
+// over 200 calls, 5 rotating pool copies), KDA B=256 H=24 T=8, us per call
+// in two runs: 8 tokens per round 171.4 and 170.8, 4 tokens 165.6 and 165.6,
+// 2 tokens 171.5 and 171.5. 16 rows per wave with 8 tokens per round gained
+// 0.3-1.2 % at T=8 (164.3) but lost 7-12 % at T=12 and 16, and the tile
+// split over 2 or 4 workgroups (each forming every token's record) lost
+// 7 and 18 %. GDN keeps 8 tokens per round (B=64 HV=32 T=8: 59.4 against
+// 62.5 with 4; B=128: 109.5 against 113.2).
 constexpr int kKdaTokChunk = 4;
 constexpr float kL2Eps = 1e-6f;
 
