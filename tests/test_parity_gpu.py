@@ -2533,7 +2533,7 @@ def _medium_combo(i):
 def test_random_medium_grids_general_kernel(i):
     """12 fixed draws of medium grids (the 32-row general kernel): variant,
     tile shape, head count, dtypes, strided pools, separate and skipped
-    writes, the per-token cache and a padded request; sampled requests
+    writes, the per-token cache and a padded request; every request
     against the oracle, every untouched byte of the pool checked."""
     cfg = _medium_combo(i)
     variant = cfg.pop("variant")
