@@ -113,6 +113,11 @@ constexpr int kXcdBlockPairs = 32;
 #define LA_ONE_SPLIT_LOG2 2
 #endif
 constexpr int kOneSplitLog2 = LA_ONE_SPLIT_LOG2;
+// Largest grid of the packed bf16 one-token kernel: what one resident round
+// of it holds on 256 CUs (eight 2-wave workgroups per CU at 4 waves per SIMD;
+// six for the KDA instance at 3). The one-token kernel takes larger grids.
+constexpr int64_t kPackedMaxTiles = 2048;
+constexpr int64_t kPackedMaxTilesKda = 1536;
 static_assert(kRowsPerWave == 8 || kRowsPerWave == 16 || kRowsPerWave == 32,
               "8, 16 or 32 rows");
 constexpr int kTokChunk = 8;
@@ -1924,19 +1929,24 @@ la_status select_kernel(const la_decode_args *a, int var, Launch &L)
     //   24.0 -> 24.5 and HV=16 B=64 24.8 -> 26.1 (48 or more heads only)
     //   K = V = 64: 2048 tiles 12.8 -> 14.4; 8192 tiles: GDN 51.5 -> 46.2,
     //   KDA 51.4 -> 46.6
-    // On a bf16 pool the packed kernel keeps up to 2048 tiles (GDN HV=32,
-    // packed against one-token kernel: 1024 tiles 13.2 against 15.1, 2048
-    // tiles 25.0 against 24.7, a tie);
-    // beyond, the one-token kernel: KDA H=24 B=96 32.3 -> 28.1 and B=128
-    // 41.2 -> 37.3 (packed), B=256 76.5 -> 72.7 (general).
+    // On a bf16 pool the packed kernel keeps the grids it runs in one
+    // resident round: 2048 tiles for Lightning and GDN (4 waves per SIMD),
+    // 1536 for KDA (142 VGPRs, 3 waves per SIMD). Packed against one-token
+    // kernel: GDN HV=32 1024 tiles 13.2 against 14.3, 1536 tiles 19.1
+    // against 19.5, 2048 tiles 25.0 against 24.7 (HV=16: 25.5 against
+    // 26.0); KDA H=24 1536 tiles 19.1 against 20.2, 1920 tiles 27.2
+    // against 23.9. Beyond, the one-token kernel: KDA H=24 B=96 32.3 ->
+    // 28.1 and B=128 41.2 -> 37.3 (packed), B=256 76.5 -> 72.7 (general).
     const int64_t tiles = static_cast<int64_t>(a->B) * a->HV;
     const bool wide = a->K == 128 && a->V == 128
                           ? tiles >= 2048 || (a->HV >= 48 && tiles >= 1024)
                           : tiles >= 4096;
+    const int64_t packed_max = var == VAR_KDA ? kPackedMaxTilesKda
+                                              : kPackedMaxTiles;
     const bool one = a->T == 1 && !a->inter && !a->token_slots && !rec &&
-                     !a->cu_seqlens && (bs ? tiles > 2048 : wide);
+                     !a->cu_seqlens && (bs ? tiles > packed_max : wide);
     // otherwise one token on a bf16 pool with no per-token writes (up to
-    // 2048 tiles): the packed tile
+    // packed_max tiles): the packed tile
     const bool packed = !one && bs && a->T == 1 && !a->inter &&
                         !a->token_slots && !rec && !a->cu_seqlens;
     // a grid of the general kernel that fills less than one resident round

@@ -1638,7 +1638,7 @@ def test_hip_graph_capture_replays_match_eager(variant):
         assert torch.equal(_bits(d.backing), _bits(eager[2])), rep
 
 
-# ---------------- one-token kernel (fp32 pools >= 2048 tiles, bf16 > 2048)
+# ------- one-token kernel (fp32 pools from 2048 tiles, bf16 beyond one packed round)
 
 
 @pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN, W.KDA])
@@ -1949,7 +1949,7 @@ def test_small_grid_instance_bit_identical(variant, T, state):
     # one token: the one-token kernel (4 workgroups of 64 threads per tile
     # row group: 256 threads) on fp32 pools at K = V = 128 from 2048 tiles,
     # or from 1024 tiles with 48 or more value heads; on bf16 pools beyond
-    # 2048 tiles (the packed kernel up to there)
+    # 2048 tiles, 1536 for KDA (the packed kernel up to there)
     ("gdn", 64, 1, 32, torch.float32, "decode1_kernel", 256, False, 0),
     ("lightning", 33, 1, 64, torch.float32, "decode1_kernel", 256, False, 0),
     ("kda", 96, 1, 24, torch.float32, "decode1_kernel", 256, False, 0),
@@ -1965,6 +1965,8 @@ def test_small_grid_instance_bit_identical(variant, T, state):
     ("kda", 22, 1, 24, torch.float32, "decode_kernel", 256, False, 8),
     ("gdn", 64, 1, 32, torch.bfloat16, "decode_packed_kernel", 128, False, 1),
     ("kda", 8, 1, 24, torch.bfloat16, "decode_packed_kernel", 128, False, 1),
+    ("kda", 64, 1, 24, torch.bfloat16, "decode_packed_kernel", 128, False, 1),
+    ("kda", 65, 1, 24, torch.bfloat16, "decode1_kernel", 256, False, 0),
     ("gdn", 72, 1, 32, torch.bfloat16, "decode1_kernel", 256, False, 0),
     ("kda", 128, 1, 24, torch.bfloat16, "decode1_kernel", 256, False, 0),
     ("gdn", 136, 1, 16, torch.bfloat16, "decode1_kernel", 256, False, 0),
