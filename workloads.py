@@ -319,12 +319,23 @@ def gdn_small_k64(seed=1):
                 pool_std=0.1, g_low=-1.0, g_high=0.0, read_idx=[2, 0, 5, 1])
 
 
+def head_decays(HV: int) -> torch.Tensor:
+    """The per-head decay input lambda_h = exp(-2^(-8 (h + 1) / HV)),
+    h = 0..HV-1 (the slope schedule of the Lightning setting), evaluated in
+    fp64 and rounded once to fp32, so that every consumer is handed the same
+    fp32 values."""
+    h = torch.arange(HV, dtype=torch.float64)
+    return torch.exp(-torch.exp2(-8.0 * (h + 1) / HV)).float()
+
+
 def lightning_b33_h64(seed=2):
     """Lightning decode: B=33 requests at random distinct slots of a pool of
     40 (the cuLA big-batch pool test), H=64, K=V=128, T=1, bf16 q/k/v
-    ~N(0,1) unnormalised, pool ~N(0,0.05), built-in per-head decay."""
+    ~N(0,1) unnormalised, pool ~N(0,0.05), per-head decays given as the
+    fp32 array head_decays(64)."""
     return make("lightning_b33_h64", LIGHTNING, B=33, T=1, H=64, HV=64,
-                K=128, V=128, pool_size=40, seed=seed, l2norm=False)
+                K=128, V=128, pool_size=40, seed=seed, l2norm=False,
+                lightning_decay=head_decays(64))
 
 
 def gdn_gva_b64(seed=3):
