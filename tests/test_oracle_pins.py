@@ -257,6 +257,31 @@ def test_lightning_builtin_decay_schedule():
     assert np.all(np.diff(vals) > 0)
 
 
+def test_named_lightning_decays_follow_the_schedule():
+    """The Lightning workload hands both sides an fp32 decay array: it is the
+    oracle's own schedule (same head indexing) rounded once to fp32, so a
+    call with it matches a call without it to fp32 rounding of the decays."""
+    import workloads as W
+    HV, K, V = 64, 4, 4
+    lam = W.head_decays(HV)
+    assert lam.dtype.is_floating_point and lam.element_size() == 4
+    rng = np.random.default_rng(12)
+    pool = rng.standard_normal((2, HV, V, K))
+    q = rng.standard_normal((1, 1, HV, K))
+    k = rng.standard_normal((1, 1, HV, K))
+    v = rng.standard_normal((1, 1, HV, V))
+    a = oracle.decode(oracle.LIGHTNING, q, k, v, None, None, pool, [1])
+    b = oracle.decode(oracle.LIGHTNING, q, k, v, lam.double().numpy(), None,
+                      pool, [1])
+    assert _rel(b["pool"], a["pool"]) < 1e-7
+    assert _rel(b["out"], a["out"]) < 1e-7
+    # and not the schedule of another head count
+    c = oracle.decode(oracle.LIGHTNING, q, k, v,
+                      W.head_decays(32).repeat(2).double().numpy(), None,
+                      pool, [1])
+    assert _rel(c["pool"], a["pool"]) > 1e-3
+
+
 def test_kda_constant_gate_equals_gdn():
     rng = np.random.default_rng(10)
     c = _random_case(rng, oracle.GDN)
