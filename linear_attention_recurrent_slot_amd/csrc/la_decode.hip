@@ -113,6 +113,14 @@ constexpr int kXcdBlockPairs = 32;
 #define LA_ONE_SPLIT_LOG2 2
 #endif
 constexpr int kOneSplitLog2 = LA_ONE_SPLIT_LOG2;
+// Whole tiles per XCD block of the split one-token kernel. Same box, steady
+// clocks, us per call, 1 tile per block -> 4: GDN B=64 HV=32 45.8 -> 45.5,
+// Lightning B=33 H=64 44.3 -> 43.9, KDA B=256 H=24 137.3 -> 134.7, GDN
+// B=256 HV=16 95.4 -> 93.5, GDN B=128 HV=32 88.4 -> 87.8, bf16 GDN B=128
+// HV=32 46.6 -> 45.6. Two tiles fell between, eight matched four, 16 and 32
+// lost at 32 heads (GDN B=64: 46.4, 47.0) and a whole request per block
+// lost more (GDN B=64 46.9, Lightning 47.8).
+constexpr int kOneXcdTiles = 4;
 // Largest grid of the packed bf16 one-token kernel: what one resident round
 // of it holds on 256 CUs (eight 2-wave workgroups per CU at 4 waves per SIMD;
 // six for the KDA instance at 3). The one-token kernel takes larger grids.
@@ -1985,10 +1993,10 @@ la_status select_kernel(const la_decode_args *a, int var, Launch &L)
                    ? pick<VAR_GDN>(a->K, a->V, bi, bo, bs, rec, small, ch)
                    : pick<VAR_KDA>(a->K, a->V, bi, bo, bs, rec, small, ch);
     // the packed kernel and the small-grid instance keep the plain order;
-    // the one-token kernel at K = V = 128 splits tiles and deals them whole
-    // (blocks of 2^split_log2 workgroups) in turn
+    // the one-token kernel at K = V = 128 splits tiles and deals blocks of
+    // kOneXcdTiles whole tiles to the XCDs in turn
     p.split_log2 = one && a->K == 128 && a->V == 128 ? kOneSplitLog2 : 0;
-    p.xcd_block = p.split_log2    ? 1 << p.split_log2
+    p.xcd_block = p.split_log2    ? kOneXcdTiles << p.split_log2
                   : packed || small ? 1
                                     : xcd_block_for(a->B, a->HV);
     L.fn = inst.fn;

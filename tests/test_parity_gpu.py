@@ -1867,13 +1867,14 @@ def test_one_token_kernel_bf16_state(variant, K, V):
     # kernel's threshold)
     (W.LIGHTNING, 17, 48, 48, 128, "decode_kernel"),
     # 2079 pairs in the one-token kernel: 8316 workgroups (4 per tile),
-    # whole tiles dealt to the XCDs in turn, 28 workgroups past them
+    # blocks of 4 whole tiles (16 workgroups) dealt to the XCDs in turn, 124
+    # workgroups past the last whole round of blocks
     (W.GDN, 63, 11, 33, 128, "decode1_kernel"),
 ], ids=["ranges_gdn", "blocks_lightning", "ranges_one_token"])
 def test_xcd_block_order_covers_every_pair(variant, B, H, HV, K, kernel):
     """Workgroups take their pairs in XCD blocks (general kernel: whole
-    ranges below 48 value heads, 32-pair blocks from 48; one-token kernel:
-    one tile's workgroups at a time) with the workgroups past the last whole
+    ranges below 48 value heads, 32-pair blocks from 48; split one-token
+    kernel: blocks of four whole tiles) with the workgroups past the last whole
     round in plain order: every request's outputs and stored state match the
     oracle, and nothing else in the pool changes."""
     wl = W.make("xcd", variant, B=B, T=1, H=H, HV=HV, K=K, V=K,
