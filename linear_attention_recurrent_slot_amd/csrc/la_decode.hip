@@ -1928,13 +1928,19 @@ la_status select_kernel(const la_decode_args *a, int var, Launch &L)
     // choice is by speed alone. Measured on MI355X at steady clocks with a
     // 4 GiB rotation (the one-token kernel in 4 workgroups per tile),
     // general -> one-token kernel, us per call:
-    //   fp32 K = V = 128, 2048 tiles or more, any head count: GDN B=64
-    //   HV=32 48.3 -> 45.3; GDN HV=16 B=256 97.8 -> 95.5; HV=24 B=256
-    //   141.4 -> 136.7; HV=32 B=256 184.9 -> 178.1; Lightning H=16 B=256
-    //   96.5 -> 92.5; Lightning B=33 H=64 -> 44.1
-    //   KDA H=24 B=96 55.4 -> 52.3, B=256 141.2 -> 136.6
-    //   1024 tiles: Lightning H=64 B=16 24.4 -> 23.1, but GDN HV=32 B=32
-    //   24.0 -> 24.5 and HV=16 B=64 24.8 -> 26.1 (48 or more heads only)
+    //   fp32 K = V = 128 beyond 1024 tiles (one resident round of the
+    //   general kernel), any head count: 1032-1536 tiles: KDA H=24 B=43
+    //   26.8 -> 25.1, B=64 37.5 -> 35.1; KDA H=12 B=128 38.1 -> 36.9; GDN
+    //   HV=32 B=48 37.4 -> 34.6; GDN HV=16 B=96 37.6 -> 35.8; Lightning
+    //   H=32 B=33 27.8 -> 24.7, B=48 37.4 -> 34.2; Lightning H=16 B=96 37.3
+    //   -> 35.1; 2048 tiles and more: GDN B=64 HV=32 48.3 -> 45.3; GDN
+    //   HV=16 B=256 97.8 -> 95.5; HV=24 B=256 141.4 -> 136.7; HV=32 B=256
+    //   184.9 -> 178.1; Lightning H=16 B=256 96.5 -> 92.5; KDA H=24 B=96
+    //   55.4 -> 52.3, B=256 141.2 -> 136.6
+    //   exactly 1024 tiles: Lightning H=64 B=16 24.4 -> 23.1 (48 or more
+    //   heads take it), but GDN HV=32 B=32 24.0 -> 24.2 and HV=16 B=64 24.8
+    //   -> 25.6; 512-768 tiles: the general kernel (Lightning H=16 B=32
+    //   12.7 against 13.8, KDA H=3 B=256 18.0 against 20.3)
     //   K = V = 64: 2048 tiles 12.8 -> 14.4; 8192 tiles: GDN 51.5 -> 46.2,
     //   KDA 51.4 -> 46.6
     // On a bf16 pool the packed kernel keeps the grids it runs in one
@@ -1947,7 +1953,7 @@ la_status select_kernel(const la_decode_args *a, int var, Launch &L)
     // 28.1 and B=128 41.2 -> 37.3 (packed), B=256 76.5 -> 72.7 (general).
     const int64_t tiles = static_cast<int64_t>(a->B) * a->HV;
     const bool wide = a->K == 128 && a->V == 128
-                          ? tiles >= 2048 || (a->HV >= 48 && tiles >= 1024)
+                          ? tiles > 1024 || (a->HV >= 48 && tiles == 1024)
                           : tiles >= 4096;
     const int64_t packed_max = var == VAR_KDA ? kPackedMaxTilesKda
                                               : kPackedMaxTiles;

@@ -1948,9 +1948,9 @@ def test_small_grid_instance_bit_identical(variant, T, state):
     # (variant, B, T, HV, state dtype, expected kernel, threads, cache,
     #  tokens per LDS round)
     # one token: the one-token kernel (4 workgroups of 64 threads per tile
-    # row group: 256 threads) on fp32 pools at K = V = 128 from 2048 tiles,
-    # or from 1024 tiles with 48 or more value heads; on bf16 pools beyond
-    # 2048 tiles, 1536 for KDA (the packed kernel up to there)
+    # row group: 256 threads) on fp32 pools at K = V = 128 beyond 1024
+    # tiles, or from 1024 tiles with 48 or more value heads; on bf16 pools
+    # beyond 2048 tiles, 1536 for KDA (the packed kernel up to there)
     ("gdn", 64, 1, 32, torch.float32, "decode1_kernel", 256, False, 0),
     ("lightning", 33, 1, 64, torch.float32, "decode1_kernel", 256, False, 0),
     ("kda", 96, 1, 24, torch.float32, "decode1_kernel", 256, False, 0),
@@ -1961,6 +1961,9 @@ def test_small_grid_instance_bit_identical(variant, T, state):
     ("lightning", 16, 1, 64, torch.float32, "decode1_kernel", 256, False, 0),
     ("lightning", 15, 1, 64, torch.float32, "decode_kernel", 256, False, 8),
     ("gdn", 32, 1, 32, torch.float32, "decode_kernel", 256, False, 8),
+    ("gdn", 33, 1, 32, torch.float32, "decode1_kernel", 256, False, 0),
+    ("kda", 43, 1, 24, torch.float32, "decode1_kernel", 256, False, 0),
+    ("kda", 42, 1, 24, torch.float32, "decode_kernel", 256, False, 8),
     ("gdn", 8, 1, 32, torch.float32, "decode_kernel", 512, False, 8),
     ("kda", 21, 1, 24, torch.float32, "decode_kernel", 512, False, 8),
     ("kda", 22, 1, 24, torch.float32, "decode_kernel", 256, False, 8),
@@ -2521,7 +2524,11 @@ def _medium_combo(i):
     T = rng.choice([1, 2, 3, 4]) if state == torch.float32 else \
         rng.choice([2, 3, 4])
     lo = 4096 * 16 // V + 1   # first grid beyond the small-grid instance
-    B = rng.randint(-(-lo // HV), 2047 // HV)
+    # one token on an fp32 pool at K = V = 128 takes the one-token kernel
+    # beyond 1024 tiles
+    hi = 1024 if (T == 1 and state == torch.float32 and K == V == 128) \
+        else 2047
+    B = rng.randint(-(-lo // HV), hi // HV)
     return dict(variant=variant, B=B, T=T, H=H, HV=HV, K=K, V=V,
                 pool_size=2 * B + 3, state_dtype=state,
                 act_dtype=rng.choice([torch.float32, torch.bfloat16]),
