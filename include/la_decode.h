@@ -312,12 +312,13 @@ typedef enum la_variant {
 /* The kernel a decode call selects, its launch shape and its register
  * budget on the current device. */
 typedef struct la_kernel_info {
-    const char *kernel;     /* "decode_kernel" (every call),
+    const char *kernel;     /* "decode_kernel" (any call),
                                "decode1_kernel" (one token, large grids),
                                "decode_packed_kernel" (one token, bf16 pool)
                                or "none" (B = 0: nothing is launched);
                                static storage owned by the library */
-    int32_t grid_blocks;    /* workgroups: B * HV                          */
+    int32_t grid_blocks;    /* workgroups: B * HV (four per tile in
+                               decode1_kernel at K = V = 128)              */
     int32_t block_threads;  /* threads per workgroup                       */
     int32_t lds_bytes;      /* dynamic LDS per workgroup                   */
     int32_t vgprs;          /* architected VGPRs per lane                  */

@@ -35,17 +35,18 @@
 //    resident round and with update records.
 //  - Workgroups take their pairs in XCD blocks (xcd_block_pair): whole
 //    requests per XCD below 48 value heads, 32-pair blocks from 48; the
-//    split one-token kernel deals whole tiles to the XCDs in turn.
+//    split one-token kernel deals blocks of four whole tiles to the XCDs in
+//    turn.
 //  - No MFMA: per token the work is two matrix-vector products and a rank-1
 //    update against one vector operand, bound by HBM traffic of the state.
 //  - Per token and element: one multiply (decay), two FMAs (read-outs) and
 //    one FMA (update); Lightning needs no key read-out.
 //  - Three kernels compute this: decode_kernel (the general one, which
 //    serves every call), the packed one-token kernel for bf16 pools up to
-//    2048 tiles and the contiguous-row one-token kernel for larger grids
-//    (decode1_kernel: each load instruction reads 1 KiB of contiguous tile
-//    bytes, a wave owns 8 rows, and a 128 x 128 tile runs as 4 workgroups
-//    with no LDS). They perform the same fp32 operations in the same order,
+//    2048 tiles (1536 for KDA) and the contiguous-row one-token kernel for
+//    larger grids (decode1_kernel: each load instruction reads 1 KiB of
+//    contiguous tile bytes, a wave owns 8 rows, and a 128 x 128 tile runs as
+//    4 workgroups with no LDS). They perform the same fp32 operations in the same order,
 //    so a request's results do not depend on which one runs: not on the
 //    batch size, nor on how its tokens are split over calls.
 
@@ -1021,7 +1022,8 @@ __global__ void __launch_bounds__(V) decode_packed_kernel(const Params p)
 // instruction of a wave reads 1 KiB of contiguous tile bytes (64 lanes x
 // 16 B: 2 to 8 whole rows); on MI355X an in-place tile update moved that way
 // keeps HBM busier than rows split into 128-byte pieces. A wave owns 8 rows,
-// so a workgroup has V / 8 waves. Lane (cl = lane % LPR, rl = lane / LPR)
+// so a tile has V / 8 waves, run as 2^split_log2 workgroups (the waves share
+// nothing). Lane (cl = lane % LPR, rl = lane / LPR)
 // holds the 16-byte chunk cl of rows 8 wave + RPI j + rl (4 fp32 or 8 bf16
 // columns, widened to fp32 in registers). Every wave forms the token
 // prologue it needs itself (q and k, its rows of v, the scalars): no LDS and
@@ -1046,7 +1048,7 @@ __global__ void __launch_bounds__((V / 8) * 64) decode1_kernel(const Params p)
     constexpr int RPL = 8 / RPI;    // rows per lane
 
     // workgroup -> (pair, part); part p of a tile split over 2^split_log2
-    // workgroups takes its waves p * NW / 2^split_log2 ...
+    // workgroups takes the tile's waves p V / (8 2^split_log2) onwards
     const int blk = pair_of_block(p.xcd_block);
     const int pair = blk >> p.split_log2;
     const int part = blk - (pair << p.split_log2);
