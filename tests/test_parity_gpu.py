@@ -1638,7 +1638,7 @@ def test_hip_graph_capture_replays_match_eager(variant):
         assert torch.equal(_bits(d.backing), _bits(eager[2])), rep
 
 
-# ------- one-token kernel (fp32 pools from 2048 tiles, bf16 beyond one packed round)
+# ------- one-token kernel (fp32 pools beyond 1024 tiles, bf16 beyond one packed round)
 
 
 @pytest.mark.parametrize("variant", [W.LIGHTNING, W.GDN, W.KDA])
@@ -2111,11 +2111,12 @@ PADDED_CASES = {
                            pool_size=12, inter=True, pads=(4, 1)),
     "general_kda_t1_v64": dict(variant=W.KDA, B=8, T=1, H=4, HV=4, K=128,
                                V=64, pool_size=16, pads=(4, 1)),
-    # one-token kernel (>= 2048 fp32 tiles)
+    # one-token kernel (fp32: beyond 1024 tiles at K = V = 128, the split
+    # form; from 4096 tiles at the other shapes, one workgroup per tile)
     "one_token_gdn": dict(variant=W.GDN, B=64, T=1, H=16, HV=32, K=128,
                           V=128, pool_size=128, pads=(4, 1)),
-    "one_token_lightning_k64": dict(variant=W.LIGHTNING, B=64, T=1, H=32,
-                                    HV=32, K=64, V=128, pool_size=128,
+    "one_token_lightning_k64": dict(variant=W.LIGHTNING, B=128, T=1, H=32,
+                                    HV=32, K=64, V=128, pool_size=256,
                                     pads=(8, 0)),
     # bf16 pools: packed kernel, one-token kernel, general kernel
     "packed_bf16_lightning": dict(variant=W.LIGHTNING, B=8, T=1, H=4, HV=4,
@@ -2142,6 +2143,11 @@ def test_padded_rows_and_heads(name):
     seed = 7300 + sorted(PADDED_CASES).index(name)
     wl = W.make("padded_" + name, variant, seed=seed, separate_write=True,
                 write_skip=0.2, l2norm=variant != W.LIGHTNING, **case)
+    # the case's name says which kernel it is for
+    assert _kernel_name(wl) == ("decode1_kernel" if name.startswith("one_")
+                                else "decode_packed_kernel"
+                                if name.startswith("packed_")
+                                else "decode_kernel"), name
     lad = _lad()
     d = wl.to(DEV)
     big, pool = _padded_pool(wl, row_pad, head_pad)
