@@ -2280,6 +2280,8 @@ def test_far_slots_bit_identical_to_contiguous(name):
     wl = W.make("far_" + name, variant, T=1, K=128, V=128,
                 seed=7700 + sorted(FAR_CASES).index(name),
                 l2norm=variant != W.LIGHTNING, **case)
+    assert _kernel_name(wl) == ("decode1_kernel" if name.startswith("one_")
+                                else "decode_packed_kernel"), name
     lad = _lad()
     d = wl.to(DEV)
     buf, far = _far_pool(wl)
