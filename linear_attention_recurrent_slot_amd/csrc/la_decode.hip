@@ -153,6 +153,29 @@ constexpr int kCacheTokChunk = 2;
 // 62.5 with 4; B=128: 109.5 against 113.2).
 constexpr int kKdaTokChunk = 4;
 constexpr float kL2Eps = 1e-6f;
+// Final write-back of the general kernel's 32-row instances without
+// per-token writes (fp32 K = V = 128 tiles): each wave passes its rows, 8 at
+// a time, through its own LDS area and writes them with instructions that
+// cover 2 whole rows (512 B each) instead of 8 128-byte row pieces. Rows
+// are kStageRowFloats apart in the area (4 floats of padding). Same box,
+// steady clocks, us per call, direct -> staged (two runs): KDA B=256 H=24
+// T=8 165.2 -> 163.0, KDA B=128 T=8 90.0 -> 88.5, GDN B=64 HV=32 T=8 60.1 ->
+// 58.3, T=2 48.6 -> 48.1, GDN B=32 HV=32 T=1 24.0 -> 23.0, Lightning B=15
+// H=64 23.4 -> 23.0; the varlen GDN batch with the cache even (110.1 and
+// 110.4). Not used where it lost: the 16-row instance (KDA B=16 T=8 15.5
+// -> 16.1) and the two-token instance that writes every token's state (GDN
+// B=32 T=4 with the cache 69.1 -> 69.6). Loading the tile the same way
+// (contiguous loads, transposed through LDS before the token loop) lost
+// everywhere (KDA T=8 170.1, GDN T=1 24.6). Instances with bf16 outputs
+// keep direct stores: their token loop leaves no registers to spare, and
+// the staging took three of them past 128 VGPRs (3 waves per SIMD).
+constexpr int kStageRowFloats = 132;
+template <int K, int V, bool BF16OUT, bool BF16S, bool REC, int R, int CH>
+constexpr bool staged_writeback()
+{
+    return !BF16S && !BF16OUT && !REC && K == 128 && V == 128 && R == 32 &&
+           CH != kCacheTokChunk;
+}
 
 // Activation strides are 32-bit: the host checks that every element offset
 // of q, k, v, g, beta and out fits in 31 bits (the pool keeps 64-bit
@@ -450,6 +473,15 @@ __device__ __forceinline__ void lds_barrier()
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Order one wave's LDS accesses to an area only it uses: what its lanes
+// wrote before is visible to all its lanes after (no workgroup barrier).
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
 // LDS record of one token: k^[K], q^[K], (KDA: e[K]), v[V] (rows permuted so
@@ -866,10 +898,36 @@ decode_kernel(const Params p)
     if (w >= 0) {  // in-place writeback to the write slot
         const BufRsrc dst = make_rsrc(
             pool + (w * p.sp_slot + hv * p.sp_head) * ES, tile_bytes);
+        if constexpr (staged_writeback<K, V, BF16OUT, BF16S, REC, R, CH>()) {
+            // this wave's area follows the token records; lane l stores
+            // 16-byte chunk l % 32 of row l / 32 of each row pair
+            float *stage = lds + (T < CH ? T : CH) * L::size +
+                           wave * (8 * kStageRowFloats);
+            const int pr = lane >> 5, pc = lane & 31;
 #pragma unroll
-        for (int i = 0; i < RPL; ++i)
-            IO::store_row(dst, lane_off,
-                          (wave * R + i * 8) * row_bytes, S[i]);
+            for (int i = 0; i < RPL; ++i) {
+#pragma unroll
+                for (int m = 0; m < CPL; ++m)
+                    *reinterpret_cast<f4 *>(stage + rs * kStageRowFloats +
+                                            (c8 + 8 * m) * 4) = S[i][m];
+                wave_lds_sync();  // the wave's writes before its reads
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    store_b128(__builtin_bit_cast(
+                                   u4, *reinterpret_cast<const f4 *>(
+                                           stage +
+                                           (2 * j + pr) * kStageRowFloats +
+                                           pc * 4)),
+                               dst, pr * row_bytes + pc * 16u,
+                               (wave * R + i * 8 + 2 * j) * row_bytes);
+                wave_lds_sync();  // its reads before the next rows' writes
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < RPL; ++i)
+                IO::store_row(dst, lane_off,
+                              (wave * R + i * 8) * row_bytes, S[i]);
+        }
     }
 }
 
@@ -1520,6 +1578,7 @@ struct Instance {
     KernelFn fn;
     int rows;
     int ch;
+    int stage_floats;  // LDS beyond the token records (staged write-back)
 };
 
 template <int VAR, int K, int V, bool BF16S, bool REC, int R, int CH>
@@ -1534,7 +1593,11 @@ Instance pick_io(bool bf16_in, bool bf16_out)
         fn = bf16_out
                  ? decode_kernel<VAR, K, V, false, true, BF16S, REC, R, CH>
                  : decode_kernel<VAR, K, V, false, false, BF16S, REC, R, CH>;
-    return {fn, R, CH};
+    // LDS of the staged write-back (fp32 outputs only)
+    constexpr int stage = staged_writeback<K, V, false, BF16S, REC, R, CH>()
+                              ? (V / R) * 8 * kStageRowFloats
+                              : 0;
+    return {fn, R, CH, bf16_out ? 0 : stage};
 }
 
 // ch: the tokens per round the call asks for (kTokChunk, kKdaTokChunk or
@@ -1988,12 +2051,12 @@ la_status select_kernel(const la_decode_args *a, int var, Launch &L)
         inst = {var == VAR_LA    ? pick_packed<VAR_LA>(a->K, a->V, bi, bo)
                 : var == VAR_GDN ? pick_packed<VAR_GDN>(a->K, a->V, bi, bo)
                                  : pick_packed<VAR_KDA>(a->K, a->V, bi, bo),
-                64, 1};
+                64, 1, 0};
     else if (one)
         inst = {var == VAR_LA    ? pick_one<VAR_LA>(a->K, a->V, bi, bo, bs)
                 : var == VAR_GDN ? pick_one<VAR_GDN>(a->K, a->V, bi, bo, bs)
                                  : pick_one<VAR_KDA>(a->K, a->V, bi, bo, bs),
-                8, 0};
+                8, 0, 0};
     else
         inst = var == VAR_LA
                    ? pick<VAR_LA>(a->K, a->V, bi, bo, bs, rec, small, ch)
@@ -2013,8 +2076,10 @@ la_status select_kernel(const la_decode_args *a, int var, Launch &L)
                     : "decode_kernel";
     L.ch = inst.ch;
     const int chunk = a->T < inst.ch ? a->T : inst.ch;
-    L.lds = static_cast<size_t>(chunk) *
-            lds_floats_per_token(var, a->K, a->V) * sizeof(float);
+    L.lds = (static_cast<size_t>(chunk) *
+                 lds_floats_per_token(var, a->K, a->V) +
+             inst.stage_floats) *
+            sizeof(float);
     L.grid = dim3((static_cast<unsigned>(a->B) * a->HV) << p.split_log2);
     L.block = dim3(((a->V / inst.rows) * 64) >> p.split_log2);
     return LA_OK;

@@ -2019,7 +2019,12 @@ def test_kernel_info_reports_the_dispatch(case):
     assert info["waves_per_simd"] == info["blocks_per_cu"] * threads // 64 // 4
     assert info["tokens_per_round"] == ch
     per_token = (3 if variant == "kda" else 2) * 128 + 128 + 4
-    assert info["lds_bytes"] == min(T, ch) * per_token * 4
+    # 32-row instances without per-token writes on an fp32 pool also stage
+    # their final write-back: 8 rows of 132 floats per wave
+    stage = (threads // 64) * 8 * 132 if (
+        kernel == "decode_kernel" and threads == 256 and ch != 2
+        and state == torch.float32) else 0
+    assert info["lds_bytes"] == (min(T, ch) * per_token + stage) * 4
     if kernel == "decode1_kernel":
         assert info["lds_bytes"] == 0 and info["waves_per_simd"] == 8
     if kernel == "decode_kernel":
