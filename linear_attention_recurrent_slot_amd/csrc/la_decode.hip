@@ -162,11 +162,13 @@ constexpr float kL2Eps = 1e-6f;
 // T=8 165.2 -> 163.0, KDA B=128 T=8 90.0 -> 88.5, GDN B=64 HV=32 T=8 60.1 ->
 // 58.3, T=2 48.6 -> 48.1, GDN B=32 HV=32 T=1 24.0 -> 23.0, Lightning B=15
 // H=64 23.4 -> 23.0; the varlen GDN batch with the cache even (110.1 and
-// 110.4). Not used where it lost: the 16-row instance (KDA B=16 T=8 15.5
-// -> 16.1) and the two-token instance that writes every token's state (GDN
-// B=32 T=4 with the cache 69.1 -> 69.6). Loading the tile the same way
-// (contiguous loads, transposed through LDS before the token loop) lost
-// everywhere (KDA T=8 170.1, GDN T=1 24.6). Instances with bf16 outputs
+// 110.4). Not used where it did not gain: the 16-row instance (KDA B=16 T=8
+// 15.5 -> 16.1) and the two-token instance that writes every token's state
+// (GDN B=32 T=4 with the cache: final write-back staged 69.1 -> 69.6; every
+// token's state staged as well 67.3 against 68.9 on one box, 69.1 against
+// 68.8-69.3 on another, with 24 scalar registers spilled to vector lanes).
+// Loading the tile the same way (contiguous loads, transposed through LDS
+// before the token loop) lost everywhere (KDA T=8 170.1, GDN T=1 24.6). Instances with bf16 outputs
 // keep direct stores: their token loop leaves no registers to spare, and
 // the staging took three of them past 128 VGPRs (3 waves per SIMD).
 constexpr int kStageRowFloats = 132;
