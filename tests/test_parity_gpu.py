@@ -2116,6 +2116,12 @@ PADDED_CASES = {
                            pool_size=12, inter=True, pads=(4, 1)),
     "general_kda_t1_v64": dict(variant=W.KDA, B=8, T=1, H=4, HV=4, K=128,
                                V=64, pool_size=16, pads=(4, 1)),
+    # 32-row instances whose final write-back goes through LDS: rows of the
+    # padded pool are K + pad floats apart
+    "general_staged_gdn_t2": dict(variant=W.GDN, B=40, T=2, H=8, HV=16,
+                                  K=128, V=128, pool_size=88, pads=(4, 1)),
+    "general_staged_kda_t6": dict(variant=W.KDA, B=24, T=6, H=24, HV=24,
+                                  K=128, V=128, pool_size=52, pads=(8, 1)),
     # one-token kernel (fp32: beyond 1024 tiles at K = V = 128, the split
     # form; from 4096 tiles at the other shapes, one workgroup per tile)
     "one_token_gdn": dict(variant=W.GDN, B=64, T=1, H=16, HV=32, K=128,
@@ -2155,6 +2161,12 @@ def test_padded_rows_and_heads(name):
                                 else "decode_kernel"), name
     lad = _lad()
     d = wl.to(DEV)
+    if "_staged_" in name:  # 32 rows per wave and the write-back's LDS area
+        kw = dict(l2norm_qk=wl.l2norm, beta_logit=wl.beta_logit)
+        info = lad.kernel_info(variant, d.q, d.k, d.v, d.g, d.beta, d.pool(),
+                               d.read_idx, d.write_idx, **kw)
+        assert info["block_threads"] == 256, info
+        assert info["lds_bytes"] >= 4 * 8 * 132 * 4, info
     big, pool = _padded_pool(wl, row_pad, head_pad)
     assert pool.stride(2) == wl.K + row_pad
     inter = None
