@@ -1902,6 +1902,17 @@ la_status validate(const la_decode_args *a, int var)
 //   32-pair blocks, >= 48 heads: Lightning B=33 H=64 74.0 -> 75.1; GDN
 //   HV=48 71.8 -> 72.7, HV=96 74.6 -> 76.1; Lightning K=V=64 H=64 71.1 ->
 //   74.2; GDN HV=64 T=2 and Lightning H=64 B=64 unchanged.
+// Dense KDA calls of more than four tokens with no per-token writes (four
+// tokens per LDS round) keep the plain order: same boxes, 4 GiB rotation,
+// steady clocks, us per call, ranges -> plain: KDA B=256 H=24 T=8 163.2 ->
+// 161.3 (three boxes, 1.0-1.1 %), B=128 T=8 88.5 -> 87.1, bf16 pool B=128
+// T=8 66.3 -> 64.9, B=96 H=8 T=8 26.7 -> 26.5, B=64 T=16 71.4 -> 71.0; T=6
+// and K = V = 64 even, T=5 143.9 -> 144.2. Varlen KDA batches keep ranges
+// (B=128 T<=8: 77.6 -> 78.0), and so do the calls that write a state per
+// token, where the plain order loses 2-4 % (GDN B=32 T=4 with the cache
+// 69.1 -> 70.5, paged GDN B=64 T=4 121.7 -> 126.7, KDA B=64 T=4 with the
+// cache 112.7 -> 116.0), and the K = V = 64 one-token grids (GDN B=256
+// HV=32: 46.2 -> 52.7).
 // The packed kernel keeps the plain order (13 bf16 shapes: -2.5 to +2.7),
 // and so does the small-grid instance, where ranges lost up to 4.5 points
 // (GDN B=32 HV=16 T=4 with the cache, 512 tiles: 66.6 -> 62.1; GDN B=64
@@ -2069,9 +2080,12 @@ la_status select_kernel(const la_decode_args *a, int var, Launch &L)
     // the one-token kernel at K = V = 128 splits tiles and deals blocks of
     // kOneXcdTiles whole tiles to the XCDs in turn
     p.split_log2 = one && a->K == 128 && a->V == 128 ? kOneSplitLog2 : 0;
-    p.xcd_block = p.split_log2    ? kOneXcdTiles << p.split_log2
-                  : packed || small ? 1
-                                    : xcd_block_for(a->B, a->HV);
+    // dense KDA calls of more than kKdaTokChunk tokens without per-token
+    // writes keep the plain order (see xcd_block_for)
+    const bool plain = packed || small || (kda_mid && !a->cu_seqlens);
+    p.xcd_block = p.split_log2 ? kOneXcdTiles << p.split_log2
+                  : plain      ? 1
+                               : xcd_block_for(a->B, a->HV);
     L.fn = inst.fn;
     L.name = packed ? "decode_packed_kernel"
              : one  ? "decode1_kernel"

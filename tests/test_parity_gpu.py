@@ -1860,24 +1860,27 @@ def test_one_token_kernel_bf16_state(variant, K, V):
     run_and_check(wl)
 
 
-@pytest.mark.parametrize("variant,B,H,HV,K,kernel", [
+@pytest.mark.parametrize("variant,B,T,H,HV,K,kernel", [
     # one range per XCD, 3 pairs past them
-    (W.GDN, 67, 5, 25, 64, "decode_kernel"),
+    (W.GDN, 67, 1, 5, 25, 64, "decode_kernel"),
     # 32-pair blocks, 48 pairs past them (816 tiles: below the one-token
     # kernel's threshold)
-    (W.LIGHTNING, 17, 48, 48, 128, "decode_kernel"),
+    (W.LIGHTNING, 17, 1, 48, 48, 128, "decode_kernel"),
     # 2079 pairs in the one-token kernel: 8316 workgroups (4 per tile),
     # blocks of 4 whole tiles (16 workgroups) dealt to the XCDs in turn, 124
     # workgroups past the last whole round of blocks
-    (W.GDN, 63, 11, 33, 128, "decode1_kernel"),
-], ids=["ranges_gdn", "blocks_lightning", "ranges_one_token"])
-def test_xcd_block_order_covers_every_pair(variant, B, H, HV, K, kernel):
+    (W.GDN, 63, 1, 11, 33, 128, "decode1_kernel"),
+    # dense KDA with more than four tokens: the plain order (1080 pairs)
+    (W.KDA, 45, 8, 24, 24, 128, "decode_kernel"),
+], ids=["ranges_gdn", "blocks_lightning", "ranges_one_token", "plain_kda_t8"])
+def test_xcd_block_order_covers_every_pair(variant, B, T, H, HV, K, kernel):
     """Workgroups take their pairs in XCD blocks (general kernel: whole
-    ranges below 48 value heads, 32-pair blocks from 48; split one-token
-    kernel: blocks of four whole tiles) with the workgroups past the last whole
-    round in plain order: every request's outputs and stored state match the
-    oracle, and nothing else in the pool changes."""
-    wl = W.make("xcd", variant, B=B, T=1, H=H, HV=HV, K=K, V=K,
+    ranges below 48 value heads, 32-pair blocks from 48, the plain order for
+    dense KDA calls of more than four tokens without per-token writes; split
+    one-token kernel: blocks of four whole tiles) with the workgroups past
+    the last whole round in plain order: every request's outputs and stored
+    state match the oracle, and nothing else in the pool changes."""
+    wl = W.make("xcd", variant, B=B, T=T, H=H, HV=HV, K=K, V=K,
                 pool_size=2 * B + 1, seed=9900 + B, separate_write=True,
                 act_dtype=torch.float32, l2norm=variant != W.LIGHTNING)
     assert _kernel_name(wl) == kernel
