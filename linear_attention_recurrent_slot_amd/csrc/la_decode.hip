@@ -23,7 +23,9 @@
 //    r = lane >> 3 holds rows {R w + 8 i + r} and the 16-byte chunks
 //    {c + 8 j} of each (4 fp32 or 8 bf16 columns). Each 128-bit buffer load
 //    of the wave reads 8 whole 128-byte row segments; every byte of the tile
-//    is read once and written once.
+//    is read once and written once. Instances that write only the final
+//    fp32 128 x 128 state pass it through a per-wave LDS area first, so each
+//    store instruction covers 2 whole rows.
 //  - Row dot products (S k and S q) reduce over the 8 lanes of a row with
 //    three DPP butterfly adds; the butterfly leaves a bit-identical sum in
 //    all 8 lanes, so the rank-1 update needs no broadcast.
@@ -34,9 +36,10 @@
 //  - Instances: 32 rows per wave; 16 on grids that fill less than one
 //    resident round and with update records.
 //  - Workgroups take their pairs in XCD blocks (xcd_block_pair): whole
-//    requests per XCD below 48 value heads, 32-pair blocks from 48; the
-//    split one-token kernel deals blocks of four whole tiles to the XCDs in
-//    turn.
+//    requests per XCD below 48 value heads, 32-pair blocks from 48, the
+//    plain order for dense KDA calls of more than four tokens without
+//    per-token writes; the split one-token kernel deals blocks of four
+//    whole tiles to the XCDs in turn.
 //  - No MFMA: per token the work is two matrix-vector products and a rank-1
 //    update against one vector operand, bound by HBM traffic of the state.
 //  - Per token and element: one multiply (decay), two FMAs (read-outs) and
@@ -93,8 +96,8 @@ constexpr int kSmallGridRowsPerWave = 16;
 constexpr int64_t kSmallGridWaves = 4096;
 // Pairs per XCD block (xcd_block_pair): calls with fewer value heads than
 // kXcdRangeMaxHeads give each XCD one contiguous range of pairs, i.e. whole
-// requests; the others deal blocks of kXcdBlockPairs pairs. See
-// xcd_block_for for the measurements.
+// requests; the others deal blocks of kXcdBlockPairs pairs (exceptions in
+// select_kernel). See xcd_block_for for the measurements.
 constexpr int kXcdRangeMaxHeads = 48;
 constexpr int kXcdBlockPairs = 32;
 // Workgroups per K = V = 128 tile of the one-token kernel: its waves are
