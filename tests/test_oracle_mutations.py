@@ -65,14 +65,28 @@ MUTATIONS = {
         "return lower_bound * exp(a_log) / (1.0 + exp(-z));"),
     "gate_kda_dt_bias_transposed": ("dt_bias[(size_t)hv * K + j],",
                                     "dt_bias[(size_t)j * HV + hv],"),
+    "read_slot_is_batch_position": (
+        "            r = read_idx[b];\n            w = write_idx",
+        "            r = read_idx[b] < 0 ? -1 : b;\n            w = write_idx"),
+    "state_restarts_each_token": (
+        "            for (int t = 0; t < Tb; ++t) {\n                const size_t qk_off",
+        "            for (int t = 0; t < Tb; ++t) {\n                memcpy(S, pool_in + "
+        "((size_t)r * HV + hv) * tile, tile * sizeof(double));\n"
+        "                const size_t qk_off"),
     "varlen_empty_request_skips_write": (
         "            if (w >= 0)\n                memcpy(pool_out + ((size_t)w * HV + hv) * tile, S,",
         "            if (w >= 0 && Tb > 0)\n                memcpy(pool_out + ((size_t)w * HV + hv) * tile, S,"),
 }
 
 
-@pytest.mark.parametrize("name", sorted(MUTATIONS))
-def test_pins_catch_planted_mistake(name, tmp_path):
+# Indexing mistakes that the property tests over random shapes and slot
+# assignments (test_oracle_properties.py) must catch on their own.
+PROPERTY_MUTATIONS = ["gva_head_map", "padded_output_not_zeroed",
+                      "write_to_read_slot", "read_slot_is_batch_position",
+                      "state_restarts_each_token"]
+
+
+def _run_against_mutant(name, tmp_path, test_file):
     old, new = MUTATIONS[name]
     text = open(SRC).read()
     assert text.count(old) >= 1, "mutation anchor not found: " + old
@@ -82,8 +96,19 @@ def test_pins_catch_planted_mistake(name, tmp_path):
     subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o",
                     str(lib), str(src), "-lm"], check=True)
     env = dict(os.environ, LA_ORACLE_LIB=str(lib))
-    proc = subprocess.run(
+    return subprocess.run(
         [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-         os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+         os.path.join(ROOT, "tests", test_file)],
         env=env, cwd=ROOT, capture_output=True, text=True, timeout=300)
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    proc = _run_against_mutant(name, tmp_path, "test_oracle_pins.py")
     assert proc.returncode != 0, "pins did not catch " + name
+
+
+@pytest.mark.parametrize("name", PROPERTY_MUTATIONS)
+def test_properties_catch_planted_indexing_mistake(name, tmp_path):
+    proc = _run_against_mutant(name, tmp_path, "test_oracle_properties.py")
+    assert proc.returncode != 0, "properties did not catch " + name
