@@ -320,7 +320,10 @@ typedef struct la_kernel_info {
     int32_t grid_blocks;    /* workgroups: B * HV (four per tile in
                                decode1_kernel at K = V = 128)              */
     int32_t block_threads;  /* threads per workgroup                       */
-    int32_t lds_bytes;      /* dynamic LDS per workgroup                   */
+    int32_t lds_bytes;      /* dynamic LDS per workgroup: the token records
+                               of one round, plus a per-wave staging area
+                               in the instances that pass the final state
+                               through LDS before storing it               */
     int32_t vgprs;          /* architected VGPRs per lane                  */
     int32_t scratch_bytes;  /* private (spill) memory per lane             */
     int32_t blocks_per_cu;  /* workgroups resident on one compute unit     */
@@ -328,7 +331,7 @@ typedef struct la_kernel_info {
     int32_t tokens_per_round; /* token records staged in LDS per round (the
                                instance's; lds_bytes holds min(T, this) of
                                them); 0 for decode1_kernel, which stages
-                               nothing                                     */
+                               nothing, 1 for decode_packed_kernel         */
 } la_kernel_info;
 
 /* Describe the kernel that the decode call `args` of `variant` would run
