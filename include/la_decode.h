@@ -189,7 +189,9 @@ typedef struct la_decode_args {
      * t strides (their b strides are ignored); inter is
      * [total_tokens, HV, V, K] and factors [total_tokens, HV, 2K + V], both
      * contiguous. A request with T_b = 0 copies its read state to its write
-     * slot. With a slot table, num_accepted must lie in [1, T_b] (otherwise
+     * slot. With total_tokens = 0 the per-token arrays are empty and q, k,
+     * v, g, beta and out may be NULL (no request can index them). With a
+     * slot table, num_accepted must lie in [1, T_b] (otherwise
      * the request is padding). Device precondition (la_check_cu_seqlens
      * checks it): 0 <= cu_seqlens[b] <= cu_seqlens[b+1] <= total_tokens and
      * T_b <= T. A request that breaks it is skipped entirely: no output is
@@ -238,7 +240,8 @@ typedef struct la_replay_args {
                                    the request                              */
     const int32_t *cu_seqlens;  /* NULL, or [B + 1] offsets as in
                                    la_decode_args: factors is then
-                                   [total_tokens, HV, 2K + V]               */
+                                   [total_tokens, HV, 2K + V] (may be NULL
+                                   when total_tokens = 0)                   */
     int32_t total_tokens;       /* with cu_seqlens, >= 0                    */
     int32_t reserved;           /* must be 0                                */
 } la_replay_args;

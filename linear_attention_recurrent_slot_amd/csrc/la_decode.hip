@@ -1815,9 +1815,13 @@ la_status validate(const la_decode_args *a, int var)
         if (a->num_accepted)
             return LA_ERR_ARG;
     }
-    if (!a->q || !a->k || !a->v || !a->pool || !a->out)
+    // A token-packed batch of no tokens indexes no per-token array (the
+    // kernels skip any request whose offsets pass total_tokens), so its
+    // empty q, k, v, g, beta and out may come without an address.
+    const bool no_tokens = a->cu_seqlens && a->total_tokens == 0;
+    if (!a->pool || (!no_tokens && (!a->q || !a->k || !a->v || !a->out)))
         return LA_ERR_NULL;
-    if (var != VAR_LA && (!a->g || !a->beta))
+    if (var != VAR_LA && !no_tokens && (!a->g || !a->beta))
         return LA_ERR_NULL;
 
     if (!strides_nonneg(a->sq) || !strides_nonneg(a->sk) ||
@@ -2208,7 +2212,11 @@ la_status la_replay(const la_replay_args *a, void *stream)
         return LA_ERR_SHAPE;
     if (a->B == 0)
         return LA_OK;
-    if (!a->factors || !a->pool || !a->read_idx || !a->num_tokens)
+    // no records to read in a token-packed batch of no tokens (a request
+    // asking for more records than its tokens is skipped)
+    const bool no_tokens = a->cu_seqlens && a->total_tokens == 0;
+    if ((!a->factors && !no_tokens) || !a->pool || !a->read_idx ||
+        !a->num_tokens)
         return LA_ERR_NULL;
     if (!aligned(a->cu_seqlens, 4))
         return LA_ERR_ALIGN;

@@ -344,6 +344,32 @@ def test_varlen_packed_outputs_accept_flat_token_strides(lib):
     assert _status("gdn", a) == 3
 
 
+@pytest.mark.parametrize("variant", ["lightning", "gdn", "kda"])
+def test_varlen_without_tokens_needs_no_per_token_arrays(lib, variant):
+    """A token-packed batch with total_tokens = 0 indexes no per-token
+    array (empty tensors come with a NULL address), so q, k, v, g, beta and
+    out may be NULL; with one token they are required. The offsets pointer
+    is misaligned so that validation ends at its last host check
+    (LA_ERR_ALIGN) and nothing is launched."""
+    a = _valid_args(variant)
+    a.cu_seqlens = FAKE + 0x900002
+    a.total_tokens = 0
+    a.q = a.k = a.v = a.g = a.beta = a.out = None
+    assert _status(variant, a) == 4
+    a.total_tokens = 1
+    assert _status(variant, a) == 1
+
+
+def test_replay_without_tokens_needs_no_records(lib):
+    a = _valid_replay()
+    a.cu_seqlens = FAKE + 0x900002
+    a.total_tokens = 0
+    a.factors = None
+    assert lib.la_replay(ctypes.byref(a), None) == 4
+    a.total_tokens = 1
+    assert lib.la_replay(ctypes.byref(a), None) == 1
+
+
 def test_check_token_slots_host_rejections(lib):
     L = lib
     assert L.la_check_token_slots(-1, 2, 4, FAKE, 2, FAKE, FAKE, None) == 2
