@@ -2449,9 +2449,94 @@ def test_random_feature_combinations(i):
     ABI and compared with the oracle: outputs, per-token cache, update
     records, every pool slot (slots the oracle leaves unchanged must keep
     their bits) and the gaps of strided pools."""
-    cfg, gate, records, pad = _combo(i)
+    _run_combo("combo%d" % i, 8100 + i, 8200 + i, *_combo(i))
+
+
+def _combo_medium(i):
+    """Draw 100 + i of the sweep moved to a medium grid, past the small-grid
+    instance (up to 2048 tiles): the 32-row instances with every feature
+    (the one-token kernel where a plain fp32 token takes it)."""
+    import random
+    cfg, gate, records, pad = _combo(100 + i)
+    rng = random.Random(77000 + i)
+    HV = rng.choice([16, 24, 32])
+    H = rng.choice([h for h in (HV // 2, HV) if HV % h == 0])
+    lo = 4096 * 16 // cfg["V"] + 1
+    B = rng.randint(-(-lo // HV), 2048 // HV)
+    cfg.update(B=B, H=H, HV=HV)
+    T, paged, sep = cfg["T"], cfg["paged"], cfg["separate_write"]
+    cfg["pool_size"] = B * T + 3 if paged else (2 * B + 3 if sep else B + 3)
+    pad = None if paged or rng.random() < 0.7 else rng.randrange(B)
+    return cfg, gate, records, pad
+
+
+def _combo_one_token(i):
+    """Draw 200 + i of the sweep as a one-token call on a large grid
+    (1100-4096 tiles, 8-64 value heads): the one-token and packed kernels,
+    and the general kernel for the shapes that keep it."""
+    import random
+    cfg, gate, _, _ = _combo(200 + i)
+    rng = random.Random(88000 + i)
+    HV = rng.choice([8, 16, 24, 32, 48, 64])
+    H = rng.choice([h for h in (HV // 2, HV) if HV % h == 0])
+    B = rng.randint(max(1, 1100 // HV), 4096 // HV)
+    sep = rng.random() < 0.5
+    cfg.update(B=B, H=H, HV=HV, T=1, inter=False, paged=False,
+               varlen_min=None, separate_write=sep,
+               write_skip=0.3 if sep and rng.random() < 0.5 else 0.0,
+               pool_size=2 * B + 3 if sep else B + 3)
+    pad = None if rng.random() < 0.5 else rng.randrange(B)
+    return cfg, gate, False, pad
+
+
+def _combo_long(i):
+    """Draw 300 + i of the sweep as a call of 12-64 tokens (many LDS
+    rounds), without the per-token cache or paged slots."""
+    import random
+    cfg, gate, records, pad = _combo(300 + i)
+    rng = random.Random(99000 + i)
+    T = rng.choice([12, 17, 33, 64])
+    HV = rng.choice([4, 16, 24, 32])
+    H = rng.choice([h for h in (HV // 2, HV) if HV % h == 0])
+    B = rng.randint(1, max(1, 1536 // HV))
+    sep = rng.random() < 0.5
+    cfg.update(B=B, H=H, HV=HV, T=T, inter=False, paged=False,
+               separate_write=sep,
+               write_skip=0.3 if sep and rng.random() < 0.5 else 0.0,
+               pool_size=2 * B + 3 if sep else B + 3)
+    if records and B * HV * T > 40000:
+        records = False
+    return cfg, gate, records, pad if pad is None or pad < B else None
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_feature_combinations_medium_grids(i):
+    """12 draws of the whole feature space on medium grids (paged slots,
+    varlen, records, the gate chain and the cache on the 32-row
+    instances), checked as the sweep checks its draws."""
+    _run_combo("combo_medium%d" % i, 8600 + i, 8700 + i, *_combo_medium(i))
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_one_token_calls_on_large_grids(i):
+    """8 one-token draws on grids of 1100-4096 tiles (dtypes, tile shapes,
+    head grouping, gate chain, strided pools, separate, skipped and padded
+    requests), checked as the sweep checks its draws."""
+    _run_combo("combo_one%d" % i, 8800 + i, 8900 + i, *_combo_one_token(i))
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_random_long_calls(i):
+    """6 draws of 12-64 tokens per call, checked as the sweep checks its
+    draws."""
+    _run_combo("combo_long%d" % i, 9000 + i, 9100 + i, *_combo_long(i))
+
+
+def _run_combo(name, seed, gate_seed, cfg, gate, records, pad):
+    """Run one sweep draw through the C ABI and compare it with the oracle:
+    outputs, cache, records, every pool slot and the stride gaps."""
     variant = cfg.pop("variant")
-    wl = W.make("combo%d" % i, variant, seed=8100 + i, **cfg)
+    wl = W.make(name, variant, seed=seed, **cfg)
     _unit_keys(wl)
     if pad is not None:
         wl.read_idx[pad] = -1
@@ -2476,7 +2561,7 @@ def test_random_feature_combinations(i):
         kw.update(cu_seqlens=d.cu_seqlens, max_tokens=wl.T)
         okw.update(cu_seqlens=wl.cu_seqlens, max_tokens=wl.T)
     if gate is not None:
-        a_log, dt = _gate_inputs(variant, wl.HV, wl.K, 8200 + i)
+        a_log, dt = _gate_inputs(variant, wl.HV, wl.K, gate_seed)
         kw.update(A_log=a_log.to(DEV), dt_bias=dt.to(DEV),
                   lower_bound=gate[1])
         okw.update(A_log=a_log, dt_bias=dt, lower_bound=gate[1])
