@@ -591,6 +591,130 @@ def test_check_indices_empty_and_large():
     assert int(lad.check_indices(r, w2, pool_size=4096).item()) == 4
 
 
+def _indices_rule(ridx, widx, P):
+    """The bits la_check_indices documents, restated over host lists: a
+    padded request (negative read slot) reads and writes nothing."""
+    w = list(ridx) if widx is None else list(widx)
+    f = 0
+    for i, r in enumerate(ridx):
+        if r >= P:
+            f |= 1
+        if r < 0:
+            continue
+        if w[i] >= P:
+            f |= 2
+        if w[i] < 0:
+            continue
+        for j, rj in enumerate(ridx):
+            if j != i and rj >= 0:
+                f |= 4 if w[j] == w[i] else 0
+                f |= 8 if rj == w[i] else 0
+    return f
+
+
+def _token_slots_rule(tab, acc, T, P):
+    """The bits la_check_token_slots documents: a request with an accepted
+    count outside [1, T] or a negative seed is padding and writes nothing;
+    an active request writes the entries of its row (negatives skip)."""
+    def seed(i):
+        return tab[i][acc[i] - 1] if 1 <= acc[i] <= T else -1
+    f = 0
+    for i in range(len(acc)):
+        if not 1 <= acc[i] <= T:
+            f |= 16
+            continue
+        if seed(i) >= P:
+            f |= 1
+        if seed(i) < 0:
+            continue
+        if any(s >= P for s in tab[i][:T]):
+            f |= 2
+        for j in range(len(acc)):
+            if j == i or seed(j) < 0:
+                continue
+            for s in tab[i][:T]:
+                if s >= 0:
+                    f |= 8 if s == seed(j) else 0
+                    f |= 4 if s in tab[j][:T] else 0
+    return f
+
+
+def _cu_seqlens_rule(cu, T, total):
+    """The bits la_check_cu_seqlens documents."""
+    f = 0
+    for c0, c1 in zip(cu[:-1], cu[1:]):
+        if not (0 <= c0 <= total and 0 <= c1 <= total):
+            f |= 1
+        if c1 < c0 or c1 - c0 > T:
+            f |= 2
+    return f
+
+
+def test_validators_follow_their_rules_on_random_inputs():
+    """200 random inputs per validator (valid sets, and sets with negative,
+    repeated and out-of-range entries): each validator's bits equal its
+    documented rules evaluated on the host."""
+    import random
+    lad = _lad()
+    rng = random.Random(4242)
+
+    def slot(P):
+        u = rng.random()
+        return -1 if u < 0.1 else (P + rng.randrange(3) if u < 0.15
+                                   else rng.randrange(P))
+    seen = {"indices": set(), "slots": set(), "cu": set()}
+    for _ in range(200):
+        B = rng.randint(1, 24)
+        P = rng.randint(1, 2 * B + 4)
+        if rng.random() < 0.3 and P >= 2 * B:
+            perm = rng.sample(range(P), 2 * B)
+            ridx, widx = perm[:B], perm[B:]
+        else:
+            ridx = [slot(P) for _ in range(B)]
+            widx = [slot(P) for _ in range(B)]
+        if rng.random() < 0.3:
+            widx = None
+        r = torch.tensor(ridx, dtype=torch.int32, device=DEV)
+        w = None if widx is None else torch.tensor(widx, dtype=torch.int32,
+                                                   device=DEV)
+        got = int(lad.check_indices(r, w, pool_size=P).item())
+        assert got == _indices_rule(ridx, widx, P), (ridx, widx, P)
+        seen["indices"].add(got)
+
+        T = rng.randint(1, 5)
+        P = rng.randint(1, 2 * B * T + 2)
+        tab = [[slot(P) for _ in range(T)] for _ in range(B)]
+        if rng.random() < 0.3 and P >= B * T:
+            flat = rng.sample(range(P), B * T)
+            tab = [flat[b * T:(b + 1) * T] for b in range(B)]
+        acc = [rng.choice([0, T + 1]) if rng.random() < 0.1
+               else rng.randint(1, T) for _ in range(B)]
+        t = torch.tensor(tab, dtype=torch.int32, device=DEV)
+        a = torch.tensor(acc, dtype=torch.int32, device=DEV)
+        got = int(lad.check_token_slots(t, a, P, T).item())
+        assert got == _token_slots_rule(tab, acc, T, P), (tab, acc, T, P)
+        seen["slots"].add(got)
+
+        lengths = [rng.randint(0, T) for _ in range(B)]
+        cu = [0]
+        for n in lengths:
+            cu.append(cu[-1] + n)
+        total = cu[-1]
+        if rng.random() < 0.4:
+            i = rng.randrange(B + 1)
+            cu[i] += rng.choice([-2, -1, 1, T + 1])
+        if rng.random() < 0.2:
+            total = max(0, total - 1)
+        c = torch.tensor(cu, dtype=torch.int32, device=DEV)
+        got = int(lad.check_cu_seqlens(c, T, total).item())
+        assert got == _cu_seqlens_rule(cu, T, total), (cu, T, total)
+        seen["cu"].add(got)
+    # the draws reach the valid case and several failure bits of each
+    assert 0 in seen["indices"] and len(seen["indices"]) >= 6, seen
+    assert 0 in seen["slots"] and len(seen["slots"]) >= 6, seen
+    assert seen["cu"] >= {0, 1, 2, 3}, seen
+
+
 def test_workload_index_sets_are_valid():
     lad = _lad()
     for name in W.NAMED:
