@@ -398,6 +398,107 @@ def test_packed_qkv_views_bit_identical(variant):
     assert torch.equal(packed["backing"], plain["backing"])
 
 
+def _scrambled_like(x, inner, rng):
+    """A view with x's shape whose outer dimensions (all but the last
+    `inner`) are laid out in a random order with padding, inside a
+    NaN-filled buffer on the device; the inner dimension keeps unit
+    stride. Holds x's values."""
+    outer = x.dim() - inner
+    order = list(range(outer))
+    rng.shuffle(order)
+    pads = [rng.randint(0, 2) for _ in range(outer)]
+    shape = [x.shape[d] + pads[d] for d in order] + list(x.shape[outer:])
+    buf = torch.full(shape, float("nan"), dtype=x.dtype, device=DEV)
+    view = buf[tuple(slice(0, x.shape[d]) for d in order)]
+    back = [order.index(d) for d in range(outer)] + list(
+        range(outer, x.dim()))
+    view = view.permute(back)
+    view.copy_(x.to(DEV))
+    return view
+
+
+LAYOUT_CASES = {
+    # name: (variant, B, T, H, HV, K, V, act, out, state, kernel)
+    "general_gdn_t3": (W.GDN, 5, 3, 2, 4, 128, 64, torch.bfloat16,
+                       torch.float32, torch.float32, "decode_kernel"),
+    "general_kda_t5": (W.KDA, 4, 5, 2, 2, 64, 128, torch.float32,
+                       torch.bfloat16, torch.float32, "decode_kernel"),
+    "general_lightning_t2": (W.LIGHTNING, 6, 2, 3, 3, 64, 64, torch.bfloat16,
+                             torch.bfloat16, torch.bfloat16, "decode_kernel"),
+    "general_kda_bf16_state_t9": (W.KDA, 3, 9, 1, 2, 128, 128, torch.bfloat16,
+                                  torch.float32, torch.bfloat16,
+                                  "decode_kernel"),
+    "general_32_rows_gdn_t3": (W.GDN, 40, 3, 8, 16, 128, 128, torch.bfloat16,
+                               torch.float32, torch.float32, "decode_kernel"),
+    "general_32_rows_kda_t8": (W.KDA, 24, 8, 24, 24, 128, 128,
+                               torch.bfloat16, torch.float32, torch.float32,
+                               "decode_kernel"),
+    "one_token_gdn": (W.GDN, 40, 1, 16, 32, 128, 128, torch.bfloat16,
+                      torch.float32, torch.float32, "decode1_kernel"),
+    "one_token_kda": (W.KDA, 48, 1, 24, 24, 128, 128, torch.float32,
+                      torch.bfloat16, torch.float32, "decode1_kernel"),
+    "packed_gdn_bf16_state": (W.GDN, 16, 1, 8, 16, 128, 128, torch.bfloat16,
+                              torch.float32, torch.bfloat16,
+                              "decode_packed_kernel"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LAYOUT_CASES))
+def test_scrambled_activation_layouts_bit_identical(name):
+    """q, k, v, g, beta and out as views whose outer dimensions lie in
+    memory in a random order with padding (any non-negative strides, the
+    innermost dimension unit-stride) give exactly the bits of the same call
+    on contiguous tensors, in every kernel; the padding of the output
+    buffer stays NaN."""
+    import random
+    (variant, B, T, H, HV, K, V, act, outd, state,
+     kernel) = LAYOUT_CASES[name]
+    seed = 5600 + sorted(LAYOUT_CASES).index(name)
+    rng = random.Random(seed)
+
+    def make():
+        return W.make("layout", variant, B=B, T=T, H=H, HV=HV, K=K, V=V,
+                      pool_size=2 * B + 1, seed=seed, act_dtype=act,
+                      out_dtype=outd, state_dtype=state, separate_write=True,
+                      write_skip=0.2, l2norm=variant != W.LIGHTNING)
+    wl = make()
+    assert _kernel_name(wl) == kernel
+    lad = _lad()
+    results = []
+    for scrambled in (False, True):
+        d = make().to(DEV)
+        pool = d.backing[:: wl.stride_mult]
+        q, k, v, g, beta = d.q, d.k, d.v, d.g, d.beta
+        out = torch.full((B, T, HV, V), float("nan"), dtype=outd, device=DEV)
+        if scrambled:
+            q = _scrambled_like(q, 1, rng)
+            k = _scrambled_like(k, 1, rng)
+            v = _scrambled_like(v, 1, rng)
+            out = _scrambled_like(out, 1, rng)
+            if variant != W.LIGHTNING:
+                g = _scrambled_like(g, 1 if variant == W.KDA else 0, rng)
+                beta = _scrambled_like(beta, 0, rng)
+            assert not q.is_contiguous() or not out.is_contiguous()
+        if variant == W.LIGHTNING:
+            lad.la_decode(q, k, v, pool, d.read_idx, d.write_idx, lam=g,
+                          out=out, out_dtype=outd)
+        else:
+            fn = lad.gdn_decode_mtp if variant == W.GDN else \
+                lad.kda_decode_mtp
+            fn(q, k, v, g, beta, pool, d.read_idx, d.write_idx,
+               l2norm_qk=wl.l2norm, beta_logit=wl.beta_logit, out=out,
+               out_dtype=outd)
+        torch.cuda.synchronize()
+        if scrambled:
+            base = out._base
+            assert int(torch.isnan(base.float()).sum()) == \
+                base.numel() - out.numel(), "a write outside the output view"
+        results.append((out.contiguous().cpu(), d.backing.cpu()))
+    assert not torch.isnan(results[0][0].float()).any()
+    assert torch.equal(_bits(results[1][0]), _bits(results[0][0]))
+    assert torch.equal(_bits(results[1][1]), _bits(results[0][1]))
+
+
 PACKED_QKV_KERNELS = {
     # name: (variant, B, T, H, HV, state dtype, kernel)
     "one_token_gdn": (W.GDN, 64, 1, 16, 32, torch.float32, "decode1_kernel"),
