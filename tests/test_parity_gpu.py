@@ -2474,6 +2474,56 @@ def test_replay_into_padded_pool(state):
 # ------------------------------------------------- extreme decays and gates
 
 
+SUBNORMAL_CASES = {
+    # name: (variant, B, T, H, HV, state dtype, kernel)
+    "general_gdn": (W.GDN, 4, 2, 8, 8, torch.float32, "decode_kernel"),
+    "general_kda_t3": (W.KDA, 4, 3, 8, 8, torch.float32, "decode_kernel"),
+    "one_token_gdn": (W.GDN, 40, 1, 16, 32, torch.float32, "decode1_kernel"),
+    "packed_bf16_gdn": (W.GDN, 16, 1, 8, 16, torch.bfloat16,
+                        "decode_packed_kernel"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SUBNORMAL_CASES))
+def test_subnormal_states_are_not_flushed(name):
+    """A pool of subnormal states through calls whose decay is exactly 1
+    (g = 0) and whose update is exactly 0 (beta logit -1e30, so beta = 0):
+    S * 1 + 0 * k returns every nonzero element bit for bit, subnormals
+    included, in each kernel; zeros stay zero (IEEE addition may turn -0
+    into +0, as the fp64 oracle's would)."""
+    variant, B, T, H, HV, state, kernel = SUBNORMAL_CASES[name]
+    wl = W.make("subnormal", variant, B=B, T=T, H=H, HV=HV, K=128, V=128,
+                pool_size=2 * B, seed=12, state_dtype=state,
+                separate_write=True, l2norm=True)
+    gen = torch.Generator().manual_seed(5)
+    if state == torch.float32:
+        # every element subnormal: random 23-bit mantissa, random sign
+        mant = torch.randint(1, 1 << 23, wl.backing.shape, generator=gen,
+                             dtype=torch.int32)
+        sign = torch.randint(0, 2, wl.backing.shape, generator=gen,
+                             dtype=torch.int32) << 31
+        wl.backing = (mant | sign).view(torch.float32)
+    else:
+        wl.backing = (wl.backing.float() * 1e-38).to(state)
+    wl.g = torch.zeros_like(wl.g)
+    wl.beta = torch.full_like(wl.beta, -1e30)
+    assert _kernel_name(wl) == kernel
+    before = wl.backing.clone()
+    got = gpu_run(wl)
+    checked = 0
+    for b in range(B):
+        r, w = int(wl.read_idx[b]), int(wl.write_idx[b])
+        if w < 0:
+            continue
+        x, y = before[r], got["backing"][w]
+        nz = x.float() != 0
+        assert int(nz.sum()) > 0
+        assert torch.equal(_bits(x)[nz], _bits(y)[nz]), "a state changed"
+        assert bool((y.float()[~nz] == 0).all()), "a zero changed"
+        checked += 1
+    assert checked > 0
+
+
 @pytest.mark.parametrize("variant", [W.GDN, W.KDA])
 @pytest.mark.parametrize("T,B,HV", [(3, 5, 4), (1, 64, 32)],
                          ids=["t3_general", "t1_large"])
