@@ -2524,6 +2524,37 @@ def test_subnormal_states_are_not_flushed(name):
     assert checked > 0
 
 
+@pytest.mark.parametrize("name", sorted(SUBNORMAL_CASES))
+def test_nonfinite_values_stay_in_their_request(name):
+    """NaN and Inf planted in one request's read tile and in another
+    request's query reach only those requests: every other request's
+    outputs and written state equal those of a clean call bit for bit."""
+    variant, B, T, H, HV, state, kernel = SUBNORMAL_CASES[name]
+
+    def make():
+        return W.make("nonfinite", variant, B=B, T=T, H=H, HV=HV, K=128,
+                      V=128, pool_size=2 * B, seed=13, state_dtype=state,
+                      separate_write=True, l2norm=True)
+    clean = make()
+    assert _kernel_name(clean) == kernel
+    ref = gpu_run(clean)
+    bad = make()
+    r1 = int(bad.read_idx[1])
+    bad.backing[r1, 0, 3, 5] = float("nan")
+    bad.backing[r1, HV - 1, 100, 7] = float("inf")
+    bad.q[2, T - 1, 0, 9] = float("nan")
+    got = gpu_run(bad)
+    for b in range(B):
+        w = int(bad.write_idx[b])
+        if b in (1, 2):
+            assert not torch.isfinite(got["out"][b].float()).all()
+            continue
+        assert torch.equal(_bits(got["out"][b]), _bits(ref["out"][b])), b
+        if w >= 0:
+            assert torch.equal(_bits(got["backing"][w]),
+                               _bits(ref["backing"][w])), b
+
+
 @pytest.mark.parametrize("variant", [W.GDN, W.KDA])
 @pytest.mark.parametrize("T,B,HV", [(3, 5, 4), (1, 64, 32)],
                          ids=["t3_general", "t1_large"])
